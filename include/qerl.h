@@ -1,0 +1,232 @@
+/*
+ * qerl.h -- C ABI of the NVFP4 weight-only linear layer with a LoRA side
+ * branch and Adaptive Quantization Noise (AQN), for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The method is QeRL's rollout-phase linear layer, as described on the
+ * page "QeRL: Beyond Efficiency -- Quantization-enhanced Reinforcement
+ * Learning for LLMs" (the long summary page; cited below as
+ * [QeRL summary, <section>, <equation>]).
+ *
+ * Conventions shared by every call
+ *   - Tensors are plain device pointers owned by the caller.  The library
+ *     never allocates, frees or retains them.
+ *   - bf16 tensors are passed as pointers to their 16-bit patterns.
+ *   - Matrices are row-major.  A weight W has the nn.Linear layout
+ *     [n = output features, k = input features]; activations x are [m, k];
+ *     outputs y are [m, n].
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Every device call is asynchronous on that stream: it returns after
+ *     validating its arguments and enqueueing its kernels, with no host
+ *     synchronisation.  Device faults surface at the caller's next sync.
+ *   - The return value reports host-side validation and launch errors
+ *     only (qerl_status).  On an error nothing has been enqueued.
+ *   - Calls are reentrant and thread-safe; the library keeps no mutable
+ *     global state besides a per-process cache of device properties.
+ *
+ * NVFP4 storage [QeRL summary, §3.4, Eq. 6: W_hat = S_FP32 * (S_E4M3 (.)
+ * W_tilde), one E4M3 scale per block of 16 contiguous elements and one
+ * FP32 scale per tensor]:
+ *   codes  uint8 [n, k/2]   two E2M1 codes per byte, the even k in the low
+ *                           nibble; code bit 3 = sign, bits 2..0 index the
+ *                           magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6 [§3.4,
+ *                           E2M1 level list]
+ *   scales uint8 [n, k/16]  OCP FP8 E4M3 (bias 7, max 448) bit patterns;
+ *                           scale j covers k = 16j .. 16j+15 of its row
+ *   gscale float [1]        S_FP32, in device memory
+ */
+#ifndef QERL_H
+#define QERL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define QERL_API __attribute__((visibility("default")))
+#else
+#define QERL_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QERL_OK = 0,
+  QERL_ERR_NULL = 1,      /* a required pointer is NULL                    */
+  QERL_ERR_SHAPE = 2,     /* a size is out of range or k % 16 != 0         */
+  QERL_ERR_ALIGN = 3,     /* a device pointer is not aligned as required   */
+  QERL_ERR_RANGE = 4,     /* a scalar argument is out of range             */
+  QERL_ERR_WORKSPACE = 5, /* the workspace is smaller than required        */
+  QERL_ERR_HIP = 6        /* the HIP runtime refused a launch or a query   */
+} qerl_status;
+
+/* Human-readable name of a status code.  Never returns NULL. */
+QERL_API const char* qerl_status_string(int status);
+
+/* Version of this ABI; bumped when a signature or a layout changes. */
+QERL_API int qerl_abi_version(void);
+
+/*
+ * qerl_quantize_nvfp4 -- bf16 weight [n, k] -> NVFP4 (codes, scales, S).
+ *
+ * Follows Eq. 6 [QeRL summary, §3.4] read as a quantizer (the pages print
+ * only the dequantization; the rounding rules below are this library's
+ * reading of Eq. 1's "scale = range / q_max" applied at both levels):
+ *   amax  = max |w| over the tensor
+ *   S     = RN_fp32(amax / (6 * 448))
+ *   s_b   = RNE_E4M3(amax_b / (6 * S)), saturating at 448, per block
+ *   code  = sign(w) | RNE_E2M1(|w| / (s_b * S)), saturating at 6, ties to
+ *           the even code
+ * where the quotients are taken exactly (the result is bit-exact and
+ * unique).  S == 0 (all-zero tensor or underflow) gives zero scales and
+ * sign-only codes.
+ *
+ *   w_bf16         device, [n, k] bf16, 16-byte aligned
+ *   n, k           n >= 1, k >= 16, k % 16 == 0
+ *   codes          device out, [n, k/2] bytes, 16-byte aligned
+ *   scales         device out, [n, k/16] bytes
+ *   gscale         device out, 1 float (also used as the amax
+ *                  accumulator while the call runs)
+ *   nonfinite_flag device out, nullable; set to 1 if w holds an inf or a
+ *                  NaN, else 0.  When it is 1, codes/scales/gscale are
+ *                  unspecified.
+ * Four kernels are enqueued (reset, amax, scale, encode).
+ */
+QERL_API qerl_status qerl_quantize_nvfp4(const void* w_bf16, int64_t n, int64_t k,
+                                void* codes, void* scales, float* gscale,
+                                int32_t* nonfinite_flag, void* stream);
+
+/*
+ * qerl_aqn_sigma -- host, pure.  The AQN exponential decay schedule
+ * [QeRL summary, §3.4, Eq. 8]:
+ *   sigma(k) = sigma_start * (sigma_end / sigma_start)^((k-1)/(K-1)),
+ * k = 1..K, with sigma(0) = 0 (stage 0 carries only quantization noise,
+ * §3.4 "Stage 0") and sigma(1) = sigma_start when K == 1.
+ *   sigma_start, sigma_end  > 0 (the paper uses 1e-2 and 5e-4)
+ *   num_stages (K)          >= 1 (the paper uses 10)
+ *   stage (k)               0 <= k <= K
+ *   sigma_out               host out, non-NULL
+ */
+QERL_API qerl_status qerl_aqn_sigma(double sigma_start, double sigma_end,
+                           int32_t num_stages, int32_t stage,
+                           double* sigma_out);
+
+/*
+ * qerl_aqn_sample -- the AQN noise vector z ~ N(0, sigma^2 I) of length
+ * d (= the layer's input dimension) [QeRL summary, §3.4, Eq. 7], drawn
+ * afresh per forward pass by changing call_id.
+ * Generator: Philox4x64-10 (Salmon et al., SC'11) with key (seed,
+ * stream_id) and counter (j/4, call_id, 0, 0); Box-Muller in fp64 on the
+ * output words: u1 = ((r >> 11) + 1) 2^-53, u2 = (r >> 11) 2^-53,
+ * n = sqrt(-2 ln u1) {cos, sin}(2 pi u2) from the pairs (r0, r1) and
+ * (r2, r3); z_j = RN_fp32(sigma * n_j).  Element j depends only on
+ * (seed, stream_id, call_id, j).
+ *   sigma  >= 0 and finite (0 gives z == 0)
+ *   d      >= 1
+ *   z_out  device out, [d] float, 4-byte aligned
+ */
+QERL_API qerl_status qerl_aqn_sample(uint64_t seed, uint64_t stream_id,
+                            uint64_t call_id, double sigma, int64_t d,
+                            float* z_out, void* stream);
+
+/*
+ * qerl_linear_workspace_bytes -- bytes of device workspace that
+ * qerl_linear_decode / qerl_linear_prefill / qerl_linear_prepare need for
+ * these sizes on the current device.  0 if the sizes are invalid.  The
+ * workspace holds the noisy activations in bf16 ([m, k]), the LoRA
+ * down-projection and, for some shapes, split-K partial sums; it is
+ * O(m k + m n), never O(n k).
+ */
+QERL_API size_t qerl_linear_workspace_bytes(int64_t m, int64_t n, int64_t k,
+                                   int32_t r);
+
+/*
+ * qerl_linear_decode -- y = bf16( x_t W_hat^T + s (x_t A^T) B^T ),
+ *                       x_t = x (.) (1 + z)
+ * The NVFP4 linear layer with its LoRA side branch [QeRL summary, §3.4,
+ * Eq. 2: W_hat + B A, with A and B in bf16] and the AQN noise merged as a
+ * per-input-channel multiplier [§3.4 "Noise Merging", Eq. 10-12: noise
+ * folded into the RMSNorm scale multiplies channel j by (1 + z_j / w_j);
+ * here the RMSNorm weight is taken as already applied to x, w == 1].
+ * W_hat is dequantized in registers (Eq. 6); no dequantized weight buffer
+ * exists.  Tuned for small m (rollout decode, m <= 128); any m >= 1 works.
+ *
+ *   x            device, [m, k] bf16, 16-byte aligned
+ *   m            >= 1
+ *   codes, scales, gscale   the NVFP4 weight [n, k] as produced by
+ *                qerl_quantize_nvfp4 (codes 16-byte aligned)
+ *   n, k         n >= 1, k >= 16, k % 16 == 0
+ *   lora_a       device, [r, k] bf16, 16-byte aligned; NULL or r == 0
+ *                means no LoRA branch
+ *   lora_b       device, [n, r] bf16 (any alignment)
+ *   r            0 <= r <= 128
+ *   lora_scale   s (= alpha / r), finite
+ *   z            device, [k] float AQN noise, 16-byte aligned; NULL means
+ *                no noise (bit-identical to z == 0)
+ *   y            device out, [m, n] bf16, 4-byte aligned
+ *   workspace    device scratch of at least
+ *                qerl_linear_workspace_bytes(m, n, k, r) bytes,
+ *                256-byte aligned; its contents on entry do not matter
+ * Concurrent calls must not share a workspace.
+ */
+QERL_API qerl_status qerl_linear_decode(const void* x, int64_t m, const void* codes,
+                               const void* scales, const float* gscale,
+                               int64_t n, int64_t k, const void* lora_a,
+                               const void* lora_b, int32_t r,
+                               float lora_scale, const float* z, void* y,
+                               void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/*
+ * qerl_linear_prefill -- the same operation and arguments as
+ * qerl_linear_decode, tuned for large m (prompt prefill): NVFP4 tiles are
+ * dequantized into LDS and contracted with bf16 MFMA.
+ */
+QERL_API qerl_status qerl_linear_prefill(const void* x, int64_t m, const void* codes,
+                                const void* scales, const float* gscale,
+                                int64_t n, int64_t k, const void* lora_a,
+                                const void* lora_b, int32_t r,
+                                float lora_scale, const float* z, void* y,
+                                void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+/*
+ * The two halves of qerl_linear_decode / qerl_linear_prefill, for callers
+ * that time or schedule them separately.
+ *
+ * qerl_linear_prepare writes into the workspace the noisy activations
+ * x_t = bf16(x (.) (1 + z)) and the scaled LoRA down-projection
+ * bf16(s x_t A^T) [QeRL summary, §3.4, Eq. 2 and Eq. 12].  Arguments as
+ * above; n is needed to size the workspace.
+ *
+ * qerl_linear_decode_prepared / qerl_linear_prefill_prepared run the main
+ * contraction y = bf16(S acc + (s x_t A^T) B^T) from a workspace that
+ * qerl_linear_prepare filled with the same (m, n, k, r).  x, z and lora_a
+ * are not read again.
+ */
+QERL_API qerl_status qerl_linear_prepare(const void* x, int64_t m, int64_t n,
+                                int64_t k, const void* lora_a, int32_t r,
+                                float lora_scale, const float* z,
+                                void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+QERL_API qerl_status qerl_linear_decode_prepared(int64_t m, const void* codes,
+                                        const void* scales,
+                                        const float* gscale, int64_t n,
+                                        int64_t k, const void* lora_b,
+                                        int32_t r, void* y, void* workspace,
+                                        size_t workspace_bytes, void* stream);
+
+QERL_API qerl_status qerl_linear_prefill_prepared(int64_t m, const void* codes,
+                                         const void* scales,
+                                         const float* gscale, int64_t n,
+                                         int64_t k, const void* lora_b,
+                                         int32_t r, void* y, void* workspace,
+                                         size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QERL_H */

@@ -1,0 +1,154 @@
+"""NVFP4 weight-only linear layer with LoRA and AQN noise for MI355X.
+
+Python binding of libqerl.so (C ABI: include/qerl.h).  Each function has
+the name of the C call it wraps and does argument marshalling only: it
+checks devices and dtypes, allocates outputs with torch, passes raw device
+pointers and torch's current HIP stream, and raises QerlError on a
+non-zero status.  Every step of the computation runs in the HIP kernels.
+"""
+import ctypes
+
+import torch
+
+from . import _lib
+
+lib = _lib.load()
+
+QERL_OK = 0
+
+
+class QerlError(RuntimeError):
+    def __init__(self, status, call):
+        self.status = int(status)
+        msg = lib.qerl_status_string(self.status).decode()
+        super().__init__(f"{call}: {msg}")
+
+
+def _check(status, call):
+    if status != QERL_OK:
+        raise QerlError(status, call)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _bits16(t, name):
+    """bf16 tensor (or its uint16/int16 bit view) -> int16 view, contiguous."""
+    if t.dtype == torch.bfloat16:
+        t = t.view(torch.int16)
+    elif t.dtype not in (torch.int16, torch.uint16):
+        raise TypeError(f"{name} must be bfloat16 (or its 16-bit pattern)")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    return t.contiguous()
+
+
+def qerl_abi_version():
+    return lib.qerl_abi_version()
+
+
+def qerl_quantize_nvfp4(w):
+    """bf16 W [n, k] -> (codes uint8 [n, k/2], scales uint8 [n, k/16],
+    gscale float32 [1], nonfinite int32 [1]) on W's device."""
+    w = _bits16(w, "w")
+    n, k = w.shape
+    dev = w.device
+    codes = torch.empty((n, k // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((n, k // 16), dtype=torch.uint8, device=dev)
+    gscale = torch.empty(1, dtype=torch.float32, device=dev)
+    flag = torch.empty(1, dtype=torch.int32, device=dev)
+    _check(lib.qerl_quantize_nvfp4(_ptr(w), n, k, _ptr(codes), _ptr(scales), _ptr(gscale),
+                                   _ptr(flag), _stream(dev)), "qerl_quantize_nvfp4")
+    return codes, scales, gscale, flag
+
+
+def qerl_aqn_sigma(sigma_start, sigma_end, num_stages, stage):
+    out = ctypes.c_double(0.0)
+    _check(lib.qerl_aqn_sigma(sigma_start, sigma_end, num_stages, stage, ctypes.byref(out)),
+           "qerl_aqn_sigma")
+    return out.value
+
+
+def qerl_aqn_sample(seed, stream_id, call_id, sigma, d, device="cuda", out=None):
+    z = out if out is not None else torch.empty(d, dtype=torch.float32, device=device)
+    _check(lib.qerl_aqn_sample(seed, stream_id, call_id, sigma, d, _ptr(z), _stream(z.device)),
+           "qerl_aqn_sample")
+    return z
+
+
+def qerl_linear_workspace_bytes(m, n, k, r):
+    return int(lib.qerl_linear_workspace_bytes(m, n, k, r))
+
+
+def workspace(m, n, k, r, device="cuda"):
+    """A device workspace of the size qerl_linear_workspace_bytes asks for."""
+    nbytes = qerl_linear_workspace_bytes(m, n, k, r)
+    if nbytes == 0:
+        raise ValueError("invalid linear sizes")
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def _linear(fn_name, x, codes, scales, gscale, lora_a, lora_b, lora_scale, z, ws, y):
+    x = _bits16(x, "x")
+    m, k = x.shape
+    n = codes.shape[0]
+    r = 0 if lora_a is None else int(lora_a.shape[0])
+    la = None if lora_a is None else _bits16(lora_a, "lora_a")
+    lb = None if lora_b is None else _bits16(lora_b, "lora_b")
+    if ws is None:
+        ws = workspace(m, n, k, r, x.device)
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.bfloat16, device=x.device)
+    fn = getattr(lib, fn_name)
+    _check(fn(_ptr(x), m, _ptr(codes), _ptr(scales), _ptr(gscale), n, k, _ptr(la), _ptr(lb), r,
+              float(lora_scale), _ptr(z), _ptr(y), _ptr(ws), ws.numel(), _stream(x.device)),
+           fn_name)
+    return y
+
+
+def qerl_linear_decode(x, codes, scales, gscale, lora_a=None, lora_b=None, lora_scale=0.0,
+                       z=None, workspace=None, y=None):
+    """y = bf16(x_t W_hat^T + s (x_t A^T) B^T), x_t = x (1 + z); tuned for small m."""
+    return _linear("qerl_linear_decode", x, codes, scales, gscale, lora_a, lora_b,
+                   lora_scale, z, workspace, y)
+
+
+def qerl_linear_prefill(x, codes, scales, gscale, lora_a=None, lora_b=None, lora_scale=0.0,
+                        z=None, workspace=None, y=None):
+    """Same as qerl_linear_decode, tuned for large m."""
+    return _linear("qerl_linear_prefill", x, codes, scales, gscale, lora_a, lora_b,
+                   lora_scale, z, workspace, y)
+
+
+def qerl_linear_prepare(x, n, lora_a, lora_scale, z, workspace):
+    x = _bits16(x, "x")
+    m, k = x.shape
+    r = 0 if lora_a is None else int(lora_a.shape[0])
+    la = None if lora_a is None else _bits16(lora_a, "lora_a")
+    _check(lib.qerl_linear_prepare(_ptr(x), m, n, k, _ptr(la), r, float(lora_scale), _ptr(z),
+                                   _ptr(workspace), workspace.numel(), _stream(x.device)),
+           "qerl_linear_prepare")
+
+
+def _prepared(fn_name, m, codes, scales, gscale, k, lora_b, r, y, workspace):
+    n = codes.shape[0]
+    lb = None if lora_b is None else _bits16(lora_b, "lora_b")
+    fn = getattr(lib, fn_name)
+    _check(fn(m, _ptr(codes), _ptr(scales), _ptr(gscale), n, k, _ptr(lb), r, _ptr(y),
+              _ptr(workspace), workspace.numel(), _stream(y.device)), fn_name)
+    return y
+
+
+def qerl_linear_decode_prepared(m, codes, scales, gscale, k, lora_b, r, y, workspace):
+    return _prepared("qerl_linear_decode_prepared", m, codes, scales, gscale, k, lora_b, r,
+                     y, workspace)
+
+
+def qerl_linear_prefill_prepared(m, codes, scales, gscale, k, lora_b, r, y, workspace):
+    return _prepared("qerl_linear_prefill_prepared", m, codes, scales, gscale, k, lora_b, r,
+                     y, workspace)

@@ -1,0 +1,45 @@
+"""ctypes declarations of libqerl.so (the C ABI in include/qerl.h).
+
+Loading fails loudly when the library has not been built: there is no
+fallback implementation of any call.
+"""
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqerl.so")
+
+c_i32, c_i64, c_u64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64
+c_f32, c_f64, c_sz, c_vp = ctypes.c_float, ctypes.c_double, ctypes.c_size_t, ctypes.c_void_p
+
+# name -> (restype, argtypes); the order follows include/qerl.h
+SIGNATURES = {
+    "qerl_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "qerl_abi_version": (ctypes.c_int, []),
+    "qerl_quantize_nvfp4": (ctypes.c_int, [c_vp, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp]),
+    "qerl_aqn_sigma": (ctypes.c_int, [c_f64, c_f64, c_i32, c_i32, ctypes.POINTER(c_f64)]),
+    "qerl_aqn_sample": (ctypes.c_int, [c_u64, c_u64, c_u64, c_f64, c_i64, c_vp, c_vp]),
+    "qerl_linear_workspace_bytes": (c_sz, [c_i64, c_i64, c_i64, c_i32]),
+    "qerl_linear_decode": (ctypes.c_int, [c_vp, c_i64, c_vp, c_vp, c_vp, c_i64, c_i64, c_vp,
+                                          c_vp, c_i32, c_f32, c_vp, c_vp, c_vp, c_sz, c_vp]),
+    "qerl_linear_prefill": (ctypes.c_int, [c_vp, c_i64, c_vp, c_vp, c_vp, c_i64, c_i64, c_vp,
+                                           c_vp, c_i32, c_f32, c_vp, c_vp, c_vp, c_sz, c_vp]),
+    "qerl_linear_prepare": (ctypes.c_int, [c_vp, c_i64, c_i64, c_i64, c_vp, c_i32, c_f32,
+                                           c_vp, c_vp, c_sz, c_vp]),
+    "qerl_linear_decode_prepared": (ctypes.c_int, [c_i64, c_vp, c_vp, c_vp, c_i64, c_i64,
+                                                   c_vp, c_i32, c_vp, c_vp, c_sz, c_vp]),
+    "qerl_linear_prefill_prepared": (ctypes.c_int, [c_i64, c_vp, c_vp, c_vp, c_i64, c_i64,
+                                                    c_vp, c_i32, c_vp, c_vp, c_sz, c_vp]),
+}
+
+
+def load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with "
+            "`python nvfp4_weight_quantized_qerl_amd/build.py`")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib

@@ -1,0 +1,213 @@
+// C ABI of libqerl (declared and documented in include/qerl.h): argument
+// validation on the host, then asynchronous launches on the caller's
+// stream.  No call allocates, frees or synchronises.
+#include <cmath>
+
+#include "qerl.h"
+#include "qerl_internal.h"
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) {
+  return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
+}
+
+qerl_status from_hip(hipError_t e) { return e == hipSuccess ? QERL_OK : QERL_ERR_HIP; }
+
+// Shared validation of the linear-layer arguments; fills the plan.
+qerl_status check_linear(const void* x, int64_t m, const void* codes,
+                         const void* scales, const float* gscale, int64_t n,
+                         int64_t k, int32_t r, float lora_scale, const float* z,
+                         const void* y, void* ws, size_t ws_bytes,
+                         qerl::LinearPlan* plan) {
+  if (!codes || !scales || !gscale || !y || !ws) return QERL_ERR_NULL;
+  if (m < 1 || n < 1 || k < 16 || k % 16) return QERL_ERR_SHAPE;
+  if (r < 0 || r > 128 || !std::isfinite(lora_scale)) return QERL_ERR_RANGE;
+  if ((x && !aligned(x, 16)) || !aligned(codes, 16) || !aligned(gscale, 4) ||
+      !aligned(y, 2) || (z && !aligned(z, 16)) || !aligned(ws, 256))
+    return QERL_ERR_ALIGN;
+  if (!qerl::make_linear_plan(m, n, k, r, plan)) return QERL_ERR_SHAPE;
+  if (ws_bytes < plan->total) return QERL_ERR_WORKSPACE;
+  return QERL_OK;
+}
+
+qerl_status check_prepare(const void* x, const void* lora_a, int32_t r) {
+  if (!x) return QERL_ERR_NULL;
+  if (r > 0 && !lora_a) return QERL_ERR_NULL;
+  if (lora_a && !aligned(lora_a, 16)) return QERL_ERR_ALIGN;
+  return QERL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* qerl_status_string(int status) {
+  switch (status) {
+    case QERL_OK: return "QERL_OK";
+    case QERL_ERR_NULL: return "QERL_ERR_NULL: a required pointer is NULL";
+    case QERL_ERR_SHAPE: return "QERL_ERR_SHAPE: a size is out of range or k % 16 != 0";
+    case QERL_ERR_ALIGN: return "QERL_ERR_ALIGN: a pointer is not aligned as required";
+    case QERL_ERR_RANGE: return "QERL_ERR_RANGE: a scalar argument is out of range";
+    case QERL_ERR_WORKSPACE: return "QERL_ERR_WORKSPACE: the workspace is too small";
+    case QERL_ERR_HIP: return "QERL_ERR_HIP: the HIP runtime reported an error";
+    default: return "unknown qerl_status";
+  }
+}
+
+int qerl_abi_version(void) { return 1; }
+
+qerl_status qerl_quantize_nvfp4(const void* w_bf16, int64_t n, int64_t k, void* codes,
+                                void* scales, float* gscale, int32_t* nonfinite_flag,
+                                void* stream) {
+  if (!w_bf16 || !codes || !scales || !gscale) return QERL_ERR_NULL;
+  if (n < 1 || k < 16 || k % 16) return QERL_ERR_SHAPE;
+  if (!aligned(w_bf16, 16) || !aligned(codes, 16) || !aligned(gscale, 4) ||
+      (nonfinite_flag && !aligned(nonfinite_flag, 4)))
+    return QERL_ERR_ALIGN;
+  return from_hip(qerl::launch_quantize(
+      static_cast<const uint16_t*>(w_bf16), n, k, static_cast<uint8_t*>(codes),
+      static_cast<uint8_t*>(scales), gscale, nonfinite_flag,
+      static_cast<hipStream_t>(stream)));
+}
+
+qerl_status qerl_aqn_sigma(double sigma_start, double sigma_end, int32_t num_stages,
+                           int32_t stage, double* sigma_out) {
+  if (!sigma_out) return QERL_ERR_NULL;
+  if (!(sigma_start > 0.0) || !(sigma_end > 0.0) || !std::isfinite(sigma_start) ||
+      !std::isfinite(sigma_end) || num_stages < 1 || stage < 0 || stage > num_stages)
+    return QERL_ERR_RANGE;
+  if (stage == 0) {
+    *sigma_out = 0.0;
+  } else if (num_stages == 1) {
+    *sigma_out = sigma_start;
+  } else {
+    const double ratio = sigma_end / sigma_start;
+    *sigma_out = sigma_start *
+                 std::pow(ratio, (double)(stage - 1) / (double)(num_stages - 1));
+  }
+  return QERL_OK;
+}
+
+qerl_status qerl_aqn_sample(uint64_t seed, uint64_t stream_id, uint64_t call_id,
+                            double sigma, int64_t d, float* z_out, void* stream) {
+  if (!z_out) return QERL_ERR_NULL;
+  if (d < 1) return QERL_ERR_SHAPE;
+  if (!(sigma >= 0.0) || !std::isfinite(sigma)) return QERL_ERR_RANGE;
+  if (!aligned(z_out, 4)) return QERL_ERR_ALIGN;
+  return from_hip(qerl::launch_aqn_sample(seed, stream_id, call_id, sigma, d, z_out,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+size_t qerl_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t r) {
+  qerl::LinearPlan p;
+  if (!qerl::make_linear_plan(m, n, k, r, &p)) return 0;
+  return p.total;
+}
+
+static qerl_status linear_full(bool prefill, const void* x, int64_t m, const void* codes,
+                               const void* scales, const float* gscale, int64_t n,
+                               int64_t k, const void* lora_a, const void* lora_b,
+                               int32_t r, float lora_scale, const float* z, void* y,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  if (!x) return QERL_ERR_NULL;
+  if (r > 0 && (!lora_a) != (!lora_b)) return QERL_ERR_NULL;
+  const int32_t r_eff = (r > 0 && lora_a && lora_b) ? r : 0;
+  if (r < 0 || r > 128) return QERL_ERR_RANGE;
+  qerl::LinearPlan plan;
+  qerl_status s = check_linear(x, m, codes, scales, gscale, n, k, r_eff, lora_scale, z, y,
+                               workspace, workspace_bytes, &plan);
+  if (s != QERL_OK) return s;
+  s = check_prepare(x, r_eff ? lora_a : nullptr, r_eff);
+  if (s != QERL_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  hipError_t e = qerl::launch_linear_prepare(plan, static_cast<const uint16_t*>(x), z,
+                                             static_cast<const uint16_t*>(lora_a),
+                                             lora_scale, ws, st);
+  if (e != hipSuccess) return QERL_ERR_HIP;
+  const uint8_t* c = static_cast<const uint8_t*>(codes);
+  const uint8_t* sc = static_cast<const uint8_t*>(scales);
+  const uint16_t* b = r_eff ? static_cast<const uint16_t*>(lora_b) : nullptr;
+  uint16_t* yy = static_cast<uint16_t*>(y);
+  e = prefill ? qerl::launch_linear_prefill_main(plan, c, sc, gscale, b, yy, ws, st)
+              : qerl::launch_linear_decode_main(plan, c, sc, gscale, b, yy, ws, st);
+  return from_hip(e);
+}
+
+qerl_status qerl_linear_decode(const void* x, int64_t m, const void* codes,
+                               const void* scales, const float* gscale, int64_t n,
+                               int64_t k, const void* lora_a, const void* lora_b,
+                               int32_t r, float lora_scale, const float* z, void* y,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  return linear_full(false, x, m, codes, scales, gscale, n, k, lora_a, lora_b, r,
+                     lora_scale, z, y, workspace, workspace_bytes, stream);
+}
+
+qerl_status qerl_linear_prefill(const void* x, int64_t m, const void* codes,
+                                const void* scales, const float* gscale, int64_t n,
+                                int64_t k, const void* lora_a, const void* lora_b,
+                                int32_t r, float lora_scale, const float* z, void* y,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  return linear_full(true, x, m, codes, scales, gscale, n, k, lora_a, lora_b, r,
+                     lora_scale, z, y, workspace, workspace_bytes, stream);
+}
+
+qerl_status qerl_linear_prepare(const void* x, int64_t m, int64_t n, int64_t k,
+                                const void* lora_a, int32_t r, float lora_scale,
+                                const float* z, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  if (!x || !workspace) return QERL_ERR_NULL;
+  if (m < 1 || n < 1 || k < 16 || k % 16) return QERL_ERR_SHAPE;
+  if (r < 0 || r > 128 || !std::isfinite(lora_scale)) return QERL_ERR_RANGE;
+  qerl_status s = check_prepare(x, lora_a, r);
+  if (s != QERL_OK) return s;
+  if (!aligned(x, 16) || (z && !aligned(z, 16)) || !aligned(workspace, 256))
+    return QERL_ERR_ALIGN;
+  qerl::LinearPlan plan;
+  if (!qerl::make_linear_plan(m, n, k, r, &plan)) return QERL_ERR_SHAPE;
+  if (workspace_bytes < plan.total) return QERL_ERR_WORKSPACE;
+  return from_hip(qerl::launch_linear_prepare(
+      plan, static_cast<const uint16_t*>(x), z, static_cast<const uint16_t*>(lora_a),
+      lora_scale, static_cast<char*>(workspace), static_cast<hipStream_t>(stream)));
+}
+
+static qerl_status linear_prepared(bool prefill, int64_t m, const void* codes,
+                                   const void* scales, const float* gscale, int64_t n,
+                                   int64_t k, const void* lora_b, int32_t r, void* y,
+                                   void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  if (r > 0 && !lora_b) return QERL_ERR_NULL;
+  qerl::LinearPlan plan;
+  qerl_status s = check_linear(nullptr, m, codes, scales, gscale, n, k, r, 1.0f, nullptr,
+                               y, workspace, workspace_bytes, &plan);
+  if (s != QERL_OK) return s;
+  const uint8_t* c = static_cast<const uint8_t*>(codes);
+  const uint8_t* sc = static_cast<const uint8_t*>(scales);
+  const uint16_t* b = r > 0 ? static_cast<const uint16_t*>(lora_b) : nullptr;
+  uint16_t* yy = static_cast<uint16_t*>(y);
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return from_hip(prefill ? qerl::launch_linear_prefill_main(plan, c, sc, gscale, b, yy, ws, st)
+                          : qerl::launch_linear_decode_main(plan, c, sc, gscale, b, yy, ws, st));
+}
+
+qerl_status qerl_linear_decode_prepared(int64_t m, const void* codes, const void* scales,
+                                        const float* gscale, int64_t n, int64_t k,
+                                        const void* lora_b, int32_t r, void* y,
+                                        void* workspace, size_t workspace_bytes,
+                                        void* stream) {
+  return linear_prepared(false, m, codes, scales, gscale, n, k, lora_b, r, y, workspace,
+                         workspace_bytes, stream);
+}
+
+qerl_status qerl_linear_prefill_prepared(int64_t m, const void* codes, const void* scales,
+                                         const float* gscale, int64_t n, int64_t k,
+                                         const void* lora_b, int32_t r, void* y,
+                                         void* workspace, size_t workspace_bytes,
+                                         void* stream) {
+  return linear_prepared(true, m, codes, scales, gscale, n, k, lora_b, r, y, workspace,
+                         workspace_bytes, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,241 @@
+// Linear layer, shared part: launch plan, workspace layout and the prepare
+// step that both the decode and the prefill contraction consume.
+//
+// The layer [QeRL summary, §3.4, Eq. 2 (LoRA on the quantized weight) and
+// Eq. 10-12 (AQN noise folded into the RMSNorm scale, i.e. a multiplier
+// (1 + z_j) on input channel j shared by every token of the call)]:
+//     x_t = x (.) (1 + z)
+//     y   = bf16( S * (x_t W0^T) + (s x_t A^T) B^T ),  W0 = e2m1 (.) s_b
+// S (the FP32 tensor scale) is applied to the fp32 accumulator once in the
+// epilogue, so the in-register dequantized weight W0 = e2m1 * s_b is exact
+// in bf16.
+//
+// prepare (one wave per 32 rows x K chunk):
+//   x_t   = bf16(x * (1 + z))  -> workspace, rows padded to a multiple of 32
+//           with zeros so the contraction kernels need no row masks;
+//   tpart = x_t A^T over the chunk (bf16 MFMA, fp32) -> workspace;
+//   it also clears the split-K arrival counters of the decode kernel.
+// treduce: t = bf16(s * sum over chunks of tpart), summed in chunk order so
+//   the result is deterministic.
+#include <algorithm>
+
+#include "qerl_device.h"
+#include "qerl_internal.h"
+
+namespace qerl {
+
+int device_cu_count() {
+  static int cached = [] {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount,
+                              dev) != hipSuccess || cus <= 0)
+      return 256;
+    return cus;
+  }();
+  return cached;
+}
+
+namespace {
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline int64_t rup(int64_t a, int64_t b) { return cdiv(a, b) * b; }
+
+int decode_nt_max(int mt) { return mt == 1 ? 6 : (mt == 2 ? 5 : 3); }
+
+// Decode rows-per-workgroup and split-K choice for one m tile count.
+void plan_decode(LinearPlan* p, int mt) {
+  const int cu = device_cu_count();
+  const int ntmax = decode_nt_max(mt);
+  const int64_t n = p->n;
+  const int64_t units = cdiv(p->k, 64);     // 64-wide K blocks (last may be partial)
+  const int64_t rows_per_cu = cdiv(n, cu);
+  int rows, split;
+  if (rows_per_cu >= 64 || units < 8) {
+    const int64_t rounds = cdiv(rows_per_cu, 32 * ntmax);
+    rows = (int)rup(cdiv(n, rounds * cu), 16);
+    rows = std::min(rows, 32 * ntmax);
+    split = 1;
+  } else {
+    double best = -1.0;
+    rows = 32 * ntmax;
+    split = 1;
+    for (int cand = 64; cand <= 32 * ntmax; cand += 16) {
+      const int64_t groups = cdiv(n, cand);
+      int64_t s = std::max<int64_t>(1, cu / groups);
+      s = std::min<int64_t>(s, std::max<int64_t>(1, units / 4));
+      const int64_t wgs = groups * s;
+      const double util = (double)wgs / (double)(cu * cdiv(wgs, cu));
+      if (util > best + 1e-9 || (util > best - 1e-9 && cand > rows)) {
+        best = util;
+        rows = cand;
+        split = (int)s;
+      }
+    }
+  }
+  int64_t per = cdiv(units, split);
+  split = (int)cdiv(units, per);
+  p->dec_mt = mt;
+  p->dec_rows = rows;
+  p->dec_nt = (int)cdiv(rows, 32);
+  p->dec_groups = (int)cdiv(n, rows);
+  p->dec_split = split;
+  p->dec_kblk_per_split = per;
+}
+
+}  // namespace
+
+bool make_linear_plan(int64_t m, int64_t n, int64_t k, int r, LinearPlan* p) {
+  if (m < 1 || n < 1 || k < 16 || k % 16 || r < 0 || r > 128) return false;
+  *p = LinearPlan{};
+  p->m = m;
+  p->n = n;
+  p->k = k;
+  p->r = r;
+  p->mpad = rup(m, 32);
+  p->rpad32 = r ? (int)rup(r, 32) : 0;
+  p->rpad16 = r ? (int)rup(r, 16) : 0;
+  const int cu = device_cu_count();
+  const int64_t ksteps = k / 16;
+  const int64_t mtiles = p->mpad / 32;
+  int64_t kc = std::max<int64_t>(1, cdiv(2 * cu, mtiles));
+  kc = std::min<int64_t>(kc, std::max<int64_t>(1, ksteps / 16));
+  const int64_t steps_per = cdiv(ksteps, kc);
+  p->kchunks = (int)cdiv(ksteps, steps_per);
+  p->kchunk = steps_per * 16;
+  const int mt = (int)std::min<int64_t>(4, mtiles);
+  plan_decode(p, mt);
+  p->pf_tile_m = 128;
+  p->pf_tile_n = 128;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = (size_t)rup((int64_t)(off + bytes), 256);
+    return o;
+  };
+  p->off_xt = take((size_t)p->mpad * k * 2);
+  p->off_tpart = take(r ? (size_t)p->kchunks * p->mpad * p->rpad32 * 4 : 0);
+  p->off_t = take(r ? (size_t)p->mpad * p->rpad16 * 2 : 0);
+  p->off_cnt = take((size_t)p->dec_groups * 4);
+  p->off_ypart = take(p->dec_split > 1
+                          ? (size_t)p->dec_split * 32 * p->dec_mt * n * 4
+                          : 0);
+  p->total = off;
+  return true;
+}
+
+namespace {
+
+struct PrepArgs {
+  const uint16_t* x;
+  const float* z;
+  const uint16_t* a;
+  uint16_t* xt;
+  float* tpart;
+  uint32_t* cnt;
+  int64_t m, mpad, k, kchunk;
+  int r, rpad32, ncnt;
+};
+
+template <int RT>
+__global__ __launch_bounds__(64) void prep_kernel(PrepArgs p) {
+  const int lane = threadIdx.x, h = lane >> 5, c = lane & 31;
+  const int64_t mrow = (int64_t)blockIdx.x * 32 + c;
+  const int64_t kbeg = (int64_t)blockIdx.y * p.kchunk;
+  const int64_t kend = std::min(p.k, kbeg + p.kchunk);
+  if (blockIdx.x == 0 && blockIdx.y == 0)
+    for (int i = lane; i < p.ncnt; i += 64) p.cnt[i] = 0u;
+  f32x16_t acc[RT > 0 ? RT : 1];
+#pragma unroll
+  for (int t = 0; t < (RT > 0 ? RT : 1); ++t) acc[t] = zero16();
+  const bool live = mrow < p.m;
+  const uint16_t* xrow = p.x + mrow * p.k;
+  uint16_t* xtrow = p.xt + mrow * p.k;
+  for (int64_t k0 = kbeg + 8 * h; k0 < kend; k0 += 16) {
+    uint4 xv = live ? *reinterpret_cast<const uint4*>(xrow + k0)
+                    : make_uint4(0u, 0u, 0u, 0u);
+    if (p.z) {
+      const float4 z0 = *reinterpret_cast<const float4*>(p.z + k0);
+      const float4 z1 = *reinterpret_cast<const float4*>(p.z + k0 + 4);
+      xv.x = pack_bf16x2(bf16_to_f32(xv.x & 0xffffu) * (1.0f + z0.x),
+                         bf16_to_f32(xv.x >> 16) * (1.0f + z0.y));
+      xv.y = pack_bf16x2(bf16_to_f32(xv.y & 0xffffu) * (1.0f + z0.z),
+                         bf16_to_f32(xv.y >> 16) * (1.0f + z0.w));
+      xv.z = pack_bf16x2(bf16_to_f32(xv.z & 0xffffu) * (1.0f + z1.x),
+                         bf16_to_f32(xv.z >> 16) * (1.0f + z1.y));
+      xv.w = pack_bf16x2(bf16_to_f32(xv.w & 0xffffu) * (1.0f + z1.z),
+                         bf16_to_f32(xv.w >> 16) * (1.0f + z1.w));
+    }
+    *reinterpret_cast<uint4*>(xtrow + k0) = xv;
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+      const int j = 32 * t + c;
+      const uint4 av = (j < p.r)
+          ? *reinterpret_cast<const uint4*>(p.a + (int64_t)j * p.k + k0)
+          : make_uint4(0u, 0u, 0u, 0u);
+      acc[t] = mfma_bf16(xv, av, acc[t]);
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < RT; ++t) {
+    float* dst = p.tpart + ((int64_t)blockIdx.y * p.mpad + (int64_t)blockIdx.x * 32) * p.rpad32
+                 + 32 * t + c;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) dst[(int64_t)acc_row(v, lane) * p.rpad32] = acc[t][v];
+  }
+}
+
+__global__ __launch_bounds__(256) void treduce_kernel(const float* __restrict__ tpart,
+                                                      uint16_t* __restrict__ t,
+                                                      int64_t mpad, int rpad32,
+                                                      int rpad16, int kchunks,
+                                                      float s) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= mpad * rpad16) return;
+  const int64_t mrow = i / rpad16;
+  const int j = (int)(i % rpad16);
+  float sum = 0.0f;
+  for (int c = 0; c < kchunks; ++c) sum += tpart[((int64_t)c * mpad + mrow) * rpad32 + j];
+  t[i] = f32_to_bf16_bits(s * sum);
+}
+
+}  // namespace
+
+hipError_t launch_linear_prepare(const LinearPlan& p, const uint16_t* x,
+                                 const float* z, const uint16_t* lora_a,
+                                 float lora_scale, char* ws,
+                                 hipStream_t stream) {
+  PrepArgs a;
+  a.x = x;
+  a.z = z;
+  a.a = lora_a;
+  a.xt = reinterpret_cast<uint16_t*>(ws + p.off_xt);
+  a.tpart = reinterpret_cast<float*>(ws + p.off_tpart);
+  a.cnt = reinterpret_cast<uint32_t*>(ws + p.off_cnt);
+  a.m = p.m;
+  a.mpad = p.mpad;
+  a.k = p.k;
+  a.kchunk = p.kchunk;
+  a.r = p.r;
+  a.rpad32 = p.rpad32;
+  a.ncnt = p.dec_groups;
+  const dim3 grid((unsigned)(p.mpad / 32), (unsigned)p.kchunks);
+  switch (p.rpad32 / 32) {
+    case 0: hipLaunchKernelGGL(prep_kernel<0>, grid, dim3(64), 0, stream, a); break;
+    case 1: hipLaunchKernelGGL(prep_kernel<1>, grid, dim3(64), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL(prep_kernel<2>, grid, dim3(64), 0, stream, a); break;
+    case 3: hipLaunchKernelGGL(prep_kernel<3>, grid, dim3(64), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL(prep_kernel<4>, grid, dim3(64), 0, stream, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.r == 0) return e;
+  const int64_t total = p.mpad * p.rpad16;
+  hipLaunchKernelGGL(treduce_kernel, dim3((unsigned)cdiv(total, 256)), dim3(256), 0,
+                     stream, (const float*)a.tpart,
+                     reinterpret_cast<uint16_t*>(ws + p.off_t), p.mpad, p.rpad32,
+                     p.rpad16, p.kchunks, lora_scale);
+  return hipGetLastError();
+}
+
+}  // namespace qerl

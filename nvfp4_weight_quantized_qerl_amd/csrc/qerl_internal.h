@@ -1,0 +1,76 @@
+// Host-side internals of libqerl: launch planning and kernel launchers.
+// Not part of the public ABI (include/qerl.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qerl {
+
+// Number of compute units of the current device (cached; 256 on MI355X,
+// and 256 when no device is visible so that sizing works on a host).
+int device_cu_count();
+
+// ---------------------------------------------------------------- quantizer
+hipError_t launch_quantize(const uint16_t* w, int64_t n, int64_t k,
+                           uint8_t* codes, uint8_t* scales, float* gscale,
+                           int32_t* flag, hipStream_t stream);
+
+// -------------------------------------------------------------------- noise
+hipError_t launch_aqn_sample(uint64_t seed, uint64_t stream_id,
+                             uint64_t call_id, double sigma, int64_t d,
+                             float* z, hipStream_t stream);
+
+// ------------------------------------------------------------------- linear
+// Workspace layout and launch shapes for one (m, n, k, r).
+struct LinearPlan {
+  int64_t m, n, k;
+  int r;
+  int64_t mpad;        // m rounded up to 32: rows of x_t and t
+  int rpad32;          // r rounded up to 32 (LoRA-down MFMA tiles), 0 if r == 0
+  int rpad16;          // r rounded up to 16: row stride of t (bf16)
+  int kchunks;         // K chunks of the LoRA-down partial sums
+  int64_t kchunk;      // multiple of 16
+  // decode main kernel (per m-chunk of at most 128 rows)
+  int dec_mt;          // 32-row m tiles per launch: 1, 2 or 4
+  int dec_nt;          // 32-row n subtiles per wave
+  int dec_rows;        // weight rows per workgroup (<= 32 * dec_nt)
+  int dec_groups;      // row groups = ceil(n / dec_rows)
+  int dec_split;       // K splits across workgroups
+  int64_t dec_kblk_per_split;  // 64-wide K blocks per split
+  // prefill main kernel
+  int pf_tile_m, pf_tile_n;
+  // workspace byte offsets
+  size_t off_xt, off_tpart, off_t, off_cnt, off_ypart, total;
+};
+
+bool make_linear_plan(int64_t m, int64_t n, int64_t k, int r, LinearPlan* p);
+
+hipError_t launch_linear_prepare(const LinearPlan& p, const uint16_t* x,
+                                 const float* z, const uint16_t* lora_a,
+                                 float lora_scale, char* ws,
+                                 hipStream_t stream);
+
+hipError_t launch_linear_decode_main(const LinearPlan& p,
+                                     const uint8_t* codes,
+                                     const uint8_t* scales,
+                                     const float* gscale,
+                                     const uint16_t* lora_b, uint16_t* y,
+                                     char* ws, hipStream_t stream);
+
+// Decode contraction over m in chunks of at most 128 rows (also the
+// fallback of the prefill entry point for shapes its tiles do not cover).
+hipError_t run_decode_chunks(const LinearPlan& p, const uint8_t* codes,
+                             const uint8_t* scales, const float* gscale,
+                             const uint16_t* lora_b, uint16_t* y, char* ws,
+                             hipStream_t stream);
+
+hipError_t launch_linear_prefill_main(const LinearPlan& p,
+                                      const uint8_t* codes,
+                                      const uint8_t* scales,
+                                      const float* gscale,
+                                      const uint16_t* lora_b, uint16_t* y,
+                                      char* ws, hipStream_t stream);
+
+}  // namespace qerl

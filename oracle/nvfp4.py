@@ -90,6 +90,38 @@ def element_magnitude_codes(a, unit):
     return code.astype(np.uint8)
 
 
+def tensor_amax(w):
+    """Step 1: amax = max |w| over the whole tensor (fp64 values)."""
+    w = np.asarray(w, dtype=np.float64)
+    if not np.all(np.isfinite(w)):
+        raise NonFiniteWeight("non-finite weight")
+    return float(np.abs(w).max()) if w.size else 0.0
+
+
+def encode_with_scale(w, S):
+    """Steps 3-5 for rows of a tensor whose global scale S is already known.
+
+    Returns (codes [rows, K/2] uint8, scales [rows, K/16] uint8).  Lets a
+    test check sampled rows of a large tensor: S depends on the whole
+    tensor, every other step only on the row's own blocks.
+    """
+    w = np.asarray(w, dtype=np.float64)
+    if w.ndim != 2 or w.shape[1] % BLOCK:
+        raise ValueError("expected W[N, K] with K a multiple of 16")
+    n, k = w.shape
+    a = np.abs(w)
+    sign = np.signbit(w).astype(np.uint8)
+    amax_b = a.reshape(n, k // BLOCK, BLOCK).max(axis=2) if a.size else \
+        np.zeros((n, k // BLOCK))
+    scodes = block_scale_codes(amax_b, S)
+    s_b = E4M3_VALUES[scodes]
+    unit = np.repeat(s_b * float(S), BLOCK, axis=1)      # exact products
+    mag = element_magnitude_codes(a, unit)
+    codes4 = mag | (sign << 3)
+    packed = (codes4[:, 0::2] | (codes4[:, 1::2] << 4)).astype(np.uint8)
+    return packed, scodes
+
+
 def quantize_values(w):
     """Quantize a real-valued [N, K] array (fp64 values) to NVFP4.
 
@@ -100,21 +132,8 @@ def quantize_values(w):
     w = np.asarray(w, dtype=np.float64)
     if w.ndim != 2 or w.shape[1] % BLOCK:
         raise ValueError("expected W[N, K] with K a multiple of 16")
-    n, k = w.shape
-    if not np.all(np.isfinite(w)):
-        raise NonFiniteWeight("non-finite weight")
-    a = np.abs(w)
-    sign = np.signbit(w).astype(np.uint8)
-    amax = float(a.max()) if a.size else 0.0
-    S = global_scale(amax)
-    amax_b = a.reshape(n, k // BLOCK, BLOCK).max(axis=2) if a.size else \
-        np.zeros((n, k // BLOCK))
-    scodes = block_scale_codes(amax_b, S)
-    s_b = E4M3_VALUES[scodes]
-    unit = np.repeat(s_b * float(S), BLOCK, axis=1)      # exact products
-    mag = element_magnitude_codes(a, unit)
-    codes4 = mag | (sign << 3)
-    packed = (codes4[:, 0::2] | (codes4[:, 1::2] << 4)).astype(np.uint8)
+    S = global_scale(tensor_amax(w))
+    packed, scodes = encode_with_scale(w, S)
     return packed, scodes, S
 
 

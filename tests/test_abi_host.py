@@ -1,0 +1,123 @@
+"""Host-side checks of the C ABI (no GPU needed): the built library loads,
+exports every call include/qerl.h declares, validates its arguments before
+touching the device, and its pure host call (the sigma schedule) matches
+the oracle."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import aqn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qerl.h")
+
+q = pytest.importorskip("nvfp4_weight_quantized_qerl_amd")
+lib = q.lib
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"QERL_API\s+[\w\s\*]+?\b(qerl_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) >= 11
+    for name in names:
+        assert hasattr(lib, name), name
+    # and the binding declares every one of them with the same name
+    from nvfp4_weight_quantized_qerl_amd import _lib
+    assert sorted(_lib.SIGNATURES) == names
+    for name in names:
+        if name not in ("qerl_status_string", "qerl_abi_version",
+                        "qerl_linear_workspace_bytes"):
+            assert hasattr(q, name), name
+
+
+def test_status_strings():
+    for s in range(7):
+        assert lib.qerl_status_string(s).decode().startswith("QERL_")
+    assert b"unknown" in lib.qerl_status_string(99)
+    assert lib.qerl_abi_version() == 1
+
+
+FAKE = ctypes.c_void_p(0x10000)        # aligned, never dereferenced on error
+MIS = ctypes.c_void_p(0x10008)         # 8-byte aligned only
+
+
+def test_quantize_validation():
+    f = lib.qerl_quantize_nvfp4
+    assert f(None, 4, 32, FAKE, FAKE, FAKE, None, None) == 1
+    assert f(FAKE, 4, 32, FAKE, None, FAKE, None, None) == 1
+    assert f(FAKE, 0, 32, FAKE, FAKE, FAKE, None, None) == 2
+    assert f(FAKE, 4, 24, FAKE, FAKE, FAKE, None, None) == 2
+    assert f(FAKE, 4, 0, FAKE, FAKE, FAKE, None, None) == 2
+    assert f(MIS, 4, 32, FAKE, FAKE, FAKE, None, None) == 3
+    assert f(FAKE, 4, 32, MIS, FAKE, FAKE, None, None) == 3
+
+
+def test_sigma_matches_oracle_and_validates():
+    out = ctypes.c_double()
+    for K in range(1, 13):
+        for k in range(0, K + 1):
+            for s0, s1 in [(1e-2, 5e-4), (0.1, 0.1), (3e-3, 7e-2)]:
+                assert lib.qerl_aqn_sigma(s0, s1, K, k, ctypes.byref(out)) == 0
+                ref = aqn.sigma(s0, s1, K, k)
+                assert abs(out.value - ref) <= np.spacing(ref), (K, k)
+    assert lib.qerl_aqn_sigma(1e-2, 5e-4, 10, 11, ctypes.byref(out)) == 4
+    assert lib.qerl_aqn_sigma(1e-2, 5e-4, 10, -1, ctypes.byref(out)) == 4
+    assert lib.qerl_aqn_sigma(0.0, 5e-4, 10, 1, ctypes.byref(out)) == 4
+    assert lib.qerl_aqn_sigma(1e-2, float("inf"), 10, 1, ctypes.byref(out)) == 4
+    assert lib.qerl_aqn_sigma(1e-2, 5e-4, 0, 0, ctypes.byref(out)) == 4
+    assert lib.qerl_aqn_sigma(1e-2, 5e-4, 10, 1, None) == 1
+    assert q.qerl_aqn_sigma(1e-2, 5e-4, 10, 1) == 1e-2
+
+
+def test_sample_validation():
+    f = lib.qerl_aqn_sample
+    assert f(0, 0, 0, 0.01, 16, None, None) == 1
+    assert f(0, 0, 0, 0.01, 0, FAKE, None) == 2
+    assert f(0, 0, 0, -0.01, 16, FAKE, None) == 4
+    assert f(0, 0, 0, float("nan"), 16, FAKE, None) == 4
+    assert f(0, 0, 0, 0.01, 16, ctypes.c_void_p(0x10002), None) == 3
+
+
+def test_workspace_sizes():
+    ws = lib.qerl_linear_workspace_bytes
+    assert ws(0, 8, 32, 0) == 0 and ws(4, 0, 32, 0) == 0
+    assert ws(4, 8, 24, 0) == 0 and ws(4, 8, 32, 129) == 0 and ws(4, 8, 32, -1) == 0
+    small = ws(4, 512, 256, 8)
+    assert small >= 32 * 256 * 2            # at least the padded x_t
+    big = ws(64, 37888, 3584, 32)
+    assert big >= 64 * 3584 * 2 and big < 37888 * 3584 // 2   # never O(n k)
+    assert ws(4096, 3584, 18944, 32) >= 4096 * 18944 * 2
+
+
+def test_linear_validation():
+    W = lib.qerl_linear_workspace_bytes(4, 64, 64, 8)
+    dec = lib.qerl_linear_decode
+    args = lambda **kw: [kw.get("x", FAKE), kw.get("m", 4), kw.get("codes", FAKE), FAKE, FAKE,
+                         kw.get("n", 64), kw.get("k", 64), kw.get("a", FAKE), kw.get("b", FAKE),
+                         kw.get("r", 8), kw.get("s", 2.0), kw.get("z", None), kw.get("y", FAKE),
+                         kw.get("ws", FAKE), kw.get("wsb", W), None]
+    assert dec(*args(x=None)) == 1
+    assert dec(*args(y=None)) == 1
+    assert dec(*args(a=None)) == 1          # LoRA A without B
+    assert dec(*args(m=0)) == 2
+    assert dec(*args(k=40)) == 2
+    assert dec(*args(r=200)) == 4
+    assert dec(*args(s=float("inf"))) == 4
+    assert dec(*args(codes=MIS)) == 3
+    assert dec(*args(z=ctypes.c_void_p(0x10004))) == 3
+    assert dec(*args(ws=ctypes.c_void_p(0x10010))) == 3
+    assert dec(*args(wsb=W - 1)) == 5
+    pre = lib.qerl_linear_prepare
+    assert pre(None, 4, 64, 64, None, 0, 1.0, None, FAKE, W, None) == 1
+    assert pre(FAKE, 4, 64, 64, None, 8, 1.0, None, FAKE, W, None) == 1
+    assert pre(FAKE, 4, 64, 64, FAKE, 8, 1.0, None, FAKE, 1, None) == 5
+    dp = lib.qerl_linear_decode_prepared
+    assert dp(4, FAKE, FAKE, FAKE, 64, 64, None, 8, FAKE, FAKE, W, None) == 1
+    assert dp(4, FAKE, FAKE, FAKE, 64, 64, FAKE, 8, FAKE, FAKE, 16, None) == 5

@@ -1,0 +1,155 @@
+"""GPU linear-layer parity: qerl_linear_decode / qerl_linear_prefill (bf16
+out) against the fp64 oracle, max relative error <= 2e-2 with the
+rms(y*) floor, on the tiny layer in full, on ragged and degenerate shapes,
+and on the full-size decode and prefill layers (sampled columns).
+
+Error budget of the HIP path (all relative to the output scale): rounding
+x_t = x (1 + z) to bf16 (2^-9 per element, averaging out over k),
+rounding s x_t A^T to bf16 (2^-9 of the LoRA term), fp32 accumulation,
+and the bf16 output rounding (2^-9).  Observed errors are ~4e-3; the 2e-2
+bound leaves a wide margin and still catches any wrong index, scale or
+sign."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import aqn, formats, linear, nvfp4
+from workloads import make_layer, CONFIGS
+from tests._gpu import dev16, host, oracle_noise, oracle_columns
+
+pytestmark = pytest.mark.gpu
+import nvfp4_weight_quantized_qerl_amd as q   # noqa: E402
+
+TOL = 2e-2
+
+
+class GpuLayer:
+    """Device copies of a layer's inputs, quantized on the GPU."""
+
+    def __init__(self, L, num_stages=10):
+        self.L = L
+        self.x = dev16(L.x)
+        wdev = dev16(L.w)
+        self.codes, self.scales, self.S, flag = q.qerl_quantize_nvfp4(wdev)
+        del wdev
+        self.a = None if L.a is None else dev16(L.a)
+        self.b = None if L.b is None else dev16(L.b)
+        self.z = None
+        if L.stage > 0:
+            sig = q.qerl_aqn_sigma(1e-2, 5e-4, num_stages, L.stage)
+            self.z = q.qerl_aqn_sample(L.seed, L.stream_id, L.call_id, sig, L.x.shape[1],
+                                       device="cuda:0")
+
+    def run(self, entry="decode", **kw):
+        fn = q.qerl_linear_decode if entry == "decode" else q.qerl_linear_prefill
+        y = fn(self.x, self.codes, self.scales, self.S, self.a, self.b, self.L.lora_scale,
+               self.z, **kw)
+        torch.cuda.synchronize()
+        return formats.bf16_bits_to_f64(host(y))
+
+
+def check(L, cols=None, entries=("decode", "prefill")):
+    g = GpuLayer(L)
+    z, _ = oracle_noise(L)
+    n = L.w.shape[0]
+    cols = np.arange(n) if cols is None else cols
+    ref = oracle_columns(L, cols, z)
+    errs = {}
+    for e in entries:
+        y = g.run(e)
+        assert y.shape == (L.x.shape[0], n)
+        err = linear.max_rel_error(y[:, cols], ref)
+        errs[e] = err
+        assert err <= TOL, (e, err)
+    return errs
+
+
+def test_tiny_layer_full():
+    cfg = CONFIGS["tiny"]
+    L = make_layer(cfg.m, cfg.layers[0].n, cfg.layers[0].k, cfg.r, seed=0, stage=cfg.stage)
+    errs = check(L)
+    assert max(errs.values()) < 1e-2
+
+
+@pytest.mark.parametrize("m,n,k,r,stage", [
+    (1, 64, 64, 8, 3),        # single token
+    (5, 17, 48, 0, 1),        # ragged n, k % 64 != 0, no LoRA
+    (33, 100, 272, 24, 2),    # ragged m / n / k, r not a multiple of 16
+    (64, 520, 1024, 32, 0),   # no noise
+    (130, 96, 512, 64, 5),    # m > 128: several m chunks
+    (2, 1, 16, 1, 1),         # one output, one K step, rank 1
+    (64, 96, 8192, 32, 1),    # few rows, long K: split-K across workgroups
+    (128, 640, 5120, 64, 1),  # m = 128 (4 m tiles)
+    (200, 300, 320, 16, 4),   # prefill-ish ragged
+])
+def test_shapes(m, n, k, r, stage):
+    L = make_layer(m, n, k, r, seed=m * 7 + n, stage=stage, outlier_frac=1e-3)
+    check(L)
+
+
+def test_no_noise_is_bit_identical_to_zero_noise_and_no_lora_b_zero():
+    L = make_layer(16, 256, 256, 8, seed=21, stage=0)
+    g = GpuLayer(L)
+    y0 = g.run()
+    g.z = torch.zeros(256, dtype=torch.float32, device="cuda:0")
+    assert np.array_equal(g.run(), y0)
+    g.z = None
+    g.b = torch.zeros_like(g.b)
+    yb0 = g.run()
+    g.a = g.b = None
+    assert np.array_equal(g.run(), yb0)
+
+
+def test_zero_weight_gives_lora_only():
+    L = make_layer(8, 64, 128, 8, seed=22, stage=2)
+    L.w = np.zeros_like(L.w)
+    g = GpuLayer(L)
+    assert float(host(g.S)[0]) == 0.0
+    z, _ = oracle_noise(L)
+    ref = 2.0 * linear.lora_down(L.x, z, L.a) @ formats.bf16_bits_to_f64(L.b).T
+    assert linear.max_rel_error(g.run(), ref) <= TOL
+
+
+def test_deterministic_and_prepared_halves():
+    L = make_layer(64, 96, 8192, 32, seed=23, stage=1)
+    g = GpuLayer(L)
+    y1, y2 = g.run(), g.run()
+    assert np.array_equal(y1, y2)
+    m, k = L.x.shape
+    ws = q.workspace(m, 96, k, 32, "cuda:0")
+    q.qerl_linear_prepare(g.x, 96, g.a, L.lora_scale, g.z, ws)
+    y = torch.empty((m, 96), dtype=torch.bfloat16, device="cuda:0")
+    for _ in range(3):       # repeated contractions reuse the arrival counters
+        q.qerl_linear_decode_prepared(m, g.codes, g.scales, g.S, k, g.b, 32, y, ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(formats.bf16_bits_to_f64(host(y)), y1)
+
+
+def _sample_cols(n, seed, count=160):
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, n - 1], rng.choice(n, count, replace=False)]))
+
+
+@pytest.mark.parametrize("idx", [0, 1])
+def test_decode_7b_mlp_full_size(idx):
+    cfg = CONFIGS["decode_7b_mlp"]
+    s = cfg.layers[idx]
+    L = make_layer(cfg.m, s.n, s.k, cfg.r, seed=1 + idx, stage=cfg.stage,
+                   outlier_frac=cfg.outlier_frac, call_id=idx)
+    check(L, cols=_sample_cols(s.n, idx), entries=("decode",))
+
+
+@pytest.mark.parametrize("idx", [0, 1])
+def test_prefill_7b_full_size(idx):
+    cfg = CONFIGS["prefill_7b"]
+    s = cfg.layers[idx]
+    L = make_layer(cfg.m, s.n, s.k, cfg.r, seed=11 + idx, stage=cfg.stage, call_id=idx)
+    check(L, cols=_sample_cols(s.n, 10 + idx, 64), entries=("prefill",))
+
+
+@pytest.mark.parametrize("idx", [0, 3])
+def test_decode_32b_layer_shapes(idx):
+    cfg = CONFIGS["decode_32b_sweep"]
+    s = cfg.layers[idx]
+    L = make_layer(cfg.m, s.n, s.k, cfg.r, seed=31 + idx, stage=cfg.stage, call_id=idx)
+    check(L, cols=_sample_cols(s.n, 30 + idx, 96), entries=("decode",))
