@@ -1,0 +1,263 @@
+"""Benchmark of the NVFP4 + LoRA + AQN linear layer on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu]
+
+A step is one rollout decode pass through a Qwen2.5-7B-shaped MLP block
+with M = 64 tokens (8 prompts x 8 samples): for each of the fused gate/up
+layer W [37888, 3584] and the down layer W [3584, 18944] (NVFP4, LoRA rank
+32, s = 2), draw the layer's AQN noise vector for stage 1 of 10 and run
+the linear layer (noisy activations, LoRA-down, NVFP4 contraction, LoRA-up
+epilogue).  The weights are quantized once before timing (the pages load
+the quantized model once); the quantizer is timed on its own.  Six copies
+of the quantized weights (684 MB) are used in rotation so that the 256 MB
+Infinity Cache cannot serve them; inputs are resident in HBM before the
+timed region.
+
+Printed: one JSON line.  `value` = decode weight-stream GB/s (algorithmic
+bytes of the step / step time); `roofline` = the decode contraction kernel
+of the gate/up layer, timed alone with HIP events on its launch stream;
+`prefill` = the 4096-token prefill of the Qwen2.5-7B qkv and down layers
+in TFLOP/s; `quantizer` = bulk quantization GB/s; `cpu_baseline` = the
+oracle on the host cores on a bounded slice of the same step.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--copies", type=int, default=6)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    return ap.parse_args()
+
+
+def linear_bytes(m, n, k, r):
+    """Algorithmic bytes of one linear call: NVFP4 codes + scales, x, y,
+    LoRA A and B (bf16), noise vector (fp32)."""
+    return 0.5625 * n * k + 2 * m * k + 2 * m * n + 2 * r * (k + n) + 4 * k
+
+
+def main_kernel_bytes(m, n, k, r):
+    """Algorithmic bytes of the decode contraction kernel alone: codes +
+    scales, x_t (bf16), y, the LoRA B factor and t = s x_t A^T (bf16)."""
+    return 0.5625 * n * k + 2 * m * k + 2 * m * n + 2 * r * n + 2 * m * r
+
+
+def linear_flops(m, n, k, r):
+    return 2.0 * m * n * k + 2.0 * m * r * (k + n)
+
+
+def source_digest(*names):
+    h = hashlib.sha256()
+    for name in names:
+        with open(os.path.join(ROOT, "nvfp4_weight_quantized_qerl_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel_key, digest):
+    """HBM bytes per launch from the committed rocprofv3 counter summary,
+    if it was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(kernel_key)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_digest") != digest:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not "
+              "supported (the layer would shard by output rows with no exchange; see "
+              "DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import nvfp4_weight_quantized_qerl_amd as q
+    from workloads import CONFIGS, make_layer
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+    stream = torch.cuda.current_stream()
+
+    cfg = CONFIGS["decode_7b_mlp"]
+    M, R = cfg.m, cfg.r
+    layers = []
+    for i, s in enumerate(cfg.layers):
+        L = make_layer(M, s.n, s.k, R, seed=1 + i, stage=cfg.stage,
+                       outlier_frac=cfg.outlier_frac, call_id=i)
+        layers.append(dict(name=s.name, n=s.n, k=s.k, L=L, x=to_dev(L.x), w=to_dev(L.w),
+                           a=to_dev(L.a), b=to_dev(L.b)))
+
+    # ---- quantize once (timed on its own: bulk quantizer GB/s)
+    torch.cuda.synchronize()
+    qtimes = []
+    for rep in range(3):
+        t0 = time.perf_counter()
+        for ly in layers:
+            ly["codes"], ly["scales"], ly["S"], ly["flag"] = q.qerl_quantize_nvfp4(ly["w"])
+        torch.cuda.synchronize()
+        qtimes.append(time.perf_counter() - t0)
+    q_elems = sum(ly["n"] * ly["k"] for ly in layers)
+    q_bytes = 2.5625 * q_elems
+    assert all(int(ly["flag"].item()) == 0 for ly in layers)
+
+    sigma = q.qerl_aqn_sigma(cfg.sigma_start, cfg.sigma_end, cfg.num_stages, cfg.stage)
+    copies = max(1, args.copies)
+    for ly in layers:
+        ly["rot"] = [(ly["codes"], ly["scales"])] + [
+            (ly["codes"].clone(), ly["scales"].clone()) for _ in range(copies - 1)]
+        ly["z"] = torch.empty(ly["k"], dtype=torch.float32, device=dev)
+        ly["ws"] = q.workspace(M, ly["n"], ly["k"], R, dev)
+        ly["y"] = torch.empty((M, ly["n"]), dtype=torch.bfloat16, device=dev)
+        del ly["w"]
+    torch.cuda.empty_cache()
+
+    def step(i):
+        for li, ly in enumerate(layers):
+            codes, scales = ly["rot"][i % copies]
+            q.qerl_aqn_sample(ly["L"].seed, 0, 2 * i + li, sigma, ly["k"], out=ly["z"])
+            q.qerl_linear_decode(ly["x"], codes, scales, ly["S"], ly["a"], ly["b"],
+                                 cfg.lora_scale, ly["z"], workspace=ly["ws"], y=ly["y"])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    ms_per_step = 1e3 * dt / args.steps
+    step_bytes = sum(linear_bytes(M, ly["n"], ly["k"], R) for ly in layers)
+    value = step_bytes / (dt / args.steps) / 1e9
+
+    # ---- dominant kernel alone: gate/up contraction, HIP events on its stream
+    ly = layers[0]
+    q.qerl_linear_prepare(ly["x"], ly["n"], ly["a"], cfg.lora_scale, ly["z"], ly["ws"])
+    reps = max(20, args.steps)
+    for i in range(5):
+        c, s = ly["rot"][i % copies]
+        q.qerl_linear_decode_prepared(M, c, s, ly["S"], ly["k"], ly["a"], ly["b"],
+                                      cfg.lora_scale, ly["y"], ly["ws"])
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for i in range(reps):
+        c, s = ly["rot"][i % copies]
+        q.qerl_linear_decode_prepared(M, c, s, ly["S"], ly["k"], ly["a"], ly["b"],
+                                      cfg.lora_scale, ly["y"], ly["ws"])
+    ev1.record(stream)
+    ev1.synchronize()
+    kern_s = ev0.elapsed_time(ev1) / 1e3 / reps
+    kbytes = main_kernel_bytes(M, ly["n"], ly["k"], R)
+    achieved = kbytes / kern_s / 1e9
+    digest = source_digest("decode_kernel.h", "qerl_device.h")
+    traffic = measured_traffic("decode_main_gate_up_7b", digest)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic, "kernel": "decode_main (gate/up 37888x3584, M=64, r=32)",
+                "avg_launch_us": round(kern_s * 1e6, 2), "bytes_per_launch": kbytes}
+
+    # ---- prefill (Qwen2.5-7B qkv and down, 4096 tokens): TFLOP/s
+    prefill = None
+    if not args.no_prefill:
+        pc = CONFIGS["prefill_7b"]
+        psig = q.qerl_aqn_sigma(pc.sigma_start, pc.sigma_end, pc.num_stages, pc.stage)
+        ptimes, pflops = [], 0.0
+        for i, s in enumerate(pc.layers):
+            L = make_layer(pc.m, s.n, s.k, pc.r, seed=11 + i, stage=pc.stage, call_id=i)
+            x, w, a, b = to_dev(L.x), to_dev(L.w), to_dev(L.a), to_dev(L.b)
+            codes, scales, S, _ = q.qerl_quantize_nvfp4(w)
+            del w
+            z = q.qerl_aqn_sample(L.seed, 0, i, psig, s.k, device=dev)
+            ws = q.workspace(pc.m, s.n, s.k, pc.r, dev)
+            y = torch.empty((pc.m, s.n), dtype=torch.bfloat16, device=dev)
+            for _ in range(2):
+                q.qerl_linear_prefill(x, codes, scales, S, a, b, pc.lora_scale, z,
+                                      workspace=ws, y=y)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            preps = 5
+            e0.record(stream)
+            for _ in range(preps):
+                q.qerl_linear_prefill(x, codes, scales, S, a, b, pc.lora_scale, z,
+                                      workspace=ws, y=y)
+            e1.record(stream)
+            e1.synchronize()
+            ptimes.append(e0.elapsed_time(e1) / 1e3 / preps)
+            pflops += linear_flops(pc.m, s.n, s.k, pc.r)
+            del x, a, b, codes, scales, ws, y
+        ptf = pflops / sum(ptimes) / 1e12
+        prefill = {"workload": "prefill_7b (qkv 4608x3584 + down 3584x18944, M=4096, r=32)",
+                   "tflops": round(ptf, 1), "ms": round(1e3 * sum(ptimes), 3),
+                   "frac_bf16_peak": round(ptf / BF16_PEAK_TFLOPS, 4)}
+
+    # ---- oracle on the host cores: bounded slice of the same step
+    cpu = None
+    if not args.no_cpu:
+        from oracle import aqn, formats, linear, nvfp4
+        cores = len(os.sched_getaffinity(0))
+        frac_rows = 0.04
+        t0 = time.perf_counter()
+        cbytes = 0.0
+        for li, ly in enumerate(layers):
+            L = ly["L"]
+            rows = max(16, int(frac_rows * ly["n"]))
+            w = formats.bf16_bits_to_f64(L.w[:rows])
+            S = nvfp4.global_scale(nvfp4.tensor_amax(w))
+            codes, scales = nvfp4.encode_with_scale(w, S)
+            sig = aqn.sigma(cfg.sigma_start, cfg.sigma_end, cfg.num_stages, cfg.stage)
+            z = aqn.sample(L.seed, 0, li, sig, ly["k"])
+            w_hat = nvfp4.dequantize(codes, scales, S)
+            linear.linear(L.x, w_hat, z, L.a, L.b[:rows], cfg.lora_scale)
+            cbytes += linear_bytes(M, rows, ly["k"], R)
+        cdt = time.perf_counter() - t0
+        cpu = {"value": round(cbytes / cdt / 1e9, 4), "unit": "GB/s", "cores": cores,
+               "kind": "oracle",
+               "sample": f"{frac_rows:.0%} of the output rows of both layers "
+                         "(quantize the slice, sample z, dequantize, fp64 linear), "
+                         f"{cdt:.1f} s"}
+
+    out = {
+        "metric": "NVFP4+LoRA linear: decode weight-stream GB/s and prefill TFLOP/s, % roofline",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 (NVFP4 weights)", "data": "synthetic",
+        "config": {"workload": "decode_7b_mlp: Qwen2.5-7B-shaped MLP, M=64 (8 prompts x 8 "
+                               "samples), gate/up 37888x3584 + down 3584x18944 NVFP4, LoRA "
+                               "r=32, AQN stage 1/10", "global_batch": M,
+                   "weight_copies_rotated": copies, "parallelism": "none (1 GPU)"},
+        "roofline": roofline,
+        "step_frac_hbm": round(value / HBM_PEAK_GBS, 4),
+        "prefill": prefill,
+        "quantizer": {"GB_per_s": round(q_bytes / min(qtimes) / 1e9, 1),
+                      "elements": q_elems, "bytes_per_elem": 2.5625},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

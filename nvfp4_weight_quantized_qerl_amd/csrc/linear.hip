@@ -10,13 +10,16 @@
 // epilogue, so the in-register dequantized weight W0 = e2m1 * s_b is exact
 // in bf16.
 //
-// prepare (one wave per 32 rows x K chunk):
-//   x_t   = bf16(x * (1 + z))  -> workspace, rows padded to a multiple of 32
-//           with zeros so the contraction kernels need no row masks;
-//   tpart = x_t A^T over the chunk (bf16 MFMA, fp32) -> workspace;
-//   it also clears the split-K arrival counters of the decode kernel.
-// treduce: t = bf16(s * sum over chunks of tpart), summed in chunk order so
-//   the result is deterministic.
+// prepare writes x_t = bf16(x * (1 + z)) to the workspace, rows padded to a
+// multiple of 32 with zeros so the contraction kernels need no row masks,
+// and clears the split-K arrival counters of the decode kernel.  When the
+// plan does not compute the LoRA-down inside the decode contraction
+// (plan.dec_rt == 0), it also produces t:
+//   prep_kernel (one wave per 32 rows x K chunk): x_t and
+//           tpart = x_t A^T over the chunk (bf16 MFMA, fp32);
+//   treduce: t = bf16(s * sum over chunks of tpart), summed in chunk order
+//           so the result is deterministic.
+// Otherwise a single elementwise kernel (xt_kernel) writes x_t.
 #include <algorithm>
 
 #include "qerl_device.h"
@@ -41,12 +44,34 @@ namespace {
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int64_t rup(int64_t a, int64_t b) { return cdiv(a, b) * b; }
 
-int decode_nt_max(int mt) { return mt == 1 ? 6 : (mt == 2 ? 5 : 3); }
+// In-kernel LoRA-down needs RT more accumulator tiles per wave; at the
+// decode shapes that pushes the wave to the register limit and the compiler
+// then sinks the prefetch loads, so the prepare step computes it instead.
+constexpr bool kDecodeInKernelLora = false;
 
-// Decode rows-per-workgroup and split-K choice for one m tile count.
+// Largest weight subtile count NT per wave that the decode kernel holds in
+// registers without spilling, for MT token tiles and RT in-kernel LoRA-down
+// tiles (measured from the compiler's resource report).
+int decode_nt_max(int mt, int rt) {
+  static const int table[3][3] = {{6, 6, 6}, {5, 5, 3}, {3, 2, 0}};
+  const int mi = mt == 1 ? 0 : (mt == 2 ? 1 : 2);
+  return rt <= 2 ? table[mi][rt] : 0;
+}
+
+// Decode rows-per-workgroup, LoRA-down placement and split-K choice for one
+// m tile count.  The LoRA-down runs inside the contraction (RT extra
+// accumulator tiles, no separate kernels) when that still leaves >= 4
+// weight subtiles, i.e. costs at most half as much MFMA work as the
+// weights.
 void plan_decode(LinearPlan* p, int mt) {
   const int cu = device_cu_count();
-  const int ntmax = decode_nt_max(mt);
+  const int rt = p->rpad32 / 32;
+  int ntmax = decode_nt_max(mt, 0);
+  p->dec_rt = 0;
+  if (kDecodeInKernelLora && rt > 0 && rt <= 2 && decode_nt_max(mt, rt) >= 4) {
+    p->dec_rt = rt;
+    ntmax = decode_nt_max(mt, rt);
+  }
   const int64_t n = p->n;
   const int64_t units = cdiv(p->k, 64);     // 64-wide K blocks (last may be partial)
   const int64_t rows_per_cu = cdiv(n, cu);
@@ -120,6 +145,10 @@ bool make_linear_plan(int64_t m, int64_t n, int64_t k, int r, LinearPlan* p) {
   p->off_ypart = take(p->dec_split > 1
                           ? (size_t)p->dec_split * 32 * p->dec_mt * n * 4
                           : 0);
+  p->off_tsplit = take(p->dec_split > 1 && p->dec_rt > 0
+                           ? (size_t)p->dec_groups * p->dec_split * 32 * p->dec_mt *
+                                 p->rpad32 * 4
+                           : 0);
   p->total = off;
   return true;
 }
@@ -151,7 +180,8 @@ __global__ __launch_bounds__(64) void prep_kernel(PrepArgs p) {
   const bool live = mrow < p.m;
   const uint16_t* xrow = p.x + mrow * p.k;
   uint16_t* xtrow = p.xt + mrow * p.k;
-  for (int64_t k0 = kbeg + 8 * h; k0 < kend; k0 += 16) {
+  for (int64_t ks = kbeg; ks < kend; ks += 16) {
+    const int64_t k0 = ks + 8 * h;
     uint4 xv = live ? *reinterpret_cast<const uint4*>(xrow + k0)
                     : make_uint4(0u, 0u, 0u, 0u);
     if (p.z) {
@@ -183,6 +213,33 @@ __global__ __launch_bounds__(64) void prep_kernel(PrepArgs p) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) dst[(int64_t)acc_row(v, lane) * p.rpad32] = acc[t][v];
   }
+}
+
+// x_t = bf16(x (1 + z)) only (the decode kernel computes the LoRA-down
+// itself): 8 elements per thread; rows m..mpad-1 are written as zeros.
+__global__ __launch_bounds__(256) void xt_kernel(PrepArgs p) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < p.ncnt) p.cnt[i] = 0u;
+  const int64_t per_row = p.k / 8;
+  if (i >= p.mpad * per_row) return;
+  const int64_t mrow = i / per_row, k0 = (i % per_row) * 8;
+  uint4 xv = make_uint4(0u, 0u, 0u, 0u);
+  if (mrow < p.m) {
+    xv = *reinterpret_cast<const uint4*>(p.x + mrow * p.k + k0);
+    if (p.z) {
+      const float4 z0 = *reinterpret_cast<const float4*>(p.z + k0);
+      const float4 z1 = *reinterpret_cast<const float4*>(p.z + k0 + 4);
+      xv.x = pack_bf16x2(bf16_to_f32(xv.x & 0xffffu) * (1.0f + z0.x),
+                         bf16_to_f32(xv.x >> 16) * (1.0f + z0.y));
+      xv.y = pack_bf16x2(bf16_to_f32(xv.y & 0xffffu) * (1.0f + z0.z),
+                         bf16_to_f32(xv.y >> 16) * (1.0f + z0.w));
+      xv.z = pack_bf16x2(bf16_to_f32(xv.z & 0xffffu) * (1.0f + z1.x),
+                         bf16_to_f32(xv.z >> 16) * (1.0f + z1.y));
+      xv.w = pack_bf16x2(bf16_to_f32(xv.w & 0xffffu) * (1.0f + z1.z),
+                         bf16_to_f32(xv.w >> 16) * (1.0f + z1.w));
+    }
+  }
+  *reinterpret_cast<uint4*>(p.xt + mrow * p.k + k0) = xv;
 }
 
 __global__ __launch_bounds__(256) void treduce_kernel(const float* __restrict__ tpart,
@@ -219,6 +276,12 @@ hipError_t launch_linear_prepare(const LinearPlan& p, const uint16_t* x,
   a.r = p.r;
   a.rpad32 = p.rpad32;
   a.ncnt = p.dec_groups;
+  if (p.r == 0 || p.dec_rt > 0 || !lora_a) {
+    // The decode contraction computes the LoRA-down (or there is none).
+    const int64_t threads = std::max<int64_t>(p.mpad * p.k / 8, a.ncnt);
+    hipLaunchKernelGGL(xt_kernel, dim3((unsigned)cdiv(threads, 256)), dim3(256), 0, stream, a);
+    return hipGetLastError();
+  }
   const dim3 grid((unsigned)(p.mpad / 32), (unsigned)p.kchunks);
   switch (p.rpad32 / 32) {
     case 0: hipLaunchKernelGGL(prep_kernel<0>, grid, dim3(64), 0, stream, a); break;
@@ -229,7 +292,7 @@ hipError_t launch_linear_prepare(const LinearPlan& p, const uint16_t* x,
     default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.r == 0) return e;
+  if (e != hipSuccess) return e;
   const int64_t total = p.mpad * p.rpad16;
   hipLaunchKernelGGL(treduce_kernel, dim3((unsigned)cdiv(total, 256)), dim3(256), 0,
                      stream, (const float*)a.tpart,
