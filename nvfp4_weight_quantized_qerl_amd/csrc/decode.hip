@@ -3,6 +3,7 @@
 #include <algorithm>
 
 #include "decode_kernel.h"
+#include "decode_lds.h"
 #include "qerl_internal.h"
 
 namespace qerl {
@@ -14,6 +15,41 @@ static decode::DecodeKernel pick_decode(int mt, int nt, int rt) {
     case 4: return decode::pick_mt4(nt, rt);
     default: return nullptr;
   }
+}
+
+// LDS-staged contraction (decode_lds.h) for one chunk of <= 64 rows, when
+// k is a multiple of 256 and the LoRA-down is precomputed.
+static hipError_t run_decode_lds(const LinearPlan& p, int mt, const uint8_t* codes,
+                                 const uint8_t* scales, const float* gscale,
+                                 const uint16_t* t, const uint16_t* lora_b, int r,
+                                 int lora_vec, const uint16_t* xt, uint16_t* y, int m_valid,
+                                 char* ws, hipStream_t stream) {
+  dlds::Kernel kern = mt == 1 ? dlds::pick_mt1(p.dec_nt) : dlds::pick_mt2(p.dec_nt);
+  if (!kern) return hipErrorInvalidConfiguration;
+  dlds::Args a;
+  a.xt = xt;
+  a.codes = codes;
+  a.scales = scales;
+  a.gscale = gscale;
+  a.t = t;
+  a.lora_b = lora_b;
+  a.y = y;
+  a.ypart = reinterpret_cast<float*>(ws + p.off_ypart);
+  a.cnt = reinterpret_cast<uint32_t*>(ws + p.off_cnt);
+  a.n = p.n;
+  a.k = p.k;
+  const int64_t nblocks = p.k / 256;
+  int64_t per = (nblocks + p.dec_split - 1) / p.dec_split;
+  const int64_t split = (nblocks + per - 1) / per;
+  a.blocks_per_split = per;
+  a.m_valid = m_valid;
+  a.rows = p.dec_rows;
+  a.split = (int)split;
+  a.r = r;
+  a.rpad16 = p.rpad16;
+  a.lora_vec = lora_vec;
+  hipLaunchKernelGGL(kern, dim3((unsigned)p.dec_groups, (unsigned)split), dim3(256), 0, stream, a);
+  return hipGetLastError();
 }
 
 hipError_t run_decode_chunks(const LinearPlan& p, const uint8_t* codes,
@@ -51,12 +87,19 @@ hipError_t run_decode_chunks(const LinearPlan& p, const uint8_t* codes,
     const int64_t tiles_left = (p.mpad - m0) / 32;
     int mt = p.dec_mt;
     if (tiles_left < mt) mt = tiles_left >= 2 ? 2 : 1;
-    decode::DecodeKernel kern = pick_decode(mt, p.dec_nt, rt);
-    if (!kern) return hipErrorInvalidConfiguration;
     a.xt = xt + m0 * p.k;
     a.t = t + m0 * p.rpad16;
     a.y = y + m0 * p.n;
     a.m_valid = (int)std::min<int64_t>(32 * mt, p.m - m0);
+    if (mt <= 2 && rt == 0 && p.k % 256 == 0 && p.dec_nt <= 5) {
+      const hipError_t e = run_decode_lds(p, mt, codes, scales, gscale, a.t, lora_b, a.r,
+                                          a.lora_vec, a.xt, a.y, a.m_valid, ws, stream);
+      if (e != hipSuccess) return e;
+      m0 += 32 * mt;
+      continue;
+    }
+    decode::DecodeKernel kern = pick_decode(mt, p.dec_nt, rt);
+    if (!kern) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(kern, dim3((unsigned)p.dec_groups, (unsigned)p.dec_split),
                        dim3(256), 0, stream, a);
     const hipError_t e = hipGetLastError();

@@ -1,0 +1,345 @@
+// Decode contraction, LDS-staged variant (template; instantiated by
+// decode_lds_mt*.hip).  Same operation as decode_kernel.h:
+//     y = bf16(S * x_t W0^T + t B^T),  W0 = E2M1 codes (.) E4M3 scales
+// [QeRL summary, §3.4, Eq. 6 (NVFP4 dequantization) and Eq. 2 (LoRA)],
+// for m <= 64 tokens and k a multiple of 256.
+//
+// Memory path.  A workgroup owns `rows` weight rows and a range of
+// 256-wide K blocks.  Each block is copied global -> LDS by direct-to-LDS
+// buffer loads that the four waves issue together:
+//   codes   8 rows x 128 B per instruction (one cache line per row)
+//   scales  64 rows x 16 B per instruction
+//   x_t     2 rows x 512 B per instruction
+// so every load instruction touches few cache lines.  Inside a row the
+// 16-byte chunks are stored XOR-swizzled by the row index (chunk q of row r
+// at position q ^ (r mod 8)); the MFMA-layout reads (lane = row) then hit
+// eight different bank groups in every group of eight lanes.
+//
+// Pipeline.  Codes and scales are triple-buffered, x_t double-buffered.
+// Iteration i: wait for this wave's copies of block i (s_waitcnt with the
+// weight copies of block i+1 still in flight), s_barrier (now every wave's
+// copies of block i have landed and every wave has finished block i-1),
+// issue the copies of x_t(i+1) and weights(i+2) into the stages block i-1
+// used, then compute block i: each wave takes one 64-wide quarter of it.
+// The raw s_barrier is used instead of __syncthreads, whose memory fence
+// would wait for every copy in flight.
+#pragma once
+
+#include "qerl_device.h"
+
+namespace qerl {
+namespace dlds {
+
+struct Args {
+  const uint16_t* xt;      // [MT*32, k] bf16 rows of this m chunk
+  const uint8_t* codes;    // [n, k/2]
+  const uint8_t* scales;   // [n, k/16]
+  const float* gscale;
+  const uint16_t* t;       // [MT*32, rpad16] bf16 s x_t A^T, or null
+  const uint16_t* lora_b;  // [n, r] bf16
+  uint16_t* y;             // [m_valid, n]
+  float* ypart;            // [split, MT*32, n] fp32 partials
+  uint32_t* cnt;           // [groups] arrival counters (zero on entry)
+  int64_t n, k;
+  int64_t blocks_per_split;  // 256-wide K blocks per split
+  int m_valid, rows, split, r, rpad16, lora_vec;
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// 16 bytes per lane global -> LDS; lane l's data lands at dst + 16 l.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* dst, uint32_t voff,
+                                      uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)dst, 16, (int)voff, (int)soff, 0, 0);
+}
+
+// s_waitcnt vmcnt(N) (gfx9 encoding; expcnt and lgkmcnt left free).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0f70);
+}
+
+__device__ __forceinline__ void barrier_nofence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ uint32_t comp(const uint4& v, int j) {
+  return j == 0 ? v.x : (j == 1 ? v.y : (j == 2 ? v.z : v.w));
+}
+
+__device__ __forceinline__ uint4 load_lora_b(const Args& a, int64_t row, bool live, int j0) {
+  if (!live || j0 >= a.r) return make_uint4(0u, 0u, 0u, 0u);
+  const uint16_t* src = a.lora_b + row * a.r + j0;
+  if (a.lora_vec) return *reinterpret_cast<const uint4*>(src);
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t lo = (j0 + 2 * i < a.r) ? src[2 * i] : 0u;
+    const uint32_t hi = (j0 + 2 * i + 1 < a.r) ? src[2 * i + 1] : 0u;
+    w[i] = lo | (hi << 16);
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// acc (full K sum of one 32x32 tile) -> S * acc + t B^T -> y.
+__device__ __forceinline__ void epilogue_tile(const Args& a, f32x16_t acc, float S, int u,
+                                              int64_t row, bool live, int lane,
+                                              const uint16_t* t_lds) {
+  const int h = lane >> 5, c = lane & 31;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc[v] *= S;
+  if (a.r > 0) {
+    const uint16_t* trow = t_lds + (32 * u + c) * a.rpad16;
+    for (int j0 = 0; j0 < a.rpad16; j0 += 16) {
+      const uint4 tv = *reinterpret_cast<const uint4*>(trow + j0 + 8 * h);
+      const uint4 bv = load_lora_b(a, row, live, j0 + 8 * h);
+      acc = mfma_bf16(tv, bv, acc);
+    }
+  }
+  if (!live) return;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int mrow = 32 * u + acc_row(v, lane);
+    if (mrow < a.m_valid) a.y[(int64_t)mrow * a.n + row] = f32_to_bf16_bits(acc[v]);
+  }
+}
+
+template <int MT, int NT>
+__global__ __launch_bounds__(256, 1) void decode_lds(Args a) {
+  constexpr int NP = MT * NT;                 // 32x32 tiles per wave
+  constexpr int XROWS = 32 * MT;              // token rows
+  constexpr int WROWS = 32 * NT;              // weight rows staged per block
+  constexpr int CODE_INSTR = WROWS / 8;       // 8 rows per code copy
+  constexpr int XINSTR = XROWS / 2;           // 2 rows per x_t copy
+  constexpr int W_PER_WAVE = CODE_INSTR / 4 + 1;   // code copies + one scale copy
+  constexpr int X_PER_WAVE = XINSTR / 4;
+  static_assert(CODE_INSTR % 4 == 0 && XINSTR % 4 == 0, "copies split evenly over 4 waves");
+  // Reduction slices of 16 x 64 floats live in the two x_t stages after the
+  // main loop: 8 * MT slices, 3 per reduced tile.
+  constexpr int TPR = (MT * 8) / 3 >= 4 ? 4 : (MT * 8) / 3;   // tiles per round
+  constexpr int ROUNDS = (NP + TPR - 1) / TPR;
+
+  __shared__ __attribute__((aligned(16))) uint4 wc0[WROWS * 8], wc1[WROWS * 8], wc2[WROWS * 8];
+  __shared__ __attribute__((aligned(16))) uint4 sc0[256], sc1[256], sc2[256];
+  __shared__ __attribute__((aligned(16))) uint4 xs0[XROWS * 32], xs1[XROWS * 32];
+  __shared__ __attribute__((aligned(16))) uint16_t t_lds[XROWS * 128];
+  __shared__ int is_last;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h = lane >> 5, c = lane & 31;
+  const int64_t row0 = (int64_t)blockIdx.x * a.rows;
+  const int64_t row_end = min(a.n, row0 + (int64_t)a.rows);
+  const int split_id = blockIdx.y;
+  const int64_t nblocks = a.k / 256;
+  const int64_t bb = (int64_t)split_id * a.blocks_per_split;
+  const int64_t be = min(nblocks, bb + a.blocks_per_split);
+
+  if (a.r > 0) {
+    const int words = XROWS * a.rpad16 / 8;
+    for (int i = threadIdx.x; i < words; i += 256)
+      reinterpret_cast<uint4*>(t_lds)[i] = reinterpret_cast<const uint4*>(a.t)[i];
+  }
+
+  const uint32_t kbytes = (uint32_t)(a.k / 2), kscales = (uint32_t)(a.k / 16);
+  const uint32_t xrow = (uint32_t)a.k * 2;
+  const __amdgpu_buffer_rsrc_t rw = rsrc(a.codes + row0 * kbytes, (uint32_t)((a.n - row0) * kbytes));
+  const __amdgpu_buffer_rsrc_t rs = rsrc(a.scales + row0 * kscales, (uint32_t)((a.n - row0) * kscales));
+  const __amdgpu_buffer_rsrc_t rx = rsrc(a.xt, (uint32_t)XROWS * xrow);
+
+  // Per-lane parts of the copy addresses (see the file comment).
+  // codes copy j of this wave covers rows 8 (wave + 4 j) .. +7
+  const uint32_t cr = (uint32_t)(lane >> 3);
+  const uint32_t vcode = (8u * wave + cr) * kbytes + 16u * ((uint32_t)(lane & 7) ^ cr);
+  // scales copy of this wave covers rows 64 wave .. +63
+  const uint32_t vscale = (64u * wave + lane) * kscales;
+  // x_t copy j of this wave covers rows 2 (wave + 4 j) and 2 (wave + 4 j) + 1
+  const uint32_t xr = 2u * wave + (uint32_t)(lane >> 5);
+  const uint32_t vx = xr * xrow + 16u * ((uint32_t)(lane & 31) ^ (xr & 7u));
+
+  auto copy_w = [&](int64_t blk, uint4* wc, uint4* sc) {
+#pragma unroll
+    for (int j = 0; j < CODE_INSTR / 4; ++j)
+      dma16(rw, wc + (wave + 4 * j) * 64, vcode, 32u * j * kbytes + 128u * (uint32_t)blk);
+    dma16(rs, sc + wave * 64, vscale, 16u * (uint32_t)blk);
+  };
+  auto copy_x = [&](int64_t blk, uint4* xs) {
+#pragma unroll
+    for (int j = 0; j < XINSTR / 4; ++j)
+      dma16(rx, xs + (wave + 4 * j) * 64, vx, 8u * j * xrow + 512u * (uint32_t)blk);
+  };
+
+  bool live[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) live[t] = row0 + 32 * t + c < row_end;
+
+  f32x16_t acc[NT][MT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int u = 0; u < MT; ++u) acc[t][u] = zero16();
+
+  // This wave computes K quarter `wave` (64 wide) of every block.
+  auto compute = [&](const uint4* wc, const uint4* sc, const uint4* xs) {
+    uint4 w[NT];
+    float sb0[NT], sb1[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int r = 32 * t + c;
+      w[t] = wc[r * 8 + ((2 * wave + h) ^ (r & 7))];
+      const uint32_t sw = reinterpret_cast<const uint16_t*>(sc)[r * 8 + 2 * wave + h];
+      sb0[t] = e4m3_to_f32(sw & 0xffu);
+      sb1[t] = e4m3_to_f32((sw >> 8) & 0xffu);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint4 xa[MT];
+#pragma unroll
+      for (int u = 0; u < MT; ++u) {
+        const int r = 32 * u + c;
+        xa[u] = xs[r * 32 + ((8 * wave + 4 * h + j) ^ (r & 7))];
+      }
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const uint4 b = dequant8_bf16(comp(w[t], j), j < 2 ? sb0[t] : sb1[t]);
+#pragma unroll
+        for (int u = 0; u < MT; ++u) acc[t][u] = mfma_bf16(xa[u], b, acc[t][u]);
+      }
+    }
+  };
+
+  if (bb < be) {
+    const int64_t last = be - 1;
+    copy_w(bb, wc0, sc0);
+    copy_x(bb, xs0);
+    copy_w(min(bb + 1, last), wc1, sc1);
+    // Block bb + i uses weight stage i % 3 and x_t stage i % 2; period 6.
+#define QERL_LDS_STEP(OFF, WC, SC, XS, XN, WN, SN)                         \
+  wait_vmcnt<W_PER_WAVE>();                                                 \
+  barrier_nofence();                                                        \
+  copy_x(min(blk + (OFF) + 1, last), XN);                                   \
+  copy_w(min(blk + (OFF) + 2, last), WN, SN);                               \
+  compute(WC, SC, XS);                                                      \
+  if (blk + (OFF) + 1 >= be) break;
+    for (int64_t blk = bb;; blk += 6) {
+      QERL_LDS_STEP(0, wc0, sc0, xs0, xs1, wc2, sc2)
+      QERL_LDS_STEP(1, wc1, sc1, xs1, xs0, wc0, sc0)
+      QERL_LDS_STEP(2, wc2, sc2, xs0, xs1, wc1, sc1)
+      QERL_LDS_STEP(3, wc0, sc0, xs1, xs0, wc2, sc2)
+      QERL_LDS_STEP(4, wc1, sc1, xs0, xs1, wc0, sc0)
+      QERL_LDS_STEP(5, wc2, sc2, xs1, xs0, wc1, sc1)
+    }
+#undef QERL_LDS_STEP
+  }
+  // Every copy has landed and every wave is done with the stages.
+  wait_vmcnt<0>();
+  barrier_nofence();
+
+  // Sum the four waves' tiles through the (now free) x_t stages; in each
+  // round TPR tiles are reduced, tile p (of the round) by wave p.
+  auto slice = [&](int s) -> float* {
+    return s < 4 * MT ? reinterpret_cast<float*>(xs0) + s * 1024
+                      : reinterpret_cast<float*>(xs1) + (s - 4 * MT) * 1024;
+  };
+#pragma unroll
+  for (int rnd = 0; rnd < ROUNDS; ++rnd) {
+#pragma unroll
+    for (int p = TPR * rnd; p < NP && p < TPR * rnd + TPR; ++p) {
+      const int owner = p - TPR * rnd;
+      if (wave != owner) {
+        const int rank = wave - (wave > owner ? 1 : 0);
+        float* dst = slice(owner * 3 + rank) + lane;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) dst[v * 64] = acc[p / MT][p % MT][v];
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int p = TPR * rnd; p < NP && p < TPR * rnd + TPR; ++p) {
+      const int owner = p - TPR * rnd;
+      if (wave == owner) {
+#pragma unroll
+        for (int rank = 0; rank < 3; ++rank) {
+          const float* src = slice(owner * 3 + rank) + lane;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[p / MT][p % MT][v] += src[v * 64];
+        }
+      }
+    }
+    __syncthreads();
+  }
+  auto owns = [&](int p) { return wave == p % TPR; };
+
+  const float S = *a.gscale;
+  if (a.split == 1) {
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+      if (owns(p))
+        epilogue_tile(a, acc[p / MT][p % MT], S, p % MT, row0 + 32 * (p / MT) + c,
+                      live[p / MT], lane, t_lds);
+    return;
+  }
+
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    if (owns(p) && live[p / MT]) {
+      const int64_t row = row0 + 32 * (p / MT) + c;
+      float* dst = a.ypart + ((int64_t)split_id * XROWS + 32 * (p % MT)) * a.n + row;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) dst[(int64_t)acc_row(v, lane) * a.n] = acc[p / MT][p % MT][v];
+    }
+  }
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t old = __hip_atomic_fetch_add(a.cnt + blockIdx.x, 1u, __ATOMIC_ACQ_REL,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+    is_last = (old == (uint32_t)(a.split - 1)) ? 1 : 0;
+  }
+  __syncthreads();
+  if (!is_last) return;
+  __threadfence();
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    if (owns(p)) {
+      const int64_t row = row0 + 32 * (p / MT) + c;
+      f32x16_t sum = zero16();
+      if (live[p / MT]) {
+        for (int s = 0; s < a.split; ++s) {
+          const float* src = a.ypart + ((int64_t)s * XROWS + 32 * (p % MT)) * a.n + row;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) sum[v] += src[(int64_t)acc_row(v, lane) * a.n];
+        }
+      }
+      epilogue_tile(a, sum, S, p % MT, row, live[p / MT], lane, t_lds);
+    }
+  }
+  if (threadIdx.x == 0) a.cnt[blockIdx.x] = 0u;
+}
+
+typedef void (*Kernel)(Args);
+
+template <int MT>
+Kernel pick_nt(int nt) {
+  switch (nt) {
+    case 1: return decode_lds<MT, 1>;
+    case 2: return decode_lds<MT, 2>;
+    case 3: return decode_lds<MT, 3>;
+    case 4: return decode_lds<MT, 4>;
+    case 5: return decode_lds<MT, 5>;
+    default: return nullptr;
+  }
+}
+
+Kernel pick_mt1(int nt);
+Kernel pick_mt2(int nt);
+
+}  // namespace dlds
+}  // namespace qerl
