@@ -48,7 +48,7 @@ static hipError_t run_decode_lds(const LinearPlan& p, int mt, const uint8_t* cod
   a.r = r;
   a.rpad16 = p.rpad16;
   a.lora_vec = lora_vec;
-  hipLaunchKernelGGL(kern, dim3((unsigned)p.dec_groups, (unsigned)split), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(kern, dim3((unsigned)p.dec_groups, (unsigned)split), dim3(512), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -202,8 +202,11 @@ __global__ __launch_bounds__(256, 1) void decode_main(DecodeArgs a) {
                                               (uint32_t)((a.n - row0) * kscales));
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.xt, (uint32_t)mrows * xrow_bytes);
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.lora_a, (uint32_t)(RT > 0 ? a.r : 0) * xrow_bytes);
-  const uint32_t vw = (uint32_t)c * kbytes + 16u * h;      // + 32 t kbytes + 32 kb
-  const uint32_t vs = (uint32_t)c * kscales + 2u * h;      // + 32 t kscales + 4 kb
+  // Row offsets go into the per-lane offset, which the buffer range check
+  // covers (rows past the end of a tensor read as zeros); the uniform
+  // offset carries only the position along K.
+  const uint32_t vw = (uint32_t)c * kbytes + 16u * h;      // + 32 t kbytes, K: + 32 kb
+  const uint32_t vs = (uint32_t)c * kscales + 2u * h;      // + 32 t kscales, K: + 4 kb
   const uint32_t vx = (uint32_t)c * xrow_bytes + 64u * h;  // + 32 u row + 128 kb + 16 i
   bool live[NT];
 #pragma unroll
@@ -221,10 +224,10 @@ __global__ __launch_bounds__(256, 1) void decode_main(DecodeArgs a) {
   auto load_w = [&](int64_t kb, uint4* wl, uint32_t (&sw)[NT]) {
 #pragma unroll
     for (int t = 0; t < NT; ++t)
-      sw[t] = bload16(rs, vs, 32u * t * kscales + 4u * (uint32_t)kb);
+      sw[t] = bload16(rs, vs + 32u * t * kscales, 4u * (uint32_t)kb);
 #pragma unroll
     for (int t = 0; t < NT; ++t)
-      dma16(rw, wl + wslot + t * 64, vw, 32u * t * kbytes + 32u * (uint32_t)kb);
+      dma16(rw, wl + wslot + t * 64, vw + 32u * t * kbytes, 32u * (uint32_t)kb);
   };
   auto load_x = [&](int64_t kb, XStage<MT, RT>& st) {
 #pragma unroll
@@ -236,7 +239,7 @@ __global__ __launch_bounds__(256, 1) void decode_main(DecodeArgs a) {
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        st.a[rt][i] = bload128(ra, vx, 32u * rt * xrow_bytes + 128u * (uint32_t)kb + 16u * i);
+        st.a[rt][i] = bload128(ra, vx + 32u * rt * xrow_bytes, 128u * (uint32_t)kb + 16u * i);
   };
   auto compute = [&](const uint4* wl, const uint32_t (&sw)[NT], const XStage<MT, RT>& xs) {
     uint4 w[NT];
@@ -305,16 +308,15 @@ __global__ __launch_bounds__(256, 1) void decode_main(DecodeArgs a) {
       for (int u = 0; u < MT; ++u) xs[u] = bload128(rx, vx16, 32u * u * xrow_bytes + 2u * k0);
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        const uint32_t cw = bload32(rw, (uint32_t)c * kbytes + 4u * h,
-                                    32u * t * kbytes + k0 / 2);
-        const uint32_t sb = bload8(rs, (uint32_t)c * kscales, 32u * t * kscales + k0 / 16);
+        const uint32_t cw = bload32(rw, (uint32_t)(32 * t + c) * kbytes + 4u * h, k0 / 2);
+        const uint32_t sb = bload8(rs, (uint32_t)(32 * t + c) * kscales, k0 / 16);
         const uint4 b = dequant8_bf16(cw, e4m3_to_f32(sb));
 #pragma unroll
         for (int u = 0; u < MT; ++u) acc[t][u] = mfma_bf16(xs[u], b, acc[t][u]);
       }
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
-        const uint4 av = bload128(ra, vx16, 32u * rt * xrow_bytes + 2u * k0);
+        const uint4 av = bload128(ra, vx16 + 32u * rt * xrow_bytes, 2u * k0);
 #pragma unroll
         for (int u = 0; u < MT; ++u) acc[NT + rt][u] = mfma_bf16(xs[u], av, acc[NT + rt][u]);
       }

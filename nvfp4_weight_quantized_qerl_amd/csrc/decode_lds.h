@@ -16,14 +16,20 @@
 // eight different bank groups in every group of eight lanes.
 //
 // Pipeline.  Codes and scales are triple-buffered, x_t double-buffered.
-// Iteration i: wait for this wave's copies of block i (s_waitcnt with the
-// weight copies of block i+1 still in flight), s_barrier (now every wave's
-// copies of block i have landed and every wave has finished block i-1),
-// issue the copies of x_t(i+1) and weights(i+2) into the stages block i-1
-// used, then compute block i: each wave takes one 64-wide quarter of it.
+// Iteration i: the four copying waves wait for their copies of block i
+// (s_waitcnt with the weight copies of block i+1 still in flight),
+// s_barrier (now every copy of block i has landed and every wave has
+// finished block i-1), the copying waves issue the copies of x_t(i+1) and
+// weights(i+2) into the stages block i-1 used, then block i is computed.
 // The raw s_barrier is used instead of __syncthreads, whose memory fence
 // would wait for every copy in flight.
+//
+// Waves.  Eight waves, two per SIMD so that one wave's LDS and VALU
+// latencies are covered by the other's MFMAs: wave w takes K quarter w % 4
+// of every block and row half w / 4 of the workgroup's weight subtiles.
 #pragma once
+
+#include <type_traits>
 
 #include "qerl_device.h"
 
@@ -112,19 +118,20 @@ __device__ __forceinline__ void epilogue_tile(const Args& a, f32x16_t acc, float
 }
 
 template <int MT, int NT>
-__global__ __launch_bounds__(256, 1) void decode_lds(Args a) {
-  constexpr int NP = MT * NT;                 // 32x32 tiles per wave
+__global__ __launch_bounds__(512, 1) void decode_lds(Args a) {
   constexpr int XROWS = 32 * MT;              // token rows
   constexpr int WROWS = 32 * NT;              // weight rows staged per block
+  constexpr int NT0 = (NT + 1) / 2;           // weight subtiles of row half 0
+  constexpr int NT1 = NT - NT0;               // ... and of row half 1
   constexpr int CODE_INSTR = WROWS / 8;       // 8 rows per code copy
   constexpr int XINSTR = XROWS / 2;           // 2 rows per x_t copy
   constexpr int W_PER_WAVE = CODE_INSTR / 4 + 1;   // code copies + one scale copy
-  constexpr int X_PER_WAVE = XINSTR / 4;
   static_assert(CODE_INSTR % 4 == 0 && XINSTR % 4 == 0, "copies split evenly over 4 waves");
   // Reduction slices of 16 x 64 floats live in the two x_t stages after the
-  // main loop: 8 * MT slices, 3 per reduced tile.
-  constexpr int TPR = (MT * 8) / 3 >= 4 ? 4 : (MT * 8) / 3;   // tiles per round
-  constexpr int ROUNDS = (NP + TPR - 1) / TPR;
+  // main loop: 8 * MT slices, half per row half, 3 per reduced tile.
+  constexpr int SPH = 4 * MT;                 // slices per row half
+  constexpr int TPR = SPH / 3;                // tiles reduced per round and half
+  constexpr int ROUNDS = (NT0 * MT + TPR - 1) / TPR;
 
   __shared__ __attribute__((aligned(16))) uint4 wc0[WROWS * 8], wc1[WROWS * 8], wc2[WROWS * 8];
   __shared__ __attribute__((aligned(16))) uint4 sc0[256], sc1[256], sc2[256];
@@ -133,7 +140,11 @@ __global__ __launch_bounds__(256, 1) void decode_lds(Args a) {
   __shared__ int is_last;
 
   const int lane = threadIdx.x & 63;
+  // Wave-uniform values the compiler cannot prove uniform by itself.
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int q = wave & 3;                     // K quarter of every block
+  const int hf = wave >> 2;                   // row half: subtiles [0, NT0) or [NT0, NT)
+  const int tbase = hf ? NT0 : 0;
   const int h = lane >> 5, c = lane & 31;
   const int64_t row0 = (int64_t)blockIdx.x * a.rows;
   const int64_t row_end = min(a.n, row0 + (int64_t)a.rows);
@@ -144,7 +155,7 @@ __global__ __launch_bounds__(256, 1) void decode_lds(Args a) {
 
   if (a.r > 0) {
     const int words = XROWS * a.rpad16 / 8;
-    for (int i = threadIdx.x; i < words; i += 256)
+    for (int i = threadIdx.x; i < words; i += 512)
       reinterpret_cast<uint4*>(t_lds)[i] = reinterpret_cast<const uint4*>(a.t)[i];
   }
 
@@ -154,79 +165,93 @@ __global__ __launch_bounds__(256, 1) void decode_lds(Args a) {
   const __amdgpu_buffer_rsrc_t rs = rsrc(a.scales + row0 * kscales, (uint32_t)((a.n - row0) * kscales));
   const __amdgpu_buffer_rsrc_t rx = rsrc(a.xt, (uint32_t)XROWS * xrow);
 
-  // Per-lane parts of the copy addresses (see the file comment).
-  // codes copy j of this wave covers rows 8 (wave + 4 j) .. +7
+  // Copies are issued by waves 0..3 (see the file comment for the layout).
+  // codes copy j of wave q covers rows 8 (q + 4 j) .. +7
   const uint32_t cr = (uint32_t)(lane >> 3);
-  const uint32_t vcode = (8u * wave + cr) * kbytes + 16u * ((uint32_t)(lane & 7) ^ cr);
-  // scales copy of this wave covers rows 64 wave .. +63
-  const uint32_t vscale = (64u * wave + lane) * kscales;
-  // x_t copy j of this wave covers rows 2 (wave + 4 j) and 2 (wave + 4 j) + 1
-  const uint32_t xr = 2u * wave + (uint32_t)(lane >> 5);
+  const uint32_t vcode = (8u * q + cr) * kbytes + 16u * ((uint32_t)(lane & 7) ^ cr);
+  // scales copy of wave q covers rows 64 q .. +63
+  const uint32_t vscale = (64u * q + lane) * kscales;
+  // x_t copy j of wave q covers rows 2 (q + 4 j) and 2 (q + 4 j) + 1
+  const uint32_t xr = 2u * q + (uint32_t)(lane >> 5);
   const uint32_t vx = xr * xrow + 16u * ((uint32_t)(lane & 31) ^ (xr & 7u));
 
   auto copy_w = [&](int64_t blk, uint4* wc, uint4* sc) {
 #pragma unroll
     for (int j = 0; j < CODE_INSTR / 4; ++j)
-      dma16(rw, wc + (wave + 4 * j) * 64, vcode, 32u * j * kbytes + 128u * (uint32_t)blk);
-    dma16(rs, sc + wave * 64, vscale, 16u * (uint32_t)blk);
+      // The row offset stays in the per-lane offset, which the buffer range
+      // check covers: rows past the end of the tensor read as zeros.
+      dma16(rw, wc + (q + 4 * j) * 64, vcode + 32u * j * kbytes, 128u * (uint32_t)blk);
+    dma16(rs, sc + q * 64, vscale, 16u * (uint32_t)blk);
   };
   auto copy_x = [&](int64_t blk, uint4* xs) {
 #pragma unroll
     for (int j = 0; j < XINSTR / 4; ++j)
-      dma16(rx, xs + (wave + 4 * j) * 64, vx, 8u * j * xrow + 512u * (uint32_t)blk);
+      dma16(rx, xs + (q + 4 * j) * 64, vx, 8u * j * xrow + 512u * (uint32_t)blk);
   };
 
-  bool live[NT];
+  f32x16_t acc[NT0][MT];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) live[t] = row0 + 32 * t + c < row_end;
-
-  f32x16_t acc[NT][MT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t)
+  for (int t = 0; t < NT0; ++t)
 #pragma unroll
     for (int u = 0; u < MT; ++u) acc[t][u] = zero16();
 
-  // This wave computes K quarter `wave` (64 wide) of every block.
-  auto compute = [&](const uint4* wc, const uint4* sc, const uint4* xs) {
-    uint4 w[NT];
-    float sb0[NT], sb1[NT];
+  // This wave computes K quarter q of the block for NTH weight subtiles
+  // starting at TB.
+  auto compute = [&](auto nth, int TB, const uint4* wc, const uint4* sc,
+                     const uint4* xs) __attribute__((always_inline)) {
+    constexpr int NTH = decltype(nth)::value;
+    uint4 w[NTH > 0 ? NTH : 1];
+    float sb0[NTH > 0 ? NTH : 1], sb1[NTH > 0 ? NTH : 1];
+    uint4 xa[4][MT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const int r = 32 * t + c;
-      w[t] = wc[r * 8 + ((2 * wave + h) ^ (r & 7))];
-      const uint32_t sw = reinterpret_cast<const uint16_t*>(sc)[r * 8 + 2 * wave + h];
+    for (int t = 0; t < NTH; ++t) {
+      const int r = 32 * (TB + t) + c;
+      w[t] = wc[r * 8 + ((2 * q + h) ^ (r & 7))];
+      const uint32_t sw = reinterpret_cast<const uint16_t*>(sc)[r * 8 + 2 * q + h];
       sb0[t] = e4m3_to_f32(sw & 0xffu);
       sb1[t] = e4m3_to_f32((sw >> 8) & 0xffu);
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      uint4 xa[MT];
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int u = 0; u < MT; ++u) {
         const int r = 32 * u + c;
-        xa[u] = xs[r * 32 + ((8 * wave + 4 * h + j) ^ (r & 7))];
+        xa[j][u] = xs[r * 32 + ((8 * q + 4 * h + j) ^ (r & 7))];
       }
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int t = 0; t < NTH; ++t) {
         const uint4 b = dequant8_bf16(comp(w[t], j), j < 2 ? sb0[t] : sb1[t]);
 #pragma unroll
-        for (int u = 0; u < MT; ++u) acc[t][u] = mfma_bf16(xa[u], b, acc[t][u]);
+        for (int u = 0; u < MT; ++u) acc[t][u] = mfma_bf16(xa[j][u], b, acc[t][u]);
       }
     }
+  };
+  auto compute_half = [&](const uint4* wc, const uint4* sc,
+                          const uint4* xs) __attribute__((always_inline)) {
+    if (hf == 0)
+      compute(std::integral_constant<int, NT0>{}, 0, wc, sc, xs);
+    else
+      compute(std::integral_constant<int, NT1>{}, NT0, wc, sc, xs);
   };
 
   if (bb < be) {
     const int64_t last = be - 1;
-    copy_w(bb, wc0, sc0);
-    copy_x(bb, xs0);
-    copy_w(min(bb + 1, last), wc1, sc1);
+    if (hf == 0) {
+      copy_w(bb, wc0, sc0);
+      copy_x(bb, xs0);
+      copy_w(min(bb + 1, last), wc1, sc1);
+    }
     // Block bb + i uses weight stage i % 3 and x_t stage i % 2; period 6.
 #define QERL_LDS_STEP(OFF, WC, SC, XS, XN, WN, SN)                         \
-  wait_vmcnt<W_PER_WAVE>();                                                 \
+  if (hf == 0) wait_vmcnt<W_PER_WAVE>();                                    \
   barrier_nofence();                                                        \
-  copy_x(min(blk + (OFF) + 1, last), XN);                                   \
-  copy_w(min(blk + (OFF) + 2, last), WN, SN);                               \
-  compute(WC, SC, XS);                                                      \
+  if (hf == 0) {                                                            \
+    copy_x(min(blk + (OFF) + 1, last), XN);                                 \
+    copy_w(min(blk + (OFF) + 2, last), WN, SN);                             \
+  }                                                                         \
+  compute_half(WC, SC, XS);                                                 \
   if (blk + (OFF) + 1 >= be) break;
     for (int64_t blk = bb;; blk += 6) {
       QERL_LDS_STEP(0, wc0, sc0, xs0, xs1, wc2, sc2)
@@ -242,32 +267,34 @@ __global__ __launch_bounds__(256, 1) void decode_lds(Args a) {
   wait_vmcnt<0>();
   barrier_nofence();
 
-  // Sum the four waves' tiles through the (now free) x_t stages; in each
-  // round TPR tiles are reduced, tile p (of the round) by wave p.
+  // Sum the four K quarters of each row half through the (now free) x_t
+  // stages.  Half hf uses slices [hf * SPH, (hf + 1) * SPH); per round TPR
+  // tiles of the half are reduced, tile p by wave q == p % TPR.
   auto slice = [&](int s) -> float* {
     return s < 4 * MT ? reinterpret_cast<float*>(xs0) + s * 1024
                       : reinterpret_cast<float*>(xs1) + (s - 4 * MT) * 1024;
   };
+  const int ntile = (hf ? NT1 : NT0) * MT;
 #pragma unroll
   for (int rnd = 0; rnd < ROUNDS; ++rnd) {
 #pragma unroll
-    for (int p = TPR * rnd; p < NP && p < TPR * rnd + TPR; ++p) {
+    for (int p = TPR * rnd; p < NT0 * MT && p < TPR * rnd + TPR; ++p) {
       const int owner = p - TPR * rnd;
-      if (wave != owner) {
-        const int rank = wave - (wave > owner ? 1 : 0);
-        float* dst = slice(owner * 3 + rank) + lane;
+      if (p < ntile && q != owner) {
+        const int rank = q - (q > owner ? 1 : 0);
+        float* dst = slice(hf * SPH + owner * 3 + rank) + lane;
 #pragma unroll
         for (int v = 0; v < 16; ++v) dst[v * 64] = acc[p / MT][p % MT][v];
       }
     }
     __syncthreads();
 #pragma unroll
-    for (int p = TPR * rnd; p < NP && p < TPR * rnd + TPR; ++p) {
+    for (int p = TPR * rnd; p < NT0 * MT && p < TPR * rnd + TPR; ++p) {
       const int owner = p - TPR * rnd;
-      if (wave == owner) {
+      if (p < ntile && q == owner) {
 #pragma unroll
         for (int rank = 0; rank < 3; ++rank) {
-          const float* src = slice(owner * 3 + rank) + lane;
+          const float* src = slice(hf * SPH + owner * 3 + rank) + lane;
 #pragma unroll
           for (int v = 0; v < 16; ++v) acc[p / MT][p % MT][v] += src[v * 64];
         }
@@ -275,23 +302,23 @@ __global__ __launch_bounds__(256, 1) void decode_lds(Args a) {
     }
     __syncthreads();
   }
-  auto owns = [&](int p) { return wave == p % TPR; };
+  auto owns = [&](int p) { return p < ntile && q == p % TPR; };
+  auto tile_row = [&](int p) { return row0 + 32 * (tbase + p / MT) + c; };
+  auto tile_live = [&](int p) { return tile_row(p) < row_end; };
 
   const float S = *a.gscale;
   if (a.split == 1) {
 #pragma unroll
-    for (int p = 0; p < NP; ++p)
+    for (int p = 0; p < NT0 * MT; ++p)
       if (owns(p))
-        epilogue_tile(a, acc[p / MT][p % MT], S, p % MT, row0 + 32 * (p / MT) + c,
-                      live[p / MT], lane, t_lds);
+        epilogue_tile(a, acc[p / MT][p % MT], S, p % MT, tile_row(p), tile_live(p), lane, t_lds);
     return;
   }
 
 #pragma unroll
-  for (int p = 0; p < NP; ++p) {
-    if (owns(p) && live[p / MT]) {
-      const int64_t row = row0 + 32 * (p / MT) + c;
-      float* dst = a.ypart + ((int64_t)split_id * XROWS + 32 * (p % MT)) * a.n + row;
+  for (int p = 0; p < NT0 * MT; ++p) {
+    if (owns(p) && tile_live(p)) {
+      float* dst = a.ypart + ((int64_t)split_id * XROWS + 32 * (p % MT)) * a.n + tile_row(p);
 #pragma unroll
       for (int v = 0; v < 16; ++v) dst[(int64_t)acc_row(v, lane) * a.n] = acc[p / MT][p % MT][v];
     }
@@ -307,18 +334,17 @@ __global__ __launch_bounds__(256, 1) void decode_lds(Args a) {
   if (!is_last) return;
   __threadfence();
 #pragma unroll
-  for (int p = 0; p < NP; ++p) {
+  for (int p = 0; p < NT0 * MT; ++p) {
     if (owns(p)) {
-      const int64_t row = row0 + 32 * (p / MT) + c;
       f32x16_t sum = zero16();
-      if (live[p / MT]) {
+      if (tile_live(p)) {
         for (int s = 0; s < a.split; ++s) {
-          const float* src = a.ypart + ((int64_t)s * XROWS + 32 * (p % MT)) * a.n + row;
+          const float* src = a.ypart + ((int64_t)s * XROWS + 32 * (p % MT)) * a.n + tile_row(p);
 #pragma unroll
           for (int v = 0; v < 16; ++v) sum[v] += src[(int64_t)acc_row(v, lane) * a.n];
         }
       }
-      epilogue_tile(a, sum, S, p % MT, row, live[p / MT], lane, t_lds);
+      epilogue_tile(a, sum, S, p % MT, tile_row(p), tile_live(p), lane, t_lds);
     }
   }
   if (threadIdx.x == 0) a.cnt[blockIdx.x] = 0u;
