@@ -196,17 +196,16 @@ QERL_API qerl_status qerl_linear_prefill(const void* x, int64_t m, const void* c
  * that time or schedule them separately.
  *
  * qerl_linear_prepare writes into the workspace the noisy activations
- * x_t = bf16(x (.) (1 + z)) [QeRL summary, §3.4, Eq. 12] and, for sizes
- * whose contraction does not compute the LoRA down-projection itself, the
- * scaled down-projection bf16(s x_t A^T) [§3.4, Eq. 2].  Arguments as
- * above; n is needed to size the workspace.
+ * x_t = bf16(x (.) (1 + z)) [QeRL summary, §3.4, Eq. 12] and, with a LoRA
+ * branch (r > 0 and lora_a non-NULL), the scaled down-projection
+ * t = bf16(s x_t A^T) [§3.4, Eq. 2].  Arguments as above; n is needed to
+ * size the workspace.
  *
  * qerl_linear_decode_prepared / qerl_linear_prefill_prepared run the main
- * contraction y = bf16(S acc + (s x_t A^T) B^T) from a workspace that
- * qerl_linear_prepare filled with the same (m, n, k, r).  x and z are not
- * read again; lora_a is read when the contraction computes the LoRA
- * down-projection itself, and must be the same tensor (and lora_scale the
- * same value) as given to qerl_linear_prepare.
+ * contraction y = bf16(S acc + t B^T) from a workspace that
+ * qerl_linear_prepare filled with the same (m, n, k, r); x, z and lora_a
+ * are not read again.  r == 0 or lora_b == NULL means no LoRA branch (r
+ * must then also have been 0 for the prepare call).
  */
 QERL_API qerl_status qerl_linear_prepare(const void* x, int64_t m, int64_t n,
                                          int64_t k, const void* lora_a, int32_t r,
@@ -216,15 +215,13 @@ QERL_API qerl_status qerl_linear_prepare(const void* x, int64_t m, int64_t n,
 
 QERL_API qerl_status qerl_linear_decode_prepared(
     int64_t m, const void* codes, const void* scales, const float* gscale,
-    int64_t n, int64_t k, const void* lora_a, const void* lora_b, int32_t r,
-    float lora_scale, void* y, void* workspace, size_t workspace_bytes,
-    void* stream);
+    int64_t n, int64_t k, const void* lora_b, int32_t r, void* y,
+    void* workspace, size_t workspace_bytes, void* stream);
 
 QERL_API qerl_status qerl_linear_prefill_prepared(
     int64_t m, const void* codes, const void* scales, const float* gscale,
-    int64_t n, int64_t k, const void* lora_a, const void* lora_b, int32_t r,
-    float lora_scale, void* y, void* workspace, size_t workspace_bytes,
-    void* stream);
+    int64_t n, int64_t k, const void* lora_b, int32_t r, void* y,
+    void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

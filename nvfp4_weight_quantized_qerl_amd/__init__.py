@@ -135,27 +135,24 @@ def qerl_linear_prepare(x, n, lora_a, lora_scale, z, workspace):
            "qerl_linear_prepare")
 
 
-def _prepared(fn_name, m, codes, scales, gscale, k, lora_a, lora_b, lora_scale, y, workspace):
+def _prepared(fn_name, m, codes, scales, gscale, k, lora_b, y, workspace):
     n = codes.shape[0]
-    r = 0 if lora_a is None else int(lora_a.shape[0])
-    la = None if lora_a is None else _bits16(lora_a, "lora_a")
+    r = 0 if lora_b is None else int(lora_b.shape[1])
     lb = None if lora_b is None else _bits16(lora_b, "lora_b")
     fn = getattr(lib, fn_name)
-    _check(fn(m, _ptr(codes), _ptr(scales), _ptr(gscale), n, k, _ptr(la), _ptr(lb), r,
-              float(lora_scale), _ptr(y), _ptr(workspace), workspace.numel(),
-              _stream(y.device)), fn_name)
+    _check(fn(m, _ptr(codes), _ptr(scales), _ptr(gscale), n, k, _ptr(lb), r, _ptr(y),
+              _ptr(workspace), workspace.numel(), _stream(y.device)), fn_name)
     return y
 
 
-def qerl_linear_decode_prepared(m, codes, scales, gscale, k, lora_a, lora_b, lora_scale, y,
-                                workspace):
-    """Contraction half of qerl_linear_decode from a prepared workspace."""
-    return _prepared("qerl_linear_decode_prepared", m, codes, scales, gscale, k, lora_a,
-                     lora_b, lora_scale, y, workspace)
+def qerl_linear_decode_prepared(m, codes, scales, gscale, k, lora_b, y, workspace):
+    """Contraction half of qerl_linear_decode from a workspace that
+    qerl_linear_prepare filled for the same (m, n, k, r)."""
+    return _prepared("qerl_linear_decode_prepared", m, codes, scales, gscale, k, lora_b, y,
+                     workspace)
 
 
-def qerl_linear_prefill_prepared(m, codes, scales, gscale, k, lora_a, lora_b, lora_scale, y,
-                                 workspace):
+def qerl_linear_prefill_prepared(m, codes, scales, gscale, k, lora_b, y, workspace):
     """Contraction half of qerl_linear_prefill from a prepared workspace."""
-    return _prepared("qerl_linear_prefill_prepared", m, codes, scales, gscale, k, lora_a,
-                     lora_b, lora_scale, y, workspace)
+    return _prepared("qerl_linear_prefill_prepared", m, codes, scales, gscale, k, lora_b, y,
+                     workspace)

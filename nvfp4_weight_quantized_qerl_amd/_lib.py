@@ -26,11 +26,9 @@ SIGNATURES = {
     "qerl_linear_prepare": (ctypes.c_int, [c_vp, c_i64, c_i64, c_i64, c_vp, c_i32, c_f32,
                                            c_vp, c_vp, c_sz, c_vp]),
     "qerl_linear_decode_prepared": (ctypes.c_int, [c_i64, c_vp, c_vp, c_vp, c_i64, c_i64,
-                                                   c_vp, c_vp, c_i32, c_f32, c_vp, c_vp,
-                                                   c_sz, c_vp]),
+                                                   c_vp, c_i32, c_vp, c_vp, c_sz, c_vp]),
     "qerl_linear_prefill_prepared": (ctypes.c_int, [c_i64, c_vp, c_vp, c_vp, c_i64, c_i64,
-                                                    c_vp, c_vp, c_i32, c_f32, c_vp, c_vp,
-                                                    c_sz, c_vp]),
+                                                    c_vp, c_i32, c_vp, c_vp, c_sz, c_vp]),
 }
 
 

@@ -55,7 +55,7 @@ const char* qerl_status_string(int status) {
   }
 }
 
-int qerl_abi_version(void) { return 1; }
+int qerl_abi_version(void) { return 2; }
 
 qerl_status qerl_quantize_nvfp4(const void* w_bf16, int64_t n, int64_t k, void* codes,
                                 void* scales, float* gscale, int32_t* nonfinite_flag,
@@ -130,11 +130,8 @@ static qerl_status linear_full(bool prefill, const void* x, int64_t m, const voi
   const uint8_t* sc = static_cast<const uint8_t*>(scales);
   const uint16_t* b = r_eff ? static_cast<const uint16_t*>(lora_b) : nullptr;
   uint16_t* yy = static_cast<uint16_t*>(y);
-  const uint16_t* a = r_eff ? static_cast<const uint16_t*>(lora_a) : nullptr;
-  e = prefill ? qerl::launch_linear_prefill_main(plan, c, sc, gscale, a, lora_scale, b, yy,
-                                                 ws, st)
-              : qerl::launch_linear_decode_main(plan, c, sc, gscale, a, lora_scale, b, yy,
-                                                ws, st);
+  e = prefill ? qerl::launch_linear_prefill_main(plan, c, sc, gscale, b, yy, ws, st)
+              : qerl::launch_linear_decode_main(plan, c, sc, gscale, b, yy, ws, st);
   return from_hip(e);
 }
 
@@ -177,44 +174,39 @@ qerl_status qerl_linear_prepare(const void* x, int64_t m, int64_t n, int64_t k,
 
 static qerl_status linear_prepared(bool prefill, int64_t m, const void* codes,
                                    const void* scales, const float* gscale, int64_t n,
-                                   int64_t k, const void* lora_a, const void* lora_b,
-                                   int32_t r, float lora_scale, void* y, void* workspace,
-                                   size_t workspace_bytes, void* stream) {
-  if (r > 0 && (!lora_a || !lora_b)) return QERL_ERR_NULL;
-  if (lora_a && !aligned(lora_a, 16)) return QERL_ERR_ALIGN;
+                                   int64_t k, const void* lora_b, int32_t r, void* y,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  if (r > 0 && !lora_b) return QERL_ERR_NULL;
   qerl::LinearPlan plan;
-  qerl_status s = check_linear(nullptr, m, codes, scales, gscale, n, k, r, lora_scale,
-                               nullptr, y, workspace, workspace_bytes, &plan);
+  qerl_status s = check_linear(nullptr, m, codes, scales, gscale, n, k, r, 1.0f, nullptr, y,
+                               workspace, workspace_bytes, &plan);
   if (s != QERL_OK) return s;
   const uint8_t* c = static_cast<const uint8_t*>(codes);
   const uint8_t* sc = static_cast<const uint8_t*>(scales);
-  const uint16_t* a = r > 0 ? static_cast<const uint16_t*>(lora_a) : nullptr;
   const uint16_t* b = r > 0 ? static_cast<const uint16_t*>(lora_b) : nullptr;
   uint16_t* yy = static_cast<uint16_t*>(y);
   char* ws = static_cast<char*>(workspace);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  return from_hip(prefill ? qerl::launch_linear_prefill_main(plan, c, sc, gscale, a, lora_scale,
-                                                             b, yy, ws, st)
-                          : qerl::launch_linear_decode_main(plan, c, sc, gscale, a, lora_scale,
-                                                            b, yy, ws, st));
+  return from_hip(prefill ? qerl::launch_linear_prefill_main(plan, c, sc, gscale, b, yy, ws, st)
+                          : qerl::launch_linear_decode_main(plan, c, sc, gscale, b, yy, ws, st));
 }
 
 qerl_status qerl_linear_decode_prepared(int64_t m, const void* codes, const void* scales,
                                         const float* gscale, int64_t n, int64_t k,
-                                        const void* lora_a, const void* lora_b, int32_t r,
-                                        float lora_scale, void* y, void* workspace,
-                                        size_t workspace_bytes, void* stream) {
-  return linear_prepared(false, m, codes, scales, gscale, n, k, lora_a, lora_b, r,
-                         lora_scale, y, workspace, workspace_bytes, stream);
+                                        const void* lora_b, int32_t r, void* y,
+                                        void* workspace, size_t workspace_bytes,
+                                        void* stream) {
+  return linear_prepared(false, m, codes, scales, gscale, n, k, lora_b, r, y, workspace,
+                         workspace_bytes, stream);
 }
 
 qerl_status qerl_linear_prefill_prepared(int64_t m, const void* codes, const void* scales,
                                          const float* gscale, int64_t n, int64_t k,
-                                         const void* lora_a, const void* lora_b, int32_t r,
-                                         float lora_scale, void* y, void* workspace,
-                                         size_t workspace_bytes, void* stream) {
-  return linear_prepared(true, m, codes, scales, gscale, n, k, lora_a, lora_b, r,
-                         lora_scale, y, workspace, workspace_bytes, stream);
+                                         const void* lora_b, int32_t r, void* y,
+                                         void* workspace, size_t workspace_bytes,
+                                         void* stream) {
+  return linear_prepared(true, m, codes, scales, gscale, n, k, lora_b, r, y, workspace,
+                         workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -1,5 +1,8 @@
-// Decode contraction: launch of decode_main (decode_kernel.h) over the m
-// rows in chunks of at most 32 * dec_mt rows.
+// Decode contraction: launches over the m rows in chunks of at most
+// 32 * dec_mt rows.  Per chunk, one contraction kernel -- the LDS-staged
+// one (decode_lds.h) where its shape conditions hold, else the general one
+// (decode_kernel.h) -- and, when K is split across workgroups, the
+// finishing kernel below.
 #include <algorithm>
 
 #include "decode_kernel.h"
@@ -8,22 +11,117 @@
 
 namespace qerl {
 
-static decode::DecodeKernel pick_decode(int mt, int nt, int rt) {
+namespace {
+
+decode::DecodeKernel pick_decode(int mt, int nt) {
   switch (mt) {
-    case 1: return decode::pick_mt1(nt, rt);
-    case 2: return decode::pick_mt2(nt, rt);
-    case 4: return decode::pick_mt4(nt, rt);
+    case 1: return decode::pick_mt1(nt);
+    case 2: return decode::pick_mt2(nt);
+    case 4: return decode::pick_mt4(nt);
     default: return nullptr;
   }
 }
 
+struct FinishArgs {
+  const float* __restrict__ ypart;      // [split, rows, n] fp32 partial sums of acc
+  const float* __restrict__ gscale;
+  const uint16_t* __restrict__ t;       // [rows, rpad16] bf16 s x_t A^T of this chunk
+  const uint16_t* __restrict__ lora_b;  // [n, r] bf16
+  uint16_t* __restrict__ y;             // [m_valid, n] rows of this chunk
+  int64_t n;
+  int split, rows, m_valid, r, rpad16, lora_vec;
+};
+
+constexpr int kFinishRows = 4;  // token rows per thread
+
+// y[m, j] = bf16(S * sum_s ypart[s, m, j] + sum_i t[m, i] B[j, i]): the
+// epilogue of a split-K contraction [QeRL summary, §3.4, Eq. 6 (S) and
+// Eq. 2 (LoRA side branch)].  The splits are summed in split order.  One
+// thread per output column j and kFinishRows token rows; t of those rows
+// sits in LDS (as fp32, exact).
+__global__ __launch_bounds__(256) void splitk_finish(FinishArgs a) {
+  __shared__ float t_lds[kFinishRows * 128];
+  const int m0 = blockIdx.y * kFinishRows;
+  for (int i = threadIdx.x; i < kFinishRows * 128; i += 256) {
+    const int mm = i / 128, jj = i % 128;
+    t_lds[i] = (m0 + mm < a.m_valid && jj < a.r)
+                   ? bf16_to_f32(a.t[(int64_t)(m0 + mm) * a.rpad16 + jj])
+                   : 0.0f;
+  }
+  __syncthreads();
+  const int64_t col = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (col >= a.n) return;
+  const float S = *a.gscale;
+  float acc[kFinishRows];
+#pragma unroll
+  for (int mm = 0; mm < kFinishRows; ++mm) acc[mm] = 0.0f;
+  const float* src = a.ypart + (int64_t)m0 * a.n + col;
+  const int64_t sstride = (int64_t)a.rows * a.n;
+  const int mrows = min(kFinishRows, a.m_valid - m0);
+#pragma unroll 4
+  for (int s = 0; s < a.split; ++s) {
+#pragma unroll
+    for (int mm = 0; mm < kFinishRows; ++mm)
+      if (mm < mrows) acc[mm] += src[s * sstride + (int64_t)mm * a.n];
+  }
+#pragma unroll
+  for (int mm = 0; mm < kFinishRows; ++mm) acc[mm] *= S;
+  const uint16_t* brow = a.lora_b + col * a.r;
+  for (int i0 = 0; i0 < a.r; i0 += 8) {
+    uint32_t bw[4];
+    if (a.lora_vec) {
+      const uint4 v = *reinterpret_cast<const uint4*>(brow + i0);
+      bw[0] = v.x; bw[1] = v.y; bw[2] = v.z; bw[3] = v.w;
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t lo = i0 + 2 * q < a.r ? brow[i0 + 2 * q] : 0u;
+        const uint32_t hi = i0 + 2 * q + 1 < a.r ? brow[i0 + 2 * q + 1] : 0u;
+        bw[q] = lo | (hi << 16);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float b0 = bf16_to_f32(bw[q] & 0xffffu), b1 = bf16_to_f32(bw[q] >> 16);
+#pragma unroll
+      for (int mm = 0; mm < kFinishRows; ++mm)
+        acc[mm] += t_lds[mm * 128 + i0 + 2 * q] * b0 + t_lds[mm * 128 + i0 + 2 * q + 1] * b1;
+    }
+  }
+#pragma unroll
+  for (int mm = 0; mm < kFinishRows; ++mm)
+    if (mm < mrows) a.y[(int64_t)(m0 + mm) * a.n + col] = f32_to_bf16_bits(acc[mm]);
+}
+
+hipError_t launch_finish(const LinearPlan& p, int split, int rows, int m_valid,
+                         const float* ypart, const float* gscale, const uint16_t* t,
+                         const uint16_t* lora_b, int r, int lora_vec, uint16_t* y,
+                         hipStream_t stream) {
+  FinishArgs f;
+  f.ypart = ypart;
+  f.gscale = gscale;
+  f.t = t;
+  f.lora_b = lora_b;
+  f.y = y;
+  f.n = p.n;
+  f.split = split;
+  f.rows = rows;
+  f.m_valid = m_valid;
+  f.r = r;
+  f.rpad16 = p.rpad16;
+  f.lora_vec = lora_vec;
+  const dim3 grid((unsigned)((p.n + 255) / 256),
+                  (unsigned)((m_valid + kFinishRows - 1) / kFinishRows));
+  hipLaunchKernelGGL(splitk_finish, grid, dim3(256), 0, stream, f);
+  return hipGetLastError();
+}
+
 // LDS-staged contraction (decode_lds.h) for one chunk of <= 64 rows, when
-// k is a multiple of 256 and the LoRA-down is precomputed.
-static hipError_t run_decode_lds(const LinearPlan& p, int mt, const uint8_t* codes,
-                                 const uint8_t* scales, const float* gscale,
-                                 const uint16_t* t, const uint16_t* lora_b, int r,
-                                 int lora_vec, const uint16_t* xt, uint16_t* y, int m_valid,
-                                 char* ws, hipStream_t stream) {
+// k is a multiple of 256.
+hipError_t run_decode_lds(const LinearPlan& p, int mt, const uint8_t* codes,
+                          const uint8_t* scales, const float* gscale, const uint16_t* t,
+                          const uint16_t* lora_b, int r, int lora_vec, const uint16_t* xt,
+                          uint16_t* y, int m_valid, char* ws, hipStream_t stream) {
   dlds::Kernel kern = mt == 1 ? dlds::pick_mt1(p.dec_nt) : dlds::pick_mt2(p.dec_nt);
   if (!kern) return hipErrorInvalidConfiguration;
   dlds::Args a;
@@ -35,37 +133,37 @@ static hipError_t run_decode_lds(const LinearPlan& p, int mt, const uint8_t* cod
   a.lora_b = lora_b;
   a.y = y;
   a.ypart = reinterpret_cast<float*>(ws + p.off_ypart);
-  a.cnt = reinterpret_cast<uint32_t*>(ws + p.off_cnt);
   a.n = p.n;
   a.k = p.k;
   const int64_t nblocks = p.k / 256;
-  int64_t per = (nblocks + p.dec_split - 1) / p.dec_split;
-  const int64_t split = (nblocks + per - 1) / per;
+  const int64_t per = (nblocks + p.dec_split - 1) / p.dec_split;
+  const int split = (int)((nblocks + per - 1) / per);
   a.blocks_per_split = per;
   a.m_valid = m_valid;
   a.rows = p.dec_rows;
-  a.split = (int)split;
+  a.split = split;
   a.r = r;
   a.rpad16 = p.rpad16;
   a.lora_vec = lora_vec;
   hipLaunchKernelGGL(kern, dim3((unsigned)p.dec_groups, (unsigned)split), dim3(512), 0, stream, a);
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || split == 1) return e;
+  return launch_finish(p, split, 32 * mt, m_valid, a.ypart, gscale, t, lora_b, r, lora_vec, y,
+                       stream);
 }
+
+}  // namespace
 
 hipError_t run_decode_chunks(const LinearPlan& p, const uint8_t* codes,
                              const uint8_t* scales, const float* gscale,
-                             const uint16_t* lora_a, float lora_scale,
                              const uint16_t* lora_b, uint16_t* y, char* ws,
                              hipStream_t stream) {
   decode::DecodeArgs a;
   a.codes = codes;
   a.scales = scales;
   a.gscale = gscale;
-  a.lora_a = lora_a;
   a.lora_b = lora_b;
   a.ypart = reinterpret_cast<float*>(ws + p.off_ypart);
-  a.tpart = reinterpret_cast<float*>(ws + p.off_tsplit);
-  a.cnt = reinterpret_cast<uint32_t*>(ws + p.off_cnt);
   a.n = p.n;
   a.k = p.k;
   a.nfull = p.k / 64;
@@ -75,11 +173,7 @@ hipError_t run_decode_chunks(const LinearPlan& p, const uint8_t* codes,
   a.split = p.dec_split;
   a.r = (lora_b && p.r > 0) ? p.r : 0;
   a.rpad16 = p.rpad16;
-  a.rpad32 = p.rpad32;
-  a.lora_scale = lora_scale;
   a.lora_vec = (a.r % 8 == 0) && ((reinterpret_cast<uintptr_t>(lora_b) & 15) == 0);
-  const int rt = a.r > 0 ? p.dec_rt : 0;
-  if (rt > 0 && !lora_a) return hipErrorInvalidValue;
   const uint16_t* xt = reinterpret_cast<const uint16_t*>(ws + p.off_xt);
   const uint16_t* t = reinterpret_cast<const uint16_t*>(ws + p.off_t);
   int64_t m0 = 0;
@@ -91,18 +185,20 @@ hipError_t run_decode_chunks(const LinearPlan& p, const uint8_t* codes,
     a.t = t + m0 * p.rpad16;
     a.y = y + m0 * p.n;
     a.m_valid = (int)std::min<int64_t>(32 * mt, p.m - m0);
-    if (mt <= 2 && rt == 0 && p.k % 256 == 0 && p.dec_nt <= 5) {
-      const hipError_t e = run_decode_lds(p, mt, codes, scales, gscale, a.t, lora_b, a.r,
-                                          a.lora_vec, a.xt, a.y, a.m_valid, ws, stream);
-      if (e != hipSuccess) return e;
-      m0 += 32 * mt;
-      continue;
+    hipError_t e;
+    if (mt <= 2 && p.k % 256 == 0 && p.dec_nt <= 5) {
+      e = run_decode_lds(p, mt, codes, scales, gscale, a.t, lora_b, a.r, a.lora_vec, a.xt,
+                         a.y, a.m_valid, ws, stream);
+    } else {
+      decode::DecodeKernel kern = pick_decode(mt, p.dec_nt);
+      if (!kern) return hipErrorInvalidConfiguration;
+      hipLaunchKernelGGL(kern, dim3((unsigned)p.dec_groups, (unsigned)p.dec_split),
+                         dim3(256), 0, stream, a);
+      e = hipGetLastError();
+      if (e == hipSuccess && p.dec_split > 1)
+        e = launch_finish(p, p.dec_split, 32 * mt, a.m_valid, a.ypart, gscale, a.t, lora_b,
+                          a.r, a.lora_vec, a.y, stream);
     }
-    decode::DecodeKernel kern = pick_decode(mt, p.dec_nt, rt);
-    if (!kern) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(kern, dim3((unsigned)p.dec_groups, (unsigned)p.dec_split),
-                       dim3(256), 0, stream, a);
-    const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     m0 += 32 * mt;
   }
@@ -111,11 +207,9 @@ hipError_t run_decode_chunks(const LinearPlan& p, const uint8_t* codes,
 
 hipError_t launch_linear_decode_main(const LinearPlan& p, const uint8_t* codes,
                                      const uint8_t* scales, const float* gscale,
-                                     const uint16_t* lora_a, float lora_scale,
                                      const uint16_t* lora_b, uint16_t* y, char* ws,
                                      hipStream_t stream) {
-  return run_decode_chunks(p, codes, scales, gscale, lora_a, lora_scale, lora_b, y, ws,
-                           stream);
+  return run_decode_chunks(p, codes, scales, gscale, lora_b, y, ws, stream);
 }
 
 }  // namespace qerl

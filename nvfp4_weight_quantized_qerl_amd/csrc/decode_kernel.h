@@ -22,10 +22,11 @@
 //     acc * S, plus the LoRA up-projection t B^T as extra bf16 MFMA steps
 //     (t = bf16(s x_t A^T) from the prepare step), round to bf16, store;
 //   * when the rows of a layer are too few to fill the GPU (down
-//     projections), K is also split across workgroups: each writes fp32
-//     partials, and the last workgroup of a row group to arrive (counted
-//     with an atomic) sums them in split order -- deterministic -- and
-//     runs the epilogue.  No workgroup ever waits for another.
+//     projections), K is also split across workgroups: each writes its
+//     fp32 partial tiles, and a separate finishing kernel sums them in
+//     split order (deterministic) and applies the epilogue.  A workgroup
+//     never waits for another: on gfx950 the device-scope fences an
+//     in-kernel hand-off needs write back and invalidate the L2.
 //
 // K layout inside a 64-wide block: lane (h = lane/32) of an MFMA holds
 // k = k0 + 32h + 8j + 0..7 at step j = 0..3, for both operands, so every
@@ -44,19 +45,15 @@ struct DecodeArgs {
   const uint8_t* codes;    // [n, k/2]
   const uint8_t* scales;   // [n, k/16]
   const float* gscale;
-  const uint16_t* lora_a;  // [r, k] bf16 (LoRA-down computed in the kernel)
   const uint16_t* t;       // [MT*32, rpad16] bf16 s x_t A^T (precomputed) or null
   const uint16_t* lora_b;  // [n, r] bf16
   uint16_t* y;             // [m_valid, n] rows of this m chunk
   float* ypart;            // [split, MT*32, n] fp32 partials
-  float* tpart;            // [groups, split, MT*32, rpad32] fp32 LoRA-down partials
-  uint32_t* cnt;           // [groups] arrival counters (zero on entry)
   int64_t n, k;
   int64_t units_per_split; // 64-wide K blocks per split
   int64_t nfull;           // full 64-wide K blocks
   int tail_steps;          // 16-wide steps in the last partial block
-  int m_valid, rows, split, r, rpad16, rpad32, lora_vec;
-  float lora_scale;
+  int m_valid, rows, split, r, rpad16, lora_vec;
 };
 
 __device__ __forceinline__ uint32_t comp(const uint4& v, int j) {
@@ -129,12 +126,10 @@ __device__ __forceinline__ uint32_t bload32(__amdgpu_buffer_rsrc_t r, uint32_t v
   return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
 }
 
-// Activation registers of one 64-wide K block: x_t of MT token tiles and
-// the RT LoRA-A tiles.
-template <int MT, int RT>
+// Activation registers of one 64-wide K block: x_t of MT token tiles.
+template <int MT>
 struct XStage {
   uint4 x[MT][4];
-  uint4 a[RT > 0 ? RT : 1][4];
 };
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -148,28 +143,27 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* dst, uint3
 
 
 
-// MT token tiles x (NT weight subtiles + RT LoRA-A tiles) of 32 x 32.
+// MT token tiles x NT weight subtiles of 32 x 32.
 //
 // Software pipeline per wave: the NVFP4 weight blocks (the HBM stream) go
 // global -> LDS by direct-to-LDS buffer loads into three LDS stages (no
 // register cost), and are issued two K blocks ahead of their MFMAs; the
-// activation and LoRA-A blocks (L2-resident) go to registers, one block
+// activation blocks (L2-resident) go to registers, one block
 // ahead, in the order X(kb+1), W(kb+2), MFMA(kb).  Loads of a wave retire
 // in issue order, so waiting for X(kb) never waits for W(kb+1): two weight
 // blocks stay in flight while a block is computed.  Loads are never
 // predicated (the block index is clamped; rows past the matrix read zeros
 // through the buffer bounds), which keeps the waits a fixed distance
 // behind the loads.
-template <int MT, int NT, int RT>
+template <int MT, int NT>
 __global__ __launch_bounds__(256, 1) void decode_main(DecodeArgs a) {
-  constexpr int NA = NT + RT;          // accumulator rows (weights, then LoRA)
+  constexpr int NA = NT;               // accumulator rows
   constexpr int NP = MT * NA;          // 32x32 tiles per wave
   constexpr int ROUNDS = (NP + 3) / 4;
   __shared__ float red[12 * 16 * 64];
   __shared__ __attribute__((aligned(16))) uint16_t t_lds[MT * 32 * 128];
   __shared__ __attribute__((aligned(16))) uint4 wl0[4 * NT * 64], wl1[4 * NT * 64],
       wl2[4 * NT * 64];
-  __shared__ int is_last;
 
   const int lane = threadIdx.x & 63;
   // Wave-uniform (the compiler cannot see that threadIdx.x / 64 is): keeps
@@ -187,8 +181,8 @@ __global__ __launch_bounds__(256, 1) void decode_main(DecodeArgs a) {
   const int64_t we = min(ue, wb + q);
   const int mrows = 32 * MT;
 
-  // Precomputed LoRA-down (RT == 0 with a LoRA branch): stage it in LDS.
-  if (RT == 0 && a.r > 0) {
+  // Precomputed LoRA-down t: stage it in LDS for the epilogue.
+  if (a.r > 0) {
     const int words = mrows * a.rpad16 / 8;
     for (int i = threadIdx.x; i < words; i += 256)
       reinterpret_cast<uint4*>(t_lds)[i] = reinterpret_cast<const uint4*>(a.t)[i];
@@ -201,7 +195,6 @@ __global__ __launch_bounds__(256, 1) void decode_main(DecodeArgs a) {
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.scales + row0 * kscales,
                                               (uint32_t)((a.n - row0) * kscales));
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.xt, (uint32_t)mrows * xrow_bytes);
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.lora_a, (uint32_t)(RT > 0 ? a.r : 0) * xrow_bytes);
   // Row offsets go into the per-lane offset, which the buffer range check
   // covers (rows past the end of a tensor read as zeros); the uniform
   // offset carries only the position along K.
@@ -229,19 +222,14 @@ __global__ __launch_bounds__(256, 1) void decode_main(DecodeArgs a) {
     for (int t = 0; t < NT; ++t)
       dma16(rw, wl + wslot + t * 64, vw + 32u * t * kbytes, 32u * (uint32_t)kb);
   };
-  auto load_x = [&](int64_t kb, XStage<MT, RT>& st) {
+  auto load_x = [&](int64_t kb, XStage<MT>& st) {
 #pragma unroll
     for (int u = 0; u < MT; ++u)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         st.x[u][i] = bload128(rx, vx, 32u * u * xrow_bytes + 128u * (uint32_t)kb + 16u * i);
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        st.a[rt][i] = bload128(ra, vx + 32u * rt * xrow_bytes, 128u * (uint32_t)kb + 16u * i);
   };
-  auto compute = [&](const uint4* wl, const uint32_t (&sw)[NT], const XStage<MT, RT>& xs) {
+  auto compute = [&](const uint4* wl, const uint32_t (&sw)[NT], const XStage<MT>& xs) {
     uint4 w[NT];
     float sb0[NT], sb1[NT];
 #pragma unroll
@@ -258,17 +246,12 @@ __global__ __launch_bounds__(256, 1) void decode_main(DecodeArgs a) {
 #pragma unroll
         for (int u = 0; u < MT; ++u) acc[t][u] = mfma_bf16(xs.x[u][j], b, acc[t][u]);
       }
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-        for (int u = 0; u < MT; ++u)
-          acc[NT + rt][u] = mfma_bf16(xs.x[u][j], xs.a[rt][j], acc[NT + rt][u]);
     }
   };
 
   const int64_t fe = min(we, a.nfull);
   if (wb < fe) {
-    XStage<MT, RT> x0, x1;
+    XStage<MT> x0, x1;
     uint32_t sl0[NT], sl1[NT], sl2[NT];
     const int64_t last = fe - 1;
     load_w(wb, wl0, sl0);
@@ -314,12 +297,6 @@ __global__ __launch_bounds__(256, 1) void decode_main(DecodeArgs a) {
 #pragma unroll
         for (int u = 0; u < MT; ++u) acc[t][u] = mfma_bf16(xs[u], b, acc[t][u]);
       }
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        const uint4 av = bload128(ra, vx16 + 32u * rt * xrow_bytes, 2u * k0);
-#pragma unroll
-        for (int u = 0; u < MT; ++u) acc[NT + rt][u] = mfma_bf16(xs[u], av, acc[NT + rt][u]);
-      }
     }
   }
 
@@ -351,26 +328,8 @@ __global__ __launch_bounds__(256, 1) void decode_main(DecodeArgs a) {
     __syncthreads();
   }
 
-  // LoRA-down tiles -> bf16(s t) in LDS for every wave's epilogue.
-  auto stage_t = [&](int p, const f32x16_t& tv) {
-    const int jt = p / MT - NT, u = p % MT;
-    const int j = 32 * jt + c;
-    if (j < a.rpad16) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v)
-        t_lds[(32 * u + acc_row(v, lane)) * a.rpad16 + j] =
-            f32_to_bf16_bits(a.lora_scale * tv[v]);
-    }
-  };
-
   const float S = *a.gscale;
   if (a.split == 1) {
-    if (RT > 0) {
-#pragma unroll
-      for (int p = MT * NT; p < NP; ++p)
-        if (wave == (p & 3)) stage_t(p, acc[p / MT][p % MT]);
-      __syncthreads();
-    }
 #pragma unroll
     for (int p = 0; p < MT * NT; ++p)
       if (wave == (p & 3))
@@ -378,107 +337,48 @@ __global__ __launch_bounds__(256, 1) void decode_main(DecodeArgs a) {
                       live[p / MT], lane, t_lds);
     return;
   }
-
+  // Split K: this workgroup's fp32 partial tiles; the finishing kernel
+  // sums the splits and applies the epilogue.
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
-    if (wave != (p & 3)) continue;
-    if (p < MT * NT) {
-      if (live[p / MT]) {
-        const int64_t row = row0 + 32 * (p / MT) + c;
-        float* dst = a.ypart + ((int64_t)split_id * mrows + 32 * (p % MT)) * a.n + row;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) dst[(int64_t)acc_row(v, lane) * a.n] = acc[p / MT][p % MT][v];
-      }
-    } else {
-      const int j = 32 * (p / MT - NT) + c;
-      float* dst = a.tpart + (((int64_t)blockIdx.x * a.split + split_id) * mrows + 32 * (p % MT)) *
-                   a.rpad32 + j;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) dst[acc_row(v, lane) * a.rpad32] = acc[p / MT][p % MT][v];
-    }
-  }
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t old = __hip_atomic_fetch_add(a.cnt + blockIdx.x, 1u, __ATOMIC_ACQ_REL,
-                                                __HIP_MEMORY_SCOPE_AGENT);
-    is_last = (old == (uint32_t)(a.split - 1)) ? 1 : 0;
-  }
-  __syncthreads();
-  if (!is_last) return;
-  __threadfence();
-#pragma unroll
-  for (int p = MT * NT; p < NP; ++p) {
-    if (wave == (p & 3)) {
-      f32x16_t sum = zero16();
-      const int j = 32 * (p / MT - NT) + c;
-      for (int s = 0; s < a.split; ++s) {
-        const float* src = a.tpart + (((int64_t)blockIdx.x * a.split + s) * mrows + 32 * (p % MT)) *
-                           a.rpad32 + j;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) sum[v] += src[acc_row(v, lane) * a.rpad32];
-      }
-      stage_t(p, sum);
-    }
-  }
-  if (RT > 0) __syncthreads();
-#pragma unroll
-  for (int p = 0; p < MT * NT; ++p) {
-    if (wave == (p & 3)) {
+    if (wave == (p & 3) && live[p / MT]) {
       const int64_t row = row0 + 32 * (p / MT) + c;
-      f32x16_t sum = zero16();
-      if (live[p / MT]) {
-        for (int s = 0; s < a.split; ++s) {
-          const float* src = a.ypart + ((int64_t)s * mrows + 32 * (p % MT)) * a.n + row;
+      float* dst = a.ypart + ((int64_t)split_id * mrows + 32 * (p % MT)) * a.n + row;
 #pragma unroll
-          for (int v = 0; v < 16; ++v) sum[v] += src[(int64_t)acc_row(v, lane) * a.n];
-        }
-      }
-      epilogue_tile(a, sum, S, p % MT, row, live[p / MT], lane, t_lds);
+      for (int v = 0; v < 16; ++v) dst[(int64_t)acc_row(v, lane) * a.n] = acc[p / MT][p % MT][v];
     }
   }
-  if (threadIdx.x == 0) a.cnt[blockIdx.x] = 0u;
 }
 
 typedef void (*DecodeKernel)(DecodeArgs);
 
-// decode_main<MT, NT, RT> if its accumulators fit ((NT + RT) * MT <= 12
-// tiles of 32 x 32), else null.
-template <int MT, int NT, int RT>
+// decode_main<MT, NT> if its accumulators fit (NT * MT <= 12 tiles of
+// 32 x 32), else null.
+template <int MT, int NT>
 DecodeKernel kernel_or_null() {
-  if constexpr ((NT + RT) * MT <= 12 && NT >= 1) {
-    return decode_main<MT, NT, RT>;
+  if constexpr (NT * MT <= 12 && NT >= 1) {
+    return decode_main<MT, NT>;
   } else {
     return nullptr;
   }
 }
 
-template <int MT, int RT>
-DecodeKernel pick_nt(int nt) {
-  switch (nt) {
-    case 1: return kernel_or_null<MT, 1, RT>();
-    case 2: return kernel_or_null<MT, 2, RT>();
-    case 3: return kernel_or_null<MT, 3, RT>();
-    case 4: return kernel_or_null<MT, 4, RT>();
-    case 5: return kernel_or_null<MT, 5, RT>();
-    case 6: return kernel_or_null<MT, 6, RT>();
-    default: return nullptr;
-  }
-}
-
 template <int MT>
-DecodeKernel pick_mt(int nt, int rt) {
-  switch (rt) {
-    case 0: return pick_nt<MT, 0>(nt);
-    case 1: return pick_nt<MT, 1>(nt);
-    case 2: return pick_nt<MT, 2>(nt);
+DecodeKernel pick_mt(int nt) {
+  switch (nt) {
+    case 1: return kernel_or_null<MT, 1>();
+    case 2: return kernel_or_null<MT, 2>();
+    case 3: return kernel_or_null<MT, 3>();
+    case 4: return kernel_or_null<MT, 4>();
+    case 5: return kernel_or_null<MT, 5>();
+    case 6: return kernel_or_null<MT, 6>();
     default: return nullptr;
   }
 }
 
-DecodeKernel pick_mt1(int nt, int rt);
-DecodeKernel pick_mt2(int nt, int rt);
-DecodeKernel pick_mt4(int nt, int rt);
+DecodeKernel pick_mt1(int nt);
+DecodeKernel pick_mt2(int nt);
+DecodeKernel pick_mt4(int nt);
 
 }  // namespace decode
 }  // namespace qerl

@@ -45,7 +45,6 @@ struct Args {
   const uint16_t* lora_b;  // [n, r] bf16
   uint16_t* y;             // [m_valid, n]
   float* ypart;            // [split, MT*32, n] fp32 partials
-  uint32_t* cnt;           // [groups] arrival counters (zero on entry)
   int64_t n, k;
   int64_t blocks_per_split;  // 256-wide K blocks per split
   int m_valid, rows, split, r, rpad16, lora_vec;
@@ -137,7 +136,6 @@ __global__ __launch_bounds__(512, 1) void decode_lds(Args a) {
   __shared__ __attribute__((aligned(16))) uint4 sc0[256], sc1[256], sc2[256];
   __shared__ __attribute__((aligned(16))) uint4 xs0[XROWS * 32], xs1[XROWS * 32];
   __shared__ __attribute__((aligned(16))) uint16_t t_lds[XROWS * 128];
-  __shared__ int is_last;
 
   const int lane = threadIdx.x & 63;
   // Wave-uniform values the compiler cannot prove uniform by itself.
@@ -315,6 +313,8 @@ __global__ __launch_bounds__(512, 1) void decode_lds(Args a) {
     return;
   }
 
+  // Split K: this workgroup's fp32 partial tiles; the finishing kernel
+  // sums the splits and applies the epilogue.
 #pragma unroll
   for (int p = 0; p < NT0 * MT; ++p) {
     if (owns(p) && tile_live(p)) {
@@ -323,31 +323,6 @@ __global__ __launch_bounds__(512, 1) void decode_lds(Args a) {
       for (int v = 0; v < 16; ++v) dst[(int64_t)acc_row(v, lane) * a.n] = acc[p / MT][p % MT][v];
     }
   }
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t old = __hip_atomic_fetch_add(a.cnt + blockIdx.x, 1u, __ATOMIC_ACQ_REL,
-                                                __HIP_MEMORY_SCOPE_AGENT);
-    is_last = (old == (uint32_t)(a.split - 1)) ? 1 : 0;
-  }
-  __syncthreads();
-  if (!is_last) return;
-  __threadfence();
-#pragma unroll
-  for (int p = 0; p < NT0 * MT; ++p) {
-    if (owns(p)) {
-      f32x16_t sum = zero16();
-      if (tile_live(p)) {
-        for (int s = 0; s < a.split; ++s) {
-          const float* src = a.ypart + ((int64_t)s * XROWS + 32 * (p % MT)) * a.n + tile_row(p);
-#pragma unroll
-          for (int v = 0; v < 16; ++v) sum[v] += src[(int64_t)acc_row(v, lane) * a.n];
-        }
-      }
-      epilogue_tile(a, sum, S, p % MT, tile_row(p), tile_live(p), lane, t_lds);
-    }
-  }
-  if (threadIdx.x == 0) a.cnt[blockIdx.x] = 0u;
 }
 
 typedef void (*Kernel)(Args);

@@ -4,7 +4,7 @@
 namespace qerl {
 namespace decode {
 
-DecodeKernel pick_mt1(int nt, int rt) { return pick_mt<1>(nt, rt); }
+DecodeKernel pick_mt1(int nt) { return pick_mt<1>(nt); }
 
 }  // namespace decode
 }  // namespace qerl

@@ -4,7 +4,7 @@
 namespace qerl {
 namespace decode {
 
-DecodeKernel pick_mt2(int nt, int rt) { return pick_mt<2>(nt, rt); }
+DecodeKernel pick_mt2(int nt) { return pick_mt<2>(nt); }
 
 }  // namespace decode
 }  // namespace qerl

@@ -4,7 +4,7 @@
 namespace qerl {
 namespace decode {
 
-DecodeKernel pick_mt4(int nt, int rt) { return pick_mt<4>(nt, rt); }
+DecodeKernel pick_mt4(int nt) { return pick_mt<4>(nt); }
 
 }  // namespace decode
 }  // namespace qerl

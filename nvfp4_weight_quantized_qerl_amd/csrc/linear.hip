@@ -7,19 +7,16 @@
 //     x_t = x (.) (1 + z)
 //     y   = bf16( S * (x_t W0^T) + (s x_t A^T) B^T ),  W0 = e2m1 (.) s_b
 // S (the FP32 tensor scale) is applied to the fp32 accumulator once in the
-// epilogue, so the in-register dequantized weight W0 = e2m1 * s_b is exact
-// in bf16.
+// epilogue, so the dequantized weight W0 = e2m1 * s_b is exact in bf16.
 //
 // prepare writes x_t = bf16(x * (1 + z)) to the workspace, rows padded to a
 // multiple of 32 with zeros so the contraction kernels need no row masks,
-// and clears the split-K arrival counters of the decode kernel.  When the
-// plan does not compute the LoRA-down inside the decode contraction
-// (plan.dec_rt == 0), it also produces t:
-//   prep_kernel (one wave per 32 rows x K chunk): x_t and
+// and, with a LoRA branch, the LoRA-down t:
+//   prep_kernel (four waves per 32 rows x 512-wide K chunk): x_t and
 //           tpart = x_t A^T over the chunk (bf16 MFMA, fp32);
 //   treduce: t = bf16(s * sum over chunks of tpart), summed in chunk order
 //           so the result is deterministic.
-// Otherwise a single elementwise kernel (xt_kernel) writes x_t.
+// Without a LoRA branch a single elementwise kernel (xt_kernel) writes x_t.
 #include <algorithm>
 
 #include "qerl_device.h"
@@ -44,34 +41,18 @@ namespace {
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int64_t rup(int64_t a, int64_t b) { return cdiv(a, b) * b; }
 
-// In-kernel LoRA-down needs RT more accumulator tiles per wave; at the
-// decode shapes that pushes the wave to the register limit and the compiler
-// then sinks the prefetch loads, so the prepare step computes it instead.
-constexpr bool kDecodeInKernelLora = false;
+// K range of one prepare workgroup: four waves of 128.
+constexpr int64_t kPrepChunk = 512;
 
-// Largest weight subtile count NT per wave that the decode kernel holds in
-// registers without spilling, for MT token tiles and RT in-kernel LoRA-down
-// tiles (measured from the compiler's resource report).
-int decode_nt_max(int mt, int rt) {
-  static const int table[3][3] = {{6, 6, 6}, {5, 5, 3}, {3, 2, 0}};
-  const int mi = mt == 1 ? 0 : (mt == 2 ? 1 : 2);
-  return rt <= 2 ? table[mi][rt] : 0;
-}
+// Largest weight subtile count NT per wave that the decode kernels hold in
+// registers without spilling, for MT token tiles (from the compiler's
+// resource report).
+int decode_nt_max(int mt) { return mt == 1 ? 6 : (mt == 2 ? 5 : 3); }
 
-// Decode rows-per-workgroup, LoRA-down placement and split-K choice for one
-// m tile count.  The LoRA-down runs inside the contraction (RT extra
-// accumulator tiles, no separate kernels) when that still leaves >= 4
-// weight subtiles, i.e. costs at most half as much MFMA work as the
-// weights.
+// Decode rows per workgroup and split-K choice for one m tile count.
 void plan_decode(LinearPlan* p, int mt) {
   const int cu = device_cu_count();
-  const int rt = p->rpad32 / 32;
-  int ntmax = decode_nt_max(mt, 0);
-  p->dec_rt = 0;
-  if (kDecodeInKernelLora && rt > 0 && rt <= 2 && decode_nt_max(mt, rt) >= 4) {
-    p->dec_rt = rt;
-    ntmax = decode_nt_max(mt, rt);
-  }
+  const int ntmax = decode_nt_max(mt);
   const int64_t n = p->n;
   const int64_t units = cdiv(p->k, 64);     // 64-wide K blocks (last may be partial)
   const int64_t rows_per_cu = cdiv(n, cu);
@@ -120,14 +101,9 @@ bool make_linear_plan(int64_t m, int64_t n, int64_t k, int r, LinearPlan* p) {
   p->mpad = rup(m, 32);
   p->rpad32 = r ? (int)rup(r, 32) : 0;
   p->rpad16 = r ? (int)rup(r, 16) : 0;
-  const int cu = device_cu_count();
-  const int64_t ksteps = k / 16;
   const int64_t mtiles = p->mpad / 32;
-  int64_t kc = std::max<int64_t>(1, cdiv(2 * cu, mtiles));
-  kc = std::min<int64_t>(kc, std::max<int64_t>(1, ksteps / 16));
-  const int64_t steps_per = cdiv(ksteps, kc);
-  p->kchunks = (int)cdiv(ksteps, steps_per);
-  p->kchunk = steps_per * 16;
+  p->kchunk = kPrepChunk;
+  p->kchunks = (int)cdiv(k, kPrepChunk);
   const int mt = (int)std::min<int64_t>(4, mtiles);
   plan_decode(p, mt);
   p->pf_tile_m = 128;
@@ -141,14 +117,9 @@ bool make_linear_plan(int64_t m, int64_t n, int64_t k, int r, LinearPlan* p) {
   p->off_xt = take((size_t)p->mpad * k * 2);
   p->off_tpart = take(r ? (size_t)p->kchunks * p->mpad * p->rpad32 * 4 : 0);
   p->off_t = take(r ? (size_t)p->mpad * p->rpad16 * 2 : 0);
-  p->off_cnt = take((size_t)p->dec_groups * 4);
   p->off_ypart = take(p->dec_split > 1
                           ? (size_t)p->dec_split * 32 * p->dec_mt * n * 4
                           : 0);
-  p->off_tsplit = take(p->dec_split > 1 && p->dec_rt > 0
-                           ? (size_t)p->dec_groups * p->dec_split * 32 * p->dec_mt *
-                                 p->rpad32 * 4
-                           : 0);
   p->total = off;
   return true;
 }
@@ -156,58 +127,89 @@ bool make_linear_plan(int64_t m, int64_t n, int64_t k, int r, LinearPlan* p) {
 namespace {
 
 struct PrepArgs {
-  const uint16_t* x;
-  const float* z;
-  const uint16_t* a;
-  uint16_t* xt;
-  float* tpart;
-  uint32_t* cnt;
-  int64_t m, mpad, k, kchunk;
-  int r, rpad32, ncnt;
+  const uint16_t* __restrict__ x;
+  const float* __restrict__ z;
+  const uint16_t* __restrict__ a;
+  uint16_t* __restrict__ xt;
+  float* __restrict__ tpart;
+  int64_t m, mpad, k;
+  int r, rpad32;
 };
 
+// x_t = bf16(x (1 + z)) of 8 consecutive channels from their noise z0, z1.
+__device__ __forceinline__ uint4 noisy8(uint4 xv, float4 z0, float4 z1) {
+  xv.x = pack_bf16x2(bf16_to_f32(xv.x & 0xffffu) * (1.0f + z0.x),
+                     bf16_to_f32(xv.x >> 16) * (1.0f + z0.y));
+  xv.y = pack_bf16x2(bf16_to_f32(xv.y & 0xffffu) * (1.0f + z0.z),
+                     bf16_to_f32(xv.y >> 16) * (1.0f + z0.w));
+  xv.z = pack_bf16x2(bf16_to_f32(xv.z & 0xffffu) * (1.0f + z1.x),
+                     bf16_to_f32(xv.z >> 16) * (1.0f + z1.y));
+  xv.w = pack_bf16x2(bf16_to_f32(xv.w & 0xffffu) * (1.0f + z1.z),
+                     bf16_to_f32(xv.w >> 16) * (1.0f + z1.w));
+  return xv;
+}
+
+// One workgroup: 32 rows x one 512-wide K chunk, wave w taking the 128
+// channels at 128 w.  Each lane issues all of its loads (8 steps of x, z
+// and RT rows of A) before the first MFMA, so the chunk costs about one
+// memory latency.  The four waves' LoRA-down tiles are summed through LDS
+// and wave 0 writes the chunk's partial tpart[chunk, rows, rpad32].
 template <int RT>
-__global__ __launch_bounds__(64) void prep_kernel(PrepArgs p) {
-  const int lane = threadIdx.x, h = lane >> 5, c = lane & 31;
+__global__ __launch_bounds__(256) void prep_kernel(PrepArgs p) {
+  constexpr int STEPS = 8;
+  __shared__ float red[3 * (RT > 0 ? RT : 1) * 16 * 64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int h = lane >> 5, c = lane & 31;
   const int64_t mrow = (int64_t)blockIdx.x * 32 + c;
-  const int64_t kbeg = (int64_t)blockIdx.y * p.kchunk;
-  const int64_t kend = std::min(p.k, kbeg + p.kchunk);
-  if (blockIdx.x == 0 && blockIdx.y == 0)
-    for (int i = lane; i < p.ncnt; i += 64) p.cnt[i] = 0u;
-  f32x16_t acc[RT > 0 ? RT : 1];
-#pragma unroll
-  for (int t = 0; t < (RT > 0 ? RT : 1); ++t) acc[t] = zero16();
+  const int64_t kb = (int64_t)blockIdx.y * kPrepChunk + 128 * wave;
   const bool live = mrow < p.m;
   const uint16_t* xrow = p.x + mrow * p.k;
   uint16_t* xtrow = p.xt + mrow * p.k;
-  for (int64_t ks = kbeg; ks < kend; ks += 16) {
-    const int64_t k0 = ks + 8 * h;
-    uint4 xv = live ? *reinterpret_cast<const uint4*>(xrow + k0)
-                    : make_uint4(0u, 0u, 0u, 0u);
-    if (p.z) {
-      const float4 z0 = *reinterpret_cast<const float4*>(p.z + k0);
-      const float4 z1 = *reinterpret_cast<const float4*>(p.z + k0 + 4);
-      xv.x = pack_bf16x2(bf16_to_f32(xv.x & 0xffffu) * (1.0f + z0.x),
-                         bf16_to_f32(xv.x >> 16) * (1.0f + z0.y));
-      xv.y = pack_bf16x2(bf16_to_f32(xv.y & 0xffffu) * (1.0f + z0.z),
-                         bf16_to_f32(xv.y >> 16) * (1.0f + z0.w));
-      xv.z = pack_bf16x2(bf16_to_f32(xv.z & 0xffffu) * (1.0f + z1.x),
-                         bf16_to_f32(xv.z >> 16) * (1.0f + z1.y));
-      xv.w = pack_bf16x2(bf16_to_f32(xv.w & 0xffffu) * (1.0f + z1.z),
-                         bf16_to_f32(xv.w >> 16) * (1.0f + z1.w));
-    }
-    *reinterpret_cast<uint4*>(xtrow + k0) = xv;
+  uint4 xv[STEPS];
+  float4 z0[STEPS], z1[STEPS];
+  uint4 av[RT > 0 ? RT : 1][STEPS];
+  const float4 zero4 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+  for (int s = 0; s < STEPS; ++s) {
+    const int64_t k0 = kb + 16 * s + 8 * h;
+    const bool in = kb + 16 * s < p.k;   // k % 16 == 0: the whole step is in range
+    xv[s] = (in && live) ? *reinterpret_cast<const uint4*>(xrow + k0) : make_uint4(0u, 0u, 0u, 0u);
+    z0[s] = (in && p.z) ? *reinterpret_cast<const float4*>(p.z + k0) : zero4;
+    z1[s] = (in && p.z) ? *reinterpret_cast<const float4*>(p.z + k0 + 4) : zero4;
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
       const int j = 32 * t + c;
-      const uint4 av = (j < p.r)
-          ? *reinterpret_cast<const uint4*>(p.a + (int64_t)j * p.k + k0)
-          : make_uint4(0u, 0u, 0u, 0u);
-      acc[t] = mfma_bf16(xv, av, acc[t]);
+      av[t][s] = (in && j < p.r) ? *reinterpret_cast<const uint4*>(p.a + (int64_t)j * p.k + k0)
+                                 : make_uint4(0u, 0u, 0u, 0u);
     }
   }
+  f32x16_t acc[RT > 0 ? RT : 1];
+#pragma unroll
+  for (int t = 0; t < (RT > 0 ? RT : 1); ++t) acc[t] = zero16();
+#pragma unroll
+  for (int s = 0; s < STEPS; ++s) {
+    const int64_t k0 = kb + 16 * s + 8 * h;
+    if (kb + 16 * s >= p.k) break;
+    if (live && p.z) xv[s] = noisy8(xv[s], z0[s], z1[s]);
+    *reinterpret_cast<uint4*>(xtrow + k0) = xv[s];
+#pragma unroll
+    for (int t = 0; t < RT; ++t) acc[t] = mfma_bf16(xv[s], av[t][s], acc[t]);
+  }
+  if (RT == 0) return;
+  if (wave > 0) {
+#pragma unroll
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) red[(((wave - 1) * RT + t) * 16 + v) * 64 + lane] = acc[t][v];
+  }
+  __syncthreads();
+  if (wave > 0) return;
 #pragma unroll
   for (int t = 0; t < RT; ++t) {
+#pragma unroll
+    for (int w = 0; w < 3; ++w)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[t][v] += red[((w * RT + t) * 16 + v) * 64 + lane];
     float* dst = p.tpart + ((int64_t)blockIdx.y * p.mpad + (int64_t)blockIdx.x * 32) * p.rpad32
                  + 32 * t + c;
 #pragma unroll
@@ -215,33 +217,26 @@ __global__ __launch_bounds__(64) void prep_kernel(PrepArgs p) {
   }
 }
 
-// x_t = bf16(x (1 + z)) only (the decode kernel computes the LoRA-down
-// itself): 8 elements per thread; rows m..mpad-1 are written as zeros.
+// x_t = bf16(x (1 + z)) only (no LoRA branch): 8 elements per thread; rows
+// m..mpad-1 are written as zeros.
 __global__ __launch_bounds__(256) void xt_kernel(PrepArgs p) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < p.ncnt) p.cnt[i] = 0u;
   const int64_t per_row = p.k / 8;
   if (i >= p.mpad * per_row) return;
   const int64_t mrow = i / per_row, k0 = (i % per_row) * 8;
   uint4 xv = make_uint4(0u, 0u, 0u, 0u);
   if (mrow < p.m) {
     xv = *reinterpret_cast<const uint4*>(p.x + mrow * p.k + k0);
-    if (p.z) {
-      const float4 z0 = *reinterpret_cast<const float4*>(p.z + k0);
-      const float4 z1 = *reinterpret_cast<const float4*>(p.z + k0 + 4);
-      xv.x = pack_bf16x2(bf16_to_f32(xv.x & 0xffffu) * (1.0f + z0.x),
-                         bf16_to_f32(xv.x >> 16) * (1.0f + z0.y));
-      xv.y = pack_bf16x2(bf16_to_f32(xv.y & 0xffffu) * (1.0f + z0.z),
-                         bf16_to_f32(xv.y >> 16) * (1.0f + z0.w));
-      xv.z = pack_bf16x2(bf16_to_f32(xv.z & 0xffffu) * (1.0f + z1.x),
-                         bf16_to_f32(xv.z >> 16) * (1.0f + z1.y));
-      xv.w = pack_bf16x2(bf16_to_f32(xv.w & 0xffffu) * (1.0f + z1.z),
-                         bf16_to_f32(xv.w >> 16) * (1.0f + z1.w));
-    }
+    if (p.z)
+      xv = noisy8(xv, *reinterpret_cast<const float4*>(p.z + k0),
+                  *reinterpret_cast<const float4*>(p.z + k0 + 4));
   }
   *reinterpret_cast<uint4*>(p.xt + mrow * p.k + k0) = xv;
 }
 
+// t = bf16(s * sum over chunks of tpart): one thread per (row, j); the
+// chunks are summed in a fixed order (four interleaved partial sums, then
+// combined), so the result is deterministic.
 __global__ __launch_bounds__(256) void treduce_kernel(const float* __restrict__ tpart,
                                                       uint16_t* __restrict__ t,
                                                       int64_t mpad, int rpad32,
@@ -251,9 +246,16 @@ __global__ __launch_bounds__(256) void treduce_kernel(const float* __restrict__ 
   if (i >= mpad * rpad16) return;
   const int64_t mrow = i / rpad16;
   const int j = (int)(i % rpad16);
-  float sum = 0.0f;
-  for (int c = 0; c < kchunks; ++c) sum += tpart[((int64_t)c * mpad + mrow) * rpad32 + j];
-  t[i] = f32_to_bf16_bits(s * sum);
+  const float* src = tpart + mrow * rpad32 + j;
+  const int64_t stride = mpad * rpad32;
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  int c = 0;
+  for (; c + 4 <= kchunks; c += 4) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc[u] += src[(c + u) * stride];
+  }
+  for (; c < kchunks; ++c) acc[c & 3] += src[c * stride];
+  t[i] = f32_to_bf16_bits(s * ((acc[0] + acc[1]) + (acc[2] + acc[3])));
 }
 
 }  // namespace
@@ -268,27 +270,22 @@ hipError_t launch_linear_prepare(const LinearPlan& p, const uint16_t* x,
   a.a = lora_a;
   a.xt = reinterpret_cast<uint16_t*>(ws + p.off_xt);
   a.tpart = reinterpret_cast<float*>(ws + p.off_tpart);
-  a.cnt = reinterpret_cast<uint32_t*>(ws + p.off_cnt);
   a.m = p.m;
   a.mpad = p.mpad;
   a.k = p.k;
-  a.kchunk = p.kchunk;
   a.r = p.r;
   a.rpad32 = p.rpad32;
-  a.ncnt = p.dec_groups;
-  if (p.r == 0 || p.dec_rt > 0 || !lora_a) {
-    // The decode contraction computes the LoRA-down (or there is none).
-    const int64_t threads = std::max<int64_t>(p.mpad * p.k / 8, a.ncnt);
+  if (p.r == 0 || !lora_a) {
+    const int64_t threads = p.mpad * p.k / 8;
     hipLaunchKernelGGL(xt_kernel, dim3((unsigned)cdiv(threads, 256)), dim3(256), 0, stream, a);
     return hipGetLastError();
   }
   const dim3 grid((unsigned)(p.mpad / 32), (unsigned)p.kchunks);
   switch (p.rpad32 / 32) {
-    case 0: hipLaunchKernelGGL(prep_kernel<0>, grid, dim3(64), 0, stream, a); break;
-    case 1: hipLaunchKernelGGL(prep_kernel<1>, grid, dim3(64), 0, stream, a); break;
-    case 2: hipLaunchKernelGGL(prep_kernel<2>, grid, dim3(64), 0, stream, a); break;
-    case 3: hipLaunchKernelGGL(prep_kernel<3>, grid, dim3(64), 0, stream, a); break;
-    case 4: hipLaunchKernelGGL(prep_kernel<4>, grid, dim3(64), 0, stream, a); break;
+    case 1: hipLaunchKernelGGL(prep_kernel<1>, grid, dim3(256), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL(prep_kernel<2>, grid, dim3(256), 0, stream, a); break;
+    case 3: hipLaunchKernelGGL(prep_kernel<3>, grid, dim3(256), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL(prep_kernel<4>, grid, dim3(256), 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();

@@ -7,11 +7,9 @@ namespace qerl {
 
 hipError_t launch_linear_prefill_main(const LinearPlan& p, const uint8_t* codes,
                                       const uint8_t* scales, const float* gscale,
-                                      const uint16_t* lora_a, float lora_scale,
                                       const uint16_t* lora_b, uint16_t* y, char* ws,
                                       hipStream_t stream) {
-  return run_decode_chunks(p, codes, scales, gscale, lora_a, lora_scale, lora_b, y, ws,
-                           stream);
+  return run_decode_chunks(p, codes, scales, gscale, lora_b, y, ws, stream);
 }
 
 }  // namespace qerl

@@ -38,13 +38,11 @@ struct LinearPlan {
   int dec_rows;        // weight rows per workgroup (<= 32 * dec_nt)
   int dec_groups;      // row groups = ceil(n / dec_rows)
   int dec_split;       // K splits across workgroups
-  int dec_rt;          // LoRA-down 32-wide tiles computed inside the decode
-                       // kernel (0: precomputed by the prepare step)
   int64_t dec_kblk_per_split;  // 64-wide K blocks per split
   // prefill main kernel
   int pf_tile_m, pf_tile_n;
   // workspace byte offsets
-  size_t off_xt, off_tpart, off_t, off_cnt, off_ypart, off_tsplit, total;
+  size_t off_xt, off_tpart, off_t, off_ypart, total;
 };
 
 bool make_linear_plan(int64_t m, int64_t n, int64_t k, int r, LinearPlan* p);
@@ -54,12 +52,10 @@ hipError_t launch_linear_prepare(const LinearPlan& p, const uint16_t* x,
                                  float lora_scale, char* ws,
                                  hipStream_t stream);
 
-// The contraction kernels read x_t (and, when the plan precomputes it, the
-// LoRA-down t) from the workspace; with plan.dec_rt > 0 the decode kernel
-// computes the LoRA-down itself from lora_a.
+// The contraction kernels read x_t and the LoRA-down t = bf16(s x_t A^T)
+// that launch_linear_prepare left in the workspace.
 hipError_t launch_linear_decode_main(const LinearPlan& p, const uint8_t* codes,
                                      const uint8_t* scales, const float* gscale,
-                                     const uint16_t* lora_a, float lora_scale,
                                      const uint16_t* lora_b, uint16_t* y, char* ws,
                                      hipStream_t stream);
 
@@ -67,13 +63,11 @@ hipError_t launch_linear_decode_main(const LinearPlan& p, const uint8_t* codes,
 // fallback of the prefill entry point for shapes its tiles do not cover).
 hipError_t run_decode_chunks(const LinearPlan& p, const uint8_t* codes,
                              const uint8_t* scales, const float* gscale,
-                             const uint16_t* lora_a, float lora_scale,
                              const uint16_t* lora_b, uint16_t* y, char* ws,
                              hipStream_t stream);
 
 hipError_t launch_linear_prefill_main(const LinearPlan& p, const uint8_t* codes,
                                       const uint8_t* scales, const float* gscale,
-                                      const uint16_t* lora_a, float lora_scale,
                                       const uint16_t* lora_b, uint16_t* y, char* ws,
                                       hipStream_t stream);
 

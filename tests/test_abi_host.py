@@ -41,7 +41,7 @@ def test_status_strings():
     for s in range(7):
         assert lib.qerl_status_string(s).decode().startswith("QERL_")
     assert b"unknown" in lib.qerl_status_string(99)
-    assert lib.qerl_abi_version() == 1
+    assert lib.qerl_abi_version() == 2
 
 
 FAKE = ctypes.c_void_p(0x10000)        # aligned, never dereferenced on error
@@ -119,7 +119,9 @@ def test_linear_validation():
     assert pre(FAKE, 4, 64, 64, None, 8, 1.0, None, FAKE, W, None) == 1
     assert pre(FAKE, 4, 64, 64, FAKE, 8, 1.0, None, FAKE, 1, None) == 5
     dp = lib.qerl_linear_decode_prepared
-    assert dp(4, FAKE, FAKE, FAKE, 64, 64, FAKE, None, 8, 2.0, FAKE, FAKE, W, None) == 1
-    assert dp(4, FAKE, FAKE, FAKE, 64, 64, None, FAKE, 8, 2.0, FAKE, FAKE, W, None) == 1
-    assert dp(4, FAKE, FAKE, FAKE, 64, 64, MIS, FAKE, 8, 2.0, FAKE, FAKE, W, None) == 3
-    assert dp(4, FAKE, FAKE, FAKE, 64, 64, FAKE, FAKE, 8, 2.0, FAKE, FAKE, 16, None) == 5
+    assert dp(4, FAKE, FAKE, FAKE, 64, 64, None, 8, FAKE, FAKE, W, None) == 1
+    assert dp(4, None, FAKE, FAKE, 64, 64, FAKE, 8, FAKE, FAKE, W, None) == 1
+    assert dp(4, MIS, FAKE, FAKE, 64, 64, FAKE, 8, FAKE, FAKE, W, None) == 3
+    assert dp(4, FAKE, FAKE, FAKE, 64, 40, FAKE, 8, FAKE, FAKE, W, None) == 2
+    assert dp(4, FAKE, FAKE, FAKE, 64, 64, FAKE, 200, FAKE, FAKE, W, None) == 4
+    assert dp(4, FAKE, FAKE, FAKE, 64, 64, FAKE, 8, FAKE, FAKE, 16, None) == 5
