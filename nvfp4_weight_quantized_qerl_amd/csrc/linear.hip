@@ -104,7 +104,9 @@ bool make_linear_plan(int64_t m, int64_t n, int64_t k, int r, LinearPlan* p) {
   const int64_t mtiles = p->mpad / 32;
   p->kchunk = kPrepChunk;
   p->kchunks = (int)cdiv(k, kPrepChunk);
-  const int mt = (int)std::min<int64_t>(4, mtiles);
+  // Token tiles per decode launch: 1, 2 or 4 (the instantiated kernels);
+  // run_decode_chunks takes smaller chunks for the remainder.
+  const int mt = mtiles >= 4 ? 4 : (mtiles >= 2 ? 2 : 1);
   plan_decode(p, mt);
   p->pf_tile_m = 128;
   p->pf_tile_n = 128;

@@ -1,15 +1,76 @@
-// Prefill contraction entry point.  Until the LDS-tiled kernel covers a
-// shape, the prefill path runs the decode contraction over m in chunks of
-// 128 rows (same arithmetic, same result).
+// Prefill contraction entry point: the LDS-tiled NVFP4 GEMM of
+// prefill_kernel.h for m > 64, the decode contraction for fewer tokens.
+#include <algorithm>
+
+#include "prefill_kernel.h"
 #include "qerl_internal.h"
 
 namespace qerl {
+
+namespace {
+
+typedef void (*GemmKernel)(prefill::Args);
+
+struct TileConfig {
+  int bm, bn;
+  GemmKernel kern;
+  int threads;
+};
+
+// Candidate tiles: (waves M x N, wave tile WM x WN).  Each compiles
+// without register spills (128 x 256 keeps its accumulators in AGPRs and
+// runs one workgroup per CU).
+const TileConfig kConfigs[] = {
+    {128, 128, prefill::gemm<2, 2, 64, 64>, 256},
+    {128, 256, prefill::gemm<2, 2, 64, 128>, 256},
+};
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// The tile whose whole number of rounds over the CUs wastes the least work
+// (cost = rounds x tile area); ties go to the earlier entry.
+const TileConfig& pick_tile(int64_t m, int64_t n) {
+  const int cu = device_cu_count();
+  const TileConfig* best = &kConfigs[0];
+  int64_t best_cost = -1;
+  for (const TileConfig& c : kConfigs) {
+    const int64_t tiles = cdiv(m, c.bm) * cdiv(n, c.bn);
+    const int64_t cost = cdiv(tiles, cu) * c.bm * c.bn;
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best = &c;
+    }
+  }
+  return *best;
+}
+
+}  // namespace
 
 hipError_t launch_linear_prefill_main(const LinearPlan& p, const uint8_t* codes,
                                       const uint8_t* scales, const float* gscale,
                                       const uint16_t* lora_b, uint16_t* y, char* ws,
                                       hipStream_t stream) {
-  return run_decode_chunks(p, codes, scales, gscale, lora_b, y, ws, stream);
+  if (p.m <= 64) return run_decode_chunks(p, codes, scales, gscale, lora_b, y, ws, stream);
+  const TileConfig& tc = pick_tile(p.m, p.n);
+  prefill::Args a;
+  a.xt = reinterpret_cast<const uint16_t*>(ws + p.off_xt);
+  a.codes = codes;
+  a.scales = scales;
+  a.gscale = gscale;
+  a.r = (lora_b && p.r > 0) ? p.r : 0;
+  a.t = a.r ? reinterpret_cast<const uint16_t*>(ws + p.off_t) : nullptr;
+  a.lora_b = lora_b;
+  a.y = y;
+  a.m = p.m;
+  a.mpad = p.mpad;
+  a.n = p.n;
+  a.k = p.k;
+  a.rpad16 = p.rpad16;
+  a.lora_vec = (a.r % 8 == 0) && ((reinterpret_cast<uintptr_t>(lora_b) & 15) == 0);
+  a.tiles_n = (int)cdiv(p.n, tc.bn);
+  const int64_t tiles = cdiv(p.m, tc.bm) * a.tiles_n;
+  hipLaunchKernelGGL(tc.kern, dim3((unsigned)tiles), dim3(tc.threads), 0, stream, a);
+  return hipGetLastError();
 }
 
 }  // namespace qerl

@@ -81,6 +81,9 @@ def test_tiny_layer_full():
     (64, 96, 8192, 32, 1),    # few rows, long K: split-K across workgroups
     (128, 640, 5120, 64, 1),  # m = 128 (4 m tiles)
     (200, 300, 320, 16, 4),   # prefill-ish ragged
+    (150, 200, 272, 12, 2),   # prefill GEMM: partial last K step, r % 8 != 0
+    (257, 130, 1040, 40, 3),  # prefill GEMM: ragged M tile, ragged N tile
+    (96, 384, 2048, 0, 1),    # prefill GEMM without LoRA
 ])
 def test_shapes(m, n, k, r, stage):
     L = make_layer(m, n, k, r, seed=m * 7 + n, stage=stage, outlier_frac=1e-3)
