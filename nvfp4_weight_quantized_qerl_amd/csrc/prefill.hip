@@ -21,8 +21,12 @@ struct TileConfig {
 // without register spills (128 x 256 keeps its accumulators in AGPRs and
 // runs one workgroup per CU).
 const TileConfig kConfigs[] = {
-    {128, 128, prefill::gemm<2, 2, 64, 64>, 256},
-    {128, 256, prefill::gemm<2, 2, 64, 128>, 256},
+    {256, 256, prefill::gemm<2, 4, 128, 64, 2>, 512},
+    {256, 256, prefill::gemm<2, 2, 128, 128, 1>, 256},
+    {256, 192, prefill::gemm<2, 2, 128, 96, 1>, 256},
+    {128, 256, prefill::gemm<2, 2, 64, 128, 1>, 256},
+    {128, 192, prefill::gemm<2, 2, 64, 96, 1>, 256},
+    {128, 128, prefill::gemm<2, 2, 64, 64, 2>, 256},
 };
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }

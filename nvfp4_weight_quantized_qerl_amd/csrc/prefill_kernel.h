@@ -100,15 +100,12 @@ __device__ __forceinline__ uint4 lora_b8(const Args& a, int64_t row, int j0) {
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-// Workgroups per CU that the LDS tiles allow (two double-buffered tiles of
-// (BM + BN) x 128 B per workgroup, 160 KB per CU).
-constexpr int wgs_per_cu(int bm, int bn) { return (bm + bn) * 256 <= 81920 ? 2 : 1; }
-
-// The second launch bound is the number of waves per SIMD to plan
-// registers for: (waves per workgroup / 4) x workgroups per CU.
-template <int WGM, int WGN, int WM, int WN>
-__global__ __launch_bounds__(64 * WGM * WGN,
-                             (WGM * WGN / 4) * wgs_per_cu(WGM * WM, WGN * WN))
+// WPE is the number of waves per SIMD the registers are planned for (the
+// second launch bound): 1 gives a wave up to 512 registers (accumulators
+// in AGPRs), 2 lets two workgroups of four waves share a CU when their LDS
+// tiles fit (two double-buffered tiles of (BM + BN) x 128 B each).
+template <int WGM, int WGN, int WM, int WN, int WPE>
+__global__ __launch_bounds__(64 * WGM * WGN, WPE)
 void gemm(Args a) {
   constexpr int WAVES = WGM * WGN;
   constexpr int THREADS = 64 * WAVES;
@@ -120,8 +117,8 @@ void gemm(Args a) {
   constexpr int B_ITEMS = 2 * BN;                  // (row, 32-wide half) per step
   constexpr int B_PER_THREAD = (B_ITEMS + THREADS - 1) / THREADS;
 
-  __shared__ __attribute__((aligned(16))) uint4 as0[BM * 8], as1[BM * 8];
-  __shared__ __attribute__((aligned(16))) uint4 bs0[BN * 8], bs1[BN * 8];
+  __shared__ __attribute__((aligned(16))) uint4 as[2][BM * 8];
+  __shared__ __attribute__((aligned(16))) uint4 bs[2][BN * 8];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -243,69 +240,56 @@ void gemm(Args a) {
   };
 
   // Prologue: step 0 into buffer 0.
-  copy_a(0, as0);
+  copy_a(0, as[0]);
   load_b(0);
   __builtin_amdgcn_s_waitcnt(0x0f70);             // vmcnt(0): B(0) in registers
-  store_b(0, bs0);
+  store_b(0, bs[0]);
   __syncthreads();
 
-  for (int step = 0; step < nsteps; step += 2) {
-#define QERL_PF_STEP(S, ACUR, BCUR, ANXT, BNXT)                          \
-  {                                                                     \
-    const bool more = (S) + 1 < nsteps;                                 \
-    if (more) {                                                         \
-      copy_a((S) + 1, ANXT);                                            \
-      load_b((S) + 1);                                                  \
-    }                                                                   \
-    compute(ACUR, BCUR);                                                \
-    if (more) {                                                         \
-      __builtin_amdgcn_s_waitcnt(0x0f70);                               \
-      store_b((S) + 1, BNXT);                                           \
-    }                                                                   \
-    __syncthreads();                                                    \
-  }
-    QERL_PF_STEP(step, as0, bs0, as1, bs1)
-    if (step + 1 >= nsteps) break;
-    QERL_PF_STEP(step + 1, as1, bs1, as0, bs0)
-#undef QERL_PF_STEP
+  // One K step per iteration; the buffer index alternates at run time so
+  // that the accumulators stay in the same registers across iterations.
+  for (int step = 0; step < nsteps; ++step) {
+    const int cur = step & 1;
+    const bool more = step + 1 < nsteps;
+    if (more) {
+      copy_a(step + 1, as[cur ^ 1]);
+      load_b(step + 1);
+    }
+    compute(as[cur], bs[cur]);
+    if (more) {
+      __builtin_amdgcn_s_waitcnt(0x0f70);           // vmcnt(0): A and B of step + 1
+      store_b(step + 1, bs[cur ^ 1]);
+    }
+    __syncthreads();
   }
 
-  // Epilogue: S * acc + t B^T (bf16 MFMA over r), round to bf16, store.
+  // Epilogue, one 32 x 32 block at a time (so that only one block's
+  // accumulators leave the AGPRs at once): S * acc + t B^T (bf16 MFMA over
+  // r), round to bf16, store.
   const float S = *a.gscale;
 #pragma unroll
-  for (int u = 0; u < MT; ++u)
+  for (int u = 0; u < MT; ++u) {
+    const int64_t trow = m0 + wm * WM + 32 * u + c;
 #pragma unroll
-    for (int t = 0; t < NW; ++t)
+    for (int t = 0; t < NW; ++t) {
+      const int64_t col = n0 + wn * WN + 32 * t + c;
+      f32x16_t o = acc[u][t];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[u][t][v] *= S;
-  if (a.r > 0) {
-    for (int j0 = 0; j0 < a.rpad16; j0 += 16) {
-      uint4 tf[MT], lb[NW];
-#pragma unroll
-      for (int u = 0; u < MT; ++u) {
-        const int64_t row = m0 + wm * WM + 32 * u + c;
-        tf[u] = row < a.mpad ? *reinterpret_cast<const uint4*>(a.t + row * a.rpad16 + j0 + 8 * h)
+      for (int v = 0; v < 16; ++v) o[v] *= S;
+      for (int j0 = 0; j0 < a.r; j0 += 16) {
+        const uint4 tf = trow < a.mpad
+                             ? *reinterpret_cast<const uint4*>(a.t + trow * a.rpad16 + j0 + 8 * h)
                              : make_uint4(0u, 0u, 0u, 0u);
+        o = mfma_bf16(tf, lora_b8(a, col, j0 + 8 * h), o);
       }
+      if (col < a.n) {
 #pragma unroll
-      for (int t = 0; t < NW; ++t) lb[t] = lora_b8(a, n0 + wn * WN + 32 * t + c, j0 + 8 * h);
-#pragma unroll
-      for (int u = 0; u < MT; ++u)
-#pragma unroll
-        for (int t = 0; t < NW; ++t) acc[u][t] = mfma_bf16(tf[u], lb[t], acc[u][t]);
+        for (int v = 0; v < 16; ++v) {
+          const int64_t row = m0 + wm * WM + 32 * u + acc_row(v, lane);
+          if (row < a.m) a.y[row * a.n + col] = f32_to_bf16_bits(o[v]);
+        }
+      }
     }
-  }
-#pragma unroll
-  for (int t = 0; t < NW; ++t) {
-    const int64_t col = n0 + wn * WN + 32 * t + c;
-    if (col >= a.n) continue;
-#pragma unroll
-    for (int u = 0; u < MT; ++u)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t row = m0 + wm * WM + 32 * u + acc_row(v, lane);
-        if (row < a.m) a.y[row * a.n + col] = f32_to_bf16_bits(acc[u][t][v]);
-      }
   }
 }
 
