@@ -19,11 +19,12 @@
 // the row index (chunk c of row r at c ^ (r mod 8)), so the MFMA operand
 // reads (lane = row) hit eight different bank groups per eight lanes.
 //
-// Pipeline (double-buffered LDS).  Iteration i: issue the copies of
-// A(i+1) and the code/scale loads of B(i+1); run the MFMAs of step i from
-// LDS; wait for the loads; dequantize B(i+1) into the other buffer; one
-// barrier.  The barrier also makes A(i+1) visible (every wave waited for
-// its own copies first).
+// Pipeline (double-buffered LDS, weight registers two steps ahead).
+// Iteration i: issue the copies of A(i+1) and the code/scale loads of
+// B(i+2); run the MFMAs of step i from LDS while dequantizing B(i+1) (loaded
+// during step i-1) into the other buffer, a quarter beside each 16-deep
+// MFMA step; wait for A(i+1); one barrier.  The barrier also makes A(i+1)
+// visible (every wave waited for its own copies first).
 //
 // Each wave accumulates a WM x WN tile in MT x NW blocks of 32 x 32
 // (v_mfma_f32_32x32x16_bf16); the epilogue scales by S, adds the LoRA-up
@@ -117,8 +118,11 @@ void gemm(Args a) {
   constexpr int B_ITEMS = 2 * BN;                  // (row, 32-wide half) per step
   constexpr int B_PER_THREAD = (B_ITEMS + THREADS - 1) / THREADS;
 
-  __shared__ __attribute__((aligned(16))) uint4 as[2][BM * 8];
-  __shared__ __attribute__((aligned(16))) uint4 bs[2][BN * 8];
+  // Separate arrays per buffer: the compiler tracks direct-to-LDS copies
+  // per array, and would otherwise wait for every load in flight before
+  // reading the buffer that is not being filled.
+  __shared__ __attribute__((aligned(16))) uint4 as0[BM * 8], as1[BM * 8];
+  __shared__ __attribute__((aligned(16))) uint4 bs0[BN * 8], bs1[BN * 8];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -158,44 +162,49 @@ void gemm(Args a) {
       dma16(ra, dst + cp * 64, avoff + 8u * cp * xrow, so);
     }
   };
-  uint4 bcode[B_PER_THREAD];
-  uint32_t bscale[B_PER_THREAD];
-  // A buffer load that crosses the end of its range reads zeros in full,
-  // so every load here covers one 16-wide group (8 B of codes, 1 scale):
-  // with k % 16 == 0 each is either wholly inside the tensor or wholly
-  // past its end (the last row's partial last step).
+  // B registers: bn receives the loads of step s + 2 while bc (step s + 1)
+  // is dequantized during the MFMAs of step s.
+  // (The two scale bytes stay in separate registers, so that each load
+  // result lives until it is used and nothing has to wait for it early.)
+  uint4 bn_code[B_PER_THREAD], bc_code[B_PER_THREAD];
+  uint32_t bn_s0[B_PER_THREAD], bn_s1[B_PER_THREAD], bc_s0[B_PER_THREAD], bc_s1[B_PER_THREAD];
+  // Every thread issues the same number of loads (items past the tile
+  // repeat the last item and are not stored), so the vmcnt waits below are
+  // exact.  A buffer load that crosses the end of its range reads zeros in
+  // full, so every load covers one 16-wide group (8 B of codes, 1 scale):
+  // with k % 16 == 0 each is either wholly inside the tensor or wholly past
+  // its end (the last row's partial last step).
+  constexpr int B_LOADS = 4 * B_PER_THREAD;        // vector loads per thread per step
   auto load_b = [&](int step) __attribute__((always_inline)) {
     const uint32_t so_c = koff(step, 32u), so_s = koff(step, 4u);
 #pragma unroll
     for (int i = 0; i < B_PER_THREAD; ++i) {
-      const int item = tid + i * THREADS;
+      const int item = min(tid + i * THREADS, B_ITEMS - 1);
       const int row = item >> 1, half = item & 1;
-      if (item < B_ITEMS) {
-        const uint32_t vc = (uint32_t)row * kbytes + 16u * half;
-        const uint32_t vs = (uint32_t)row * kscales + 2u * half;
-        const uint2 c0 = bload64(rw, vc, so_c), c1 = bload64(rw, vc + 8u, so_c);
-        bcode[i] = make_uint4(c0.x, c0.y, c1.x, c1.y);
-        bscale[i] = bload8(rs, vs, so_s) | (bload8(rs, vs + 1u, so_s) << 8);
-      }
+      const uint32_t vc = (uint32_t)row * kbytes + 16u * half;
+      const uint32_t vs = (uint32_t)row * kscales + 2u * half;
+      const uint2 c0 = bload64(rw, vc, so_c), c1 = bload64(rw, vc + 8u, so_c);
+      bn_code[i] = make_uint4(c0.x, c0.y, c1.x, c1.y);
+      bn_s0[i] = bload8(rs, vs, so_s);
+      bn_s1[i] = bload8(rs, vs + 1u, so_s);
     }
   };
-  // Scales of 16-wide groups at or past k are zeroed (their codes may be
-  // the next row's), so a partial last step contributes nothing there.
-  auto store_b = [&](int step, uint4* dst) __attribute__((always_inline)) {
+  // Dequantize chunk q (8 codes = one 16-byte LDS chunk) of every item of
+  // bc (step `step`) into dst.  Scales of 16-wide groups at or past k are
+  // zeroed (their codes may be the next row's), so a partial last step
+  // contributes nothing there.
+  auto store_b_chunk = [&](int step, uint4* dst, int q) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < B_PER_THREAD; ++i) {
       const int item = tid + i * THREADS;
-      const int row = item >> 1, half = item & 1;
-      if (item < B_ITEMS) {
-        const int64_t g0 = step * 4 + 2 * half;          // first 16-wide group
-        const float s0 = 16 * g0 < a.k ? e4m3_to_f32(bscale[i] & 0xffu) : 0.0f;
-        const float s1 = 16 * (g0 + 1) < a.k ? e4m3_to_f32((bscale[i] >> 8) & 0xffu) : 0.0f;
-        const int sw = row & 7;
-        uint4* drow = dst + row * 8;
-        drow[(4 * half + 0) ^ sw] = dequant8_bf16(bcode[i].x, s0);
-        drow[(4 * half + 1) ^ sw] = dequant8_bf16(bcode[i].y, s0);
-        drow[(4 * half + 2) ^ sw] = dequant8_bf16(bcode[i].z, s1);
-        drow[(4 * half + 3) ^ sw] = dequant8_bf16(bcode[i].w, s1);
+      if (B_ITEMS % THREADS == 0 || item < B_ITEMS) {
+        const int row = item >> 1, half = item & 1;
+        const int g = step * 4 + 2 * half + (q >> 1);     // 16-wide group
+        const uint32_t sbyte = q < 2 ? bc_s0[i] : bc_s1[i];
+        const float sb = 16 * (int64_t)g < a.k ? e4m3_to_f32(sbyte) : 0.0f;
+        const uint32_t cw = q == 0 ? bc_code[i].x
+                            : (q == 1 ? bc_code[i].y : (q == 2 ? bc_code[i].z : bc_code[i].w));
+        dst[row * 8 + ((4 * half + q) ^ (row & 7))] = dequant8_bf16(cw, sb);
       }
     }
   };
@@ -208,7 +217,8 @@ void gemm(Args a) {
 
   // Operand reads run one 16-deep MFMA step ahead of the MFMAs (two sets of
   // fragments live); the scheduling barriers keep the compiler from
-  // hoisting all four steps' reads, which would spill.
+  // hoisting all four steps' reads, which would spill.  Chunk kk of the
+  // next step's weight tile is dequantized beside the MFMAs of step kk.
   auto read_frags = [&](const uint4* as, const uint4* bs, int kk, uint4 (&af)[MT],
                         uint4 (&bf)[NW]) __attribute__((always_inline)) {
     const int ch = 2 * kk + h;
@@ -223,7 +233,8 @@ void gemm(Args a) {
       bf[t] = bs[r * 8 + (ch ^ (r & 7))];
     }
   };
-  auto compute = [&](const uint4* as, const uint4* bs) __attribute__((always_inline)) {
+  auto compute = [&](const uint4* as, const uint4* bs, int next_step,
+                     uint4* bs_next) __attribute__((always_inline)) {
     uint4 af[2][MT], bf[2][NW];
     read_frags(as, bs, 0, af[0], bf[0]);
 #pragma unroll
@@ -235,33 +246,63 @@ void gemm(Args a) {
 #pragma unroll
         for (int t = 0; t < NW; ++t)
           acc[u][t] = mfma_bf16(af[kk & 1][u], bf[kk & 1][t], acc[u][t]);
+      store_b_chunk(next_step, bs_next, kk);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  // Prologue: step 0 into buffer 0.
-  copy_a(0, as[0]);
+  // Prologue: step 0 into buffer 0, the loads of step 1 in flight.
+  copy_a(0, as0);
   load_b(0);
-  __builtin_amdgcn_s_waitcnt(0x0f70);             // vmcnt(0): B(0) in registers
-  store_b(0, bs[0]);
+  __builtin_amdgcn_s_waitcnt(0x0f70);             // vmcnt(0)
+#pragma unroll
+  for (int i = 0; i < B_PER_THREAD; ++i) {
+    bc_code[i] = bn_code[i];
+    bc_s0[i] = bn_s0[i];
+    bc_s1[i] = bn_s1[i];
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) store_b_chunk(0, bs0, q);
+  if (nsteps > 1) load_b(1);
   __syncthreads();
 
-  // One K step per iteration; the buffer index alternates at run time so
-  // that the accumulators stay in the same registers across iterations.
-  for (int step = 0; step < nsteps; ++step) {
-    const int cur = step & 1;
-    const bool more = step + 1 < nsteps;
-    if (more) {
-      copy_a(step + 1, as[cur ^ 1]);
-      load_b(step + 1);
-    }
-    compute(as[cur], bs[cur]);
-    if (more) {
-      __builtin_amdgcn_s_waitcnt(0x0f70);           // vmcnt(0): A and B of step + 1
-      store_b(step + 1, bs[cur ^ 1]);
-    }
-    __syncthreads();
+  // Step S: wait for B(S+1) (loaded one step ago), move it to bc, issue
+  // A(S+1) and B(S+2), run the MFMAs of S while dequantizing B(S+1) into the
+  // other buffer, wait for A(S+1) (B(S+2) may stay in flight), barrier.  On
+  // the last step the dequantized tile is stale and never read.  Buffers
+  // are named at compile time (two steps per loop iteration, the odd first
+  // step peeled) and no iteration leaves early, so the accumulators keep
+  // their registers.
+#define QERL_PF_STEP(S, ACUR, BCUR, ANXT, BNXT)                                  \
+  {                                                                             \
+    __builtin_amdgcn_s_waitcnt(0x0f70);                                         \
+    _Pragma("unroll") for (int i = 0; i < B_PER_THREAD; ++i) {                  \
+      bc_code[i] = bn_code[i];                                                  \
+      bc_s0[i] = bn_s0[i];                                                      \
+      bc_s1[i] = bn_s1[i];                                                      \
+    }                                                                           \
+    if ((S) + 1 < nsteps) copy_a((S) + 1, ANXT);                                \
+    if ((S) + 2 < nsteps) load_b((S) + 2);                                      \
+    compute(ACUR, BCUR, (S) + 1, BNXT);                                         \
+    if ((S) + 2 < nsteps)                                                       \
+      __builtin_amdgcn_s_waitcnt((B_LOADS & 15) | ((B_LOADS >> 4) << 14) | 0x0f70); \
+    else                                                                        \
+      __builtin_amdgcn_s_waitcnt(0x0f70);                                       \
+    __syncthreads();                                                            \
   }
+  if (nsteps & 1) {
+    QERL_PF_STEP(0, as0, bs0, as1, bs1)
+    for (int step = 1; step < nsteps; step += 2) {
+      QERL_PF_STEP(step, as1, bs1, as0, bs0)
+      QERL_PF_STEP(step + 1, as0, bs0, as1, bs1)
+    }
+  } else {
+    for (int step = 0; step < nsteps; step += 2) {
+      QERL_PF_STEP(step, as0, bs0, as1, bs1)
+      QERL_PF_STEP(step + 1, as1, bs1, as0, bs0)
+    }
+  }
+#undef QERL_PF_STEP
 
   // Epilogue, one 32 x 32 block at a time (so that only one block's
   // accumulators leave the AGPRs at once): S * acc + t B^T (bf16 MFMA over
