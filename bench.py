@@ -50,6 +50,7 @@ def parse():
 
 
 COPY_BYTES = 512 << 20         # calibration copy of the profiling pass
+PROFILE_LAUNCHES = 50          # gate/up contractions in the profiling pass
 
 
 def linear_bytes(m, n, k, r):
@@ -95,7 +96,7 @@ def measured_traffic(kernel_key, digest):
     return rec.get("hbm_bytes_per_launch")
 
 
-def oracle_step_rate(cfg, layers, M, R, min_seconds=10.0, max_reps=4):
+def oracle_step_rate(cfg, layers, M, R, min_seconds=10.0, max_reps=20):
     """The oracle running the decode step on the host: per layer, sample z,
     dequantize the NVFP4 weight and evaluate the fp64 linear layer with the
     LoRA branch.  As on the GPU, the weights are quantized (by the oracle)
@@ -200,11 +201,11 @@ def main():
         ly = layers[0]
         q.qerl_aqn_sample(ly["L"].seed, 0, 0, sigma, ly["k"], out=ly["z"])
         q.qerl_linear_prepare(ly["x"], ly["n"], ly["a"], cfg.lora_scale, ly["z"], ly["ws"])
-        for i in range(10):
+        for i in range(PROFILE_LAUNCHES):
             c, s = ly["rot"][i % copies]
             q.qerl_linear_decode_prepared(M, c, s, ly["S"], ly["k"], ly["b"], ly["y"], ly["ws"])
         torch.cuda.synchronize()
-        print(f"profile pass done: copy {COPY_BYTES} B, 10 gate/up contractions "
+        print(f"profile pass done: copy {COPY_BYTES} B, {PROFILE_LAUNCHES} gate/up contractions "
               f"({main_kernel_bytes(M, ly['n'], ly['k'], R):.0f} algorithmic B each)")
         return
 
@@ -251,12 +252,13 @@ def main():
                 "traffic": traffic, "kernel": "decode_main (gate/up 37888x3584, M=64, r=32)",
                 "avg_launch_us": round(kern_s * 1e6, 2), "bytes_per_launch": kbytes}
 
-    # ---- prefill (Qwen2.5-7B qkv and down, 4096 tokens): TFLOP/s
+    # ---- prefill (Qwen2.5-7B qkv and down, 4096 tokens): TFLOP/s, for the
+    # whole call (prepare + GEMM) and for the GEMM kernel alone
     prefill = None
     if not args.no_prefill:
         pc = CONFIGS["prefill_7b"]
         psig = q.qerl_aqn_sigma(pc.sigma_start, pc.sigma_end, pc.num_stages, pc.stage)
-        ptimes, pflops = [], 0.0
+        per_layer, t_full, t_main, pflops = [], 0.0, 0.0, 0.0
         for i, s in enumerate(pc.layers):
             L = make_layer(pc.m, s.n, s.k, pc.r, seed=11 + i, stage=pc.stage, call_id=i)
             x, w, a, b = to_dev(L.x), to_dev(L.w), to_dev(L.a), to_dev(L.b)
@@ -265,24 +267,40 @@ def main():
             z = q.qerl_aqn_sample(L.seed, 0, i, psig, s.k, device=dev)
             ws = q.workspace(pc.m, s.n, s.k, pc.r, dev)
             y = torch.empty((pc.m, s.n), dtype=torch.bfloat16, device=dev)
-            for _ in range(2):
-                q.qerl_linear_prefill(x, codes, scales, S, a, b, pc.lora_scale, z,
-                                      workspace=ws, y=y)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            preps = 5
-            e0.record(stream)
-            for _ in range(preps):
-                q.qerl_linear_prefill(x, codes, scales, S, a, b, pc.lora_scale, z,
-                                      workspace=ws, y=y)
-            e1.record(stream)
-            e1.synchronize()
-            ptimes.append(e0.elapsed_time(e1) / 1e3 / preps)
-            pflops += linear_flops(pc.m, s.n, s.k, pc.r)
+
+            def timed(fn, reps=5):
+                for _ in range(2):
+                    fn()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(reps):
+                    fn()
+                e1.record(stream)
+                e1.synchronize()
+                return e0.elapsed_time(e1) / 1e3 / reps
+
+            tf = timed(lambda: q.qerl_linear_prefill(x, codes, scales, S, a, b, pc.lora_scale,
+                                                      z, workspace=ws, y=y))
+            q.qerl_linear_prepare(x, s.n, a, pc.lora_scale, z, ws)
+            tm = timed(lambda: q.qerl_linear_prefill_prepared(pc.m, codes, scales, S, s.k, b,
+                                                               y, ws))
+            fl = linear_flops(pc.m, s.n, s.k, pc.r)
+            per_layer.append({"layer": f"{s.name} {s.n}x{s.k}",
+                              "tflops": round(fl / tf / 1e12, 1),
+                              "gemm_tflops": round(fl / tm / 1e12, 1),
+                              "ms": round(1e3 * tf, 3), "gemm_ms": round(1e3 * tm, 3)})
+            t_full += tf
+            t_main += tm
+            pflops += fl
             del x, a, b, codes, scales, ws, y
-        ptf = pflops / sum(ptimes) / 1e12
         prefill = {"workload": "prefill_7b (qkv 4608x3584 + down 3584x18944, M=4096, r=32)",
-                   "tflops": round(ptf, 1), "ms": round(1e3 * sum(ptimes), 3),
-                   "frac_bf16_peak": round(ptf / BF16_PEAK_TFLOPS, 4)}
+                   "tflops": round(pflops / t_full / 1e12, 1),
+                   "gemm_tflops": round(pflops / t_main / 1e12, 1),
+                   "ms": round(1e3 * t_full, 3),
+                   "frac_bf16_peak": round(pflops / t_full / 1e12 / BF16_PEAK_TFLOPS, 4),
+                   "gemm_frac_bf16_peak": round(pflops / t_main / 1e12 / BF16_PEAK_TFLOPS, 4),
+                   "layers": per_layer}
 
     # ---- oracle on the host cores: the same step, weights quantized beforehand
     cpu = None
