@@ -14,8 +14,10 @@
 // and, with a LoRA branch, the LoRA-down t:
 //   prep_kernel (four waves per 32 rows x 512-wide K chunk): x_t and
 //           tpart = x_t A^T over the chunk (bf16 MFMA, fp32);
-//   treduce: t = bf16(s * sum over chunks of tpart), summed in chunk order
-//           so the result is deterministic.
+//   treduce: t = bf16(sum over chunks of tpart), summed in a fixed order
+//           so the result is deterministic.  When every decode chunk of the
+//           shape splits K, the split-K finishing kernel sums tpart for its
+//           own rows instead, and treduce is not launched.
 // Without a LoRA branch a single elementwise kernel (xt_kernel) writes x_t.
 #include <algorithm>
 
@@ -136,6 +138,7 @@ struct PrepArgs {
   float* __restrict__ tpart;
   int64_t m, mpad, k;
   int r, rpad32;
+  float lora_scale;
 };
 
 // x_t = bf16(x (1 + z)) of 8 consecutive channels from their noise z0, z1.
@@ -215,7 +218,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs p) {
     float* dst = p.tpart + ((int64_t)blockIdx.y * p.mpad + (int64_t)blockIdx.x * 32) * p.rpad32
                  + 32 * t + c;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) dst[(int64_t)acc_row(v, lane) * p.rpad32] = acc[t][v];
+    for (int v = 0; v < 16; ++v) dst[(int64_t)acc_row(v, lane) * p.rpad32] = p.lora_scale * acc[t][v];
   }
 }
 
@@ -236,14 +239,13 @@ __global__ __launch_bounds__(256) void xt_kernel(PrepArgs p) {
   *reinterpret_cast<uint4*>(p.xt + mrow * p.k + k0) = xv;
 }
 
-// t = bf16(s * sum over chunks of tpart): one thread per (row, j); the
-// chunks are summed in a fixed order (four interleaved partial sums, then
-// combined), so the result is deterministic.
+// t = bf16(sum over chunks of tpart) (the partials carry s already): one
+// thread per (row, j); the chunks are summed in a fixed order (four
+// interleaved partial sums, then combined), so the result is deterministic.
 __global__ __launch_bounds__(256) void treduce_kernel(const float* __restrict__ tpart,
                                                       uint16_t* __restrict__ t,
                                                       int64_t mpad, int rpad32,
-                                                      int rpad16, int kchunks,
-                                                      float s) {
+                                                      int rpad16, int kchunks) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= mpad * rpad16) return;
   const int64_t mrow = i / rpad16;
@@ -257,10 +259,35 @@ __global__ __launch_bounds__(256) void treduce_kernel(const float* __restrict__ 
     for (int u = 0; u < 4; ++u) acc[u] += src[(c + u) * stride];
   }
   for (; c < kchunks; ++c) acc[c & 3] += src[c * stride];
-  t[i] = f32_to_bf16_bits(s * ((acc[0] + acc[1]) + (acc[2] + acc[3])));
+  t[i] = f32_to_bf16_bits((acc[0] + acc[1]) + (acc[2] + acc[3]));
 }
 
 }  // namespace
+
+bool decode_splits_every_chunk(const LinearPlan& p) {
+  if (p.dec_split <= 1) return false;
+  // The LDS-staged kernel re-derives its split from 256-wide blocks.
+  const int64_t nb = p.k / 256;
+  const bool lds = p.k % 256 == 0 && p.dec_nt <= 5;
+  if (lds && nb > 0) {
+    const int64_t per = cdiv(nb, p.dec_split);
+    if (cdiv(nb, per) <= 1) return false;
+  }
+  return true;
+}
+
+bool prepare_reduces_t(const LinearPlan& p) {
+  return p.r > 0 && !(p.m <= 64 && decode_splits_every_chunk(p));
+}
+
+hipError_t launch_treduce(const LinearPlan& p, char* ws, hipStream_t stream) {
+  const int64_t total = p.mpad * p.rpad16;
+  hipLaunchKernelGGL(treduce_kernel, dim3((unsigned)cdiv(total, 256)), dim3(256), 0, stream,
+                     reinterpret_cast<const float*>(ws + p.off_tpart),
+                     reinterpret_cast<uint16_t*>(ws + p.off_t), p.mpad, p.rpad32, p.rpad16,
+                     p.kchunks);
+  return hipGetLastError();
+}
 
 hipError_t launch_linear_prepare(const LinearPlan& p, const uint16_t* x,
                                  const float* z, const uint16_t* lora_a,
@@ -277,6 +304,7 @@ hipError_t launch_linear_prepare(const LinearPlan& p, const uint16_t* x,
   a.k = p.k;
   a.r = p.r;
   a.rpad32 = p.rpad32;
+  a.lora_scale = lora_scale;
   if (p.r == 0 || !lora_a) {
     const int64_t threads = p.mpad * p.k / 8;
     hipLaunchKernelGGL(xt_kernel, dim3((unsigned)cdiv(threads, 256)), dim3(256), 0, stream, a);
@@ -291,13 +319,8 @@ hipError_t launch_linear_prepare(const LinearPlan& p, const uint16_t* x,
     default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int64_t total = p.mpad * p.rpad16;
-  hipLaunchKernelGGL(treduce_kernel, dim3((unsigned)cdiv(total, 256)), dim3(256), 0,
-                     stream, (const float*)a.tpart,
-                     reinterpret_cast<uint16_t*>(ws + p.off_t), p.mpad, p.rpad32,
-                     p.rpad16, p.kchunks, lora_scale);
-  return hipGetLastError();
+  if (e != hipSuccess || !prepare_reduces_t(p)) return e;
+  return launch_treduce(p, ws, stream);
 }
 
 }  // namespace qerl

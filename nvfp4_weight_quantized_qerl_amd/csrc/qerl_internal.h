@@ -52,6 +52,15 @@ hipError_t launch_linear_prepare(const LinearPlan& p, const uint16_t* x,
                                  float lora_scale, char* ws,
                                  hipStream_t stream);
 
+// LoRA-down reduction: launch_linear_prepare writes the chunk partials
+// s x_t A^T (tpart) and, when prepare_reduces_t(p), also t = bf16(sum of
+// the partials).  Otherwise (every decode chunk splits K) the split-K
+// finishing kernel reduces tpart itself, and any other consumer of t calls
+// launch_treduce first.
+bool decode_splits_every_chunk(const LinearPlan& p);
+bool prepare_reduces_t(const LinearPlan& p);
+hipError_t launch_treduce(const LinearPlan& p, char* ws, hipStream_t stream);
+
 // The contraction kernels read x_t and the LoRA-down t = bf16(s x_t A^T)
 // that launch_linear_prepare left in the workspace.
 hipError_t launch_linear_decode_main(const LinearPlan& p, const uint8_t* codes,

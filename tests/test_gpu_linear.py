@@ -84,6 +84,9 @@ def test_tiny_layer_full():
     (150, 200, 272, 12, 2),   # prefill GEMM: partial last K step, r % 8 != 0
     (257, 130, 1040, 40, 3),  # prefill GEMM: ragged M tile, ragged N tile
     (96, 384, 2048, 0, 1),    # prefill GEMM without LoRA
+    (40, 200, 4096, 12, 2),   # split-K finish: LoRA-down partials reduced there, r % 8 != 0
+    (64, 130, 6144, 72, 1),   # split-K finish, r > 64 (B row read in the loop)
+    (17, 64, 1040, 24, 3),    # split-K in the general kernel (k % 256 != 0)
 ])
 def test_shapes(m, n, k, r, stage):
     L = make_layer(m, n, k, r, seed=m * 7 + n, stage=stage, outlier_frac=1e-3)
