@@ -11,9 +11,11 @@
 //   scales  64 rows x 16 B per instruction
 //   x_t     2 rows x 512 B per instruction
 // so every load instruction touches few cache lines.  Inside a row the
-// 16-byte chunks are stored XOR-swizzled by the row index (chunk q of row r
-// at position q ^ (r mod 8)); the MFMA-layout reads (lane = row) then hit
-// eight different bank groups in every group of eight lanes.
+// 16-byte chunks are stored XOR-swizzled by the row index: chunk q of code
+// row r (128 B) at q ^ ((r / 2) mod 8), chunk q of x_t row r (512 B) at
+// q ^ (r mod 16).  The LDS has 64 banks of 4 bytes and serves 16-byte
+// accesses 16 lanes per clock; with these keys the MFMA-layout reads
+// (lane = row) of 16 consecutive rows hit 16 different bank groups.
 //
 // Pipeline.  Codes and scales are triple-buffered, x_t double-buffered.
 // Iteration i: the four copying waves wait for their copies of block i
@@ -165,13 +167,17 @@ __global__ __launch_bounds__(512, 1) void decode_lds(Args a) {
 
   // Copies are issued by waves 0..3 (see the file comment for the layout).
   // codes copy j of wave q covers rows 8 (q + 4 j) .. +7
+  // (swizzle key of row r: (r / 2) mod 8 = (4 q + cr / 2) mod 8 for these rows)
   const uint32_t cr = (uint32_t)(lane >> 3);
-  const uint32_t vcode = (8u * q + cr) * kbytes + 16u * ((uint32_t)(lane & 7) ^ cr);
+  const uint32_t vcode = (8u * q + cr) * kbytes +
+                         16u * ((uint32_t)(lane & 7) ^ ((4u * (uint32_t)q + (cr >> 1)) & 7u));
   // scales copy of wave q covers rows 64 q .. +63
   const uint32_t vscale = (64u * q + lane) * kscales;
   // x_t copy j of wave q covers rows 2 (q + 4 j) and 2 (q + 4 j) + 1
+  // (swizzle key of row r: r mod 16 = (xr + 8 (j mod 2)) mod 16)
   const uint32_t xr = 2u * q + (uint32_t)(lane >> 5);
-  const uint32_t vx = xr * xrow + 16u * ((uint32_t)(lane & 31) ^ (xr & 7u));
+  const uint32_t vx_e = xr * xrow + 16u * ((uint32_t)(lane & 31) ^ (xr & 15u));
+  const uint32_t vx_o = xr * xrow + 16u * ((uint32_t)(lane & 31) ^ ((xr + 8u) & 15u));
 
   auto copy_w = [&](int64_t blk, uint4* wc, uint4* sc) {
 #pragma unroll
@@ -184,7 +190,7 @@ __global__ __launch_bounds__(512, 1) void decode_lds(Args a) {
   auto copy_x = [&](int64_t blk, uint4* xs) {
 #pragma unroll
     for (int j = 0; j < XINSTR / 4; ++j)
-      dma16(rx, xs + (q + 4 * j) * 64, vx, 8u * j * xrow + 512u * (uint32_t)blk);
+      dma16(rx, xs + (q + 4 * j) * 64, (j & 1) ? vx_o : vx_e, 8u * j * xrow + 512u * (uint32_t)blk);
   };
 
   f32x16_t acc[NT0][MT];
@@ -204,7 +210,7 @@ __global__ __launch_bounds__(512, 1) void decode_lds(Args a) {
 #pragma unroll
     for (int t = 0; t < NTH; ++t) {
       const int r = 32 * (TB + t) + c;
-      w[t] = wc[r * 8 + ((2 * q + h) ^ (r & 7))];
+      w[t] = wc[r * 8 + ((2 * q + h) ^ ((r >> 1) & 7))];
       const uint32_t sw = reinterpret_cast<const uint16_t*>(sc)[r * 8 + 2 * q + h];
       sb0[t] = e4m3_to_f32(sw & 0xffu);
       sb1[t] = e4m3_to_f32((sw >> 8) & 0xffu);
@@ -214,7 +220,7 @@ __global__ __launch_bounds__(512, 1) void decode_lds(Args a) {
 #pragma unroll
       for (int u = 0; u < MT; ++u) {
         const int r = 32 * u + c;
-        xa[j][u] = xs[r * 32 + ((8 * q + 4 * h + j) ^ (r & 7))];
+        xa[j][u] = xs[r * 32 + ((8 * q + 4 * h + j) ^ (r & 15))];
       }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {

@@ -16,8 +16,11 @@
 //                  bf16 BN x 64 LDS tile (each 32-wide row half by one
 //                  thread: 16 B of codes, two scales, four 16-byte writes).
 // Both LDS tiles store the eight 16-byte chunks of a row XOR-swizzled by
-// the row index (chunk c of row r at c ^ (r mod 8)), so the MFMA operand
-// reads (lane = row) hit eight different bank groups per eight lanes.
+// the row index (chunk c of row r at c ^ ((r / 2) mod 8)).  The LDS has 64
+// banks of 4 bytes and serves a 16-byte-per-lane access 16 lanes per clock;
+// with 128-byte rows, lanes r and r + 1 differ in bank half and the key
+// (r / 2) mod 8 separates the eight rows of each parity, so the MFMA operand
+// reads (lane = row) and the dequantized-tile writes are conflict-free.
 //
 // Pipeline (double-buffered LDS, weight registers two steps ahead).
 // Iteration i: issue the copies of A(i+1) and the code/scale loads of
@@ -140,9 +143,12 @@ void gemm(Args a) {
   const int64_t arows = a.mpad - m0;
   const __amdgpu_buffer_rsrc_t ra =
       rsrc(a.xt + m0 * a.k, (uint64_t)(arows > 0 ? arows : 0) * xrow);
-  // Copy j of this wave: rows 8 (wave * A_PER_WAVE + j) .. +7, lane = (row, chunk).
+  // Copy j of this wave: rows 8 cp .. 8 cp + 7 (cp = wave * A_PER_WAVE + j),
+  // lane = (row, chunk position); the swizzle key ((8 cp + ar) / 2) mod 8
+  // depends on the parity of cp.
   const uint32_t ar = (uint32_t)(lane >> 3);
-  const uint32_t avoff = ar * xrow + 16u * (((uint32_t)lane & 7u) ^ ar);
+  const uint32_t avoff_e = ar * xrow + 16u * (((uint32_t)lane & 7u) ^ ((ar >> 1) & 7u));
+  const uint32_t avoff_o = ar * xrow + 16u * (((uint32_t)lane & 7u) ^ (((ar >> 1) + 4u) & 7u));
 
   // B: rows n0 .. n0+BN-1 of the codes and scales; rows past n read zeros.
   const uint32_t kbytes = (uint32_t)(a.k / 2), kscales = (uint32_t)(a.k / 16);
@@ -159,7 +165,7 @@ void gemm(Args a) {
 #pragma unroll
     for (int j = 0; j < A_PER_WAVE; ++j) {
       const int cp = wave * A_PER_WAVE + j;
-      dma16(ra, dst + cp * 64, avoff + 8u * cp * xrow, so);
+      dma16(ra, dst + cp * 64, ((cp & 1) ? avoff_o : avoff_e) + 8u * cp * xrow, so);
     }
   };
   // B registers: bn receives the loads of step s + 2 while bc (step s + 1)
@@ -204,7 +210,7 @@ void gemm(Args a) {
         const float sb = 16 * (int64_t)g < a.k ? e4m3_to_f32(sbyte) : 0.0f;
         const uint32_t cw = q == 0 ? bc_code[i].x
                             : (q == 1 ? bc_code[i].y : (q == 2 ? bc_code[i].z : bc_code[i].w));
-        dst[row * 8 + ((4 * half + q) ^ (row & 7))] = dequant8_bf16(cw, sb);
+        dst[row * 8 + ((4 * half + q) ^ ((row >> 1) & 7))] = dequant8_bf16(cw, sb);
       }
     }
   };
@@ -225,12 +231,12 @@ void gemm(Args a) {
 #pragma unroll
     for (int u = 0; u < MT; ++u) {
       const int r = wm * WM + 32 * u + c;
-      af[u] = as[r * 8 + (ch ^ (r & 7))];
+      af[u] = as[r * 8 + (ch ^ ((r >> 1) & 7))];
     }
 #pragma unroll
     for (int t = 0; t < NW; ++t) {
       const int r = wn * WN + 32 * t + c;
-      bf[t] = bs[r * 8 + (ch ^ (r & 7))];
+      bf[t] = bs[r * 8 + (ch ^ ((r >> 1) & 7))];
     }
   };
   auto compute = [&](const uint4* as, const uint4* bs, int next_step,
