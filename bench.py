@@ -42,10 +42,12 @@ def parse():
     ap.add_argument("--copies", type=int, default=6)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
-    ap.add_argument("--profile", action="store_true",
-                    help="profiling pass for rocprofv3: one plain device copy of "
-                         "COPY_BYTES (counter calibration) and ten launches of the "
-                         "gate/up decode contraction; no timing, no JSON line")
+    ap.add_argument("--profile", nargs="?", const="decode", choices=("decode", "prefill"),
+                    help="profiling pass for rocprofv3, no timing and no JSON line: "
+                         "'decode' runs one plain device copy of COPY_BYTES (counter "
+                         "calibration) and PROFILE_LAUNCHES gate/up decode contractions; "
+                         "'prefill' runs one prepare and three prefill GEMMs on each of "
+                         "the 7B qkv and down layers at M=4096")
     return ap.parse_args()
 
 
@@ -94,6 +96,27 @@ def measured_traffic(kernel_key, digest):
     if not rec or rec.get("source_digest") != digest:
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def profile_prefill(q, pc, make_layer, to_dev, dev):
+    """Profiling pass of the prefill GEMM: per 7B layer at M=4096, one
+    qerl_linear_prepare and three qerl_linear_prefill_prepared launches."""
+    import torch
+    psig = q.qerl_aqn_sigma(pc.sigma_start, pc.sigma_end, pc.num_stages, pc.stage)
+    for i, s in enumerate(pc.layers):
+        L = make_layer(pc.m, s.n, s.k, pc.r, seed=11 + i, stage=pc.stage, call_id=i)
+        x, w, a, b = to_dev(L.x), to_dev(L.w), to_dev(L.a), to_dev(L.b)
+        codes, scales, S, _ = q.qerl_quantize_nvfp4(w)
+        del w
+        z = q.qerl_aqn_sample(L.seed, 0, i, psig, s.k, device=dev)
+        ws = q.workspace(pc.m, s.n, s.k, pc.r, dev)
+        y = torch.empty((pc.m, s.n), dtype=torch.bfloat16, device=dev)
+        q.qerl_linear_prepare(x, s.n, a, pc.lora_scale, z, ws)
+        for _ in range(3):
+            q.qerl_linear_prefill_prepared(pc.m, codes, scales, S, s.k, b, y, ws)
+        torch.cuda.synchronize()
+        del x, a, b, codes, scales, ws, y
+    print("profile pass done: prefill_7b qkv and down, 3 GEMMs each")
 
 
 def oracle_step_rate(cfg, layers, M, R, min_seconds=10.0, max_reps=20):
@@ -155,6 +178,10 @@ def main():
     torch.cuda.set_device(0)
     to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
     stream = torch.cuda.current_stream()
+
+    if args.profile == "prefill":
+        profile_prefill(q, CONFIGS["prefill_7b"], make_layer, to_dev, dev)
+        return
 
     cfg = CONFIGS["decode_7b_mlp"]
     M, R = cfg.m, cfg.r
