@@ -44,16 +44,24 @@ __global__ __launch_bounds__(256) void qz_amax(const uint4* __restrict__ w,
                                                int64_t nvec,
                                                uint32_t* __restrict__ slot) {
   uint32_t m = 0;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nvec;
-       i += stride) {
-    uint4 v = w[i];
-    uint32_t a = max(v.x & 0x7fffu, (v.x >> 16) & 0x7fffu);
-    uint32_t b = max(v.y & 0x7fffu, (v.y >> 16) & 0x7fffu);
-    uint32_t c = max(v.z & 0x7fffu, (v.z >> 16) & 0x7fffu);
-    uint32_t d = max(v.w & 0x7fffu, (v.w >> 16) & 0x7fffu);
+  auto fold = [&](const uint4& v) {
+    const uint32_t a = max(v.x & 0x7fffu, (v.x >> 16) & 0x7fffu);
+    const uint32_t b = max(v.y & 0x7fffu, (v.y >> 16) & 0x7fffu);
+    const uint32_t c = max(v.z & 0x7fffu, (v.z >> 16) & 0x7fffu);
+    const uint32_t d = max(v.w & 0x7fffu, (v.w >> 16) & 0x7fffu);
     m = max(m, max(max(a, b), max(c, d)));
+  };
+  // Four independent 16-byte loads per thread in flight per iteration.
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; i + 3 * stride < nvec; i += 4 * stride) {
+    const uint4 v0 = w[i], v1 = w[i + stride], v2 = w[i + 2 * stride], v3 = w[i + 3 * stride];
+    fold(v0);
+    fold(v1);
+    fold(v2);
+    fold(v3);
   }
+  for (; i < nvec; i += stride) fold(w[i]);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
   __shared__ uint32_t red[4];
