@@ -7,8 +7,10 @@ with M = 64 tokens (8 prompts x 8 samples): for each of the fused gate/up
 layer W [37888, 3584] and the down layer W [3584, 18944] (NVFP4, LoRA rank
 32, s = 2), draw the layer's AQN noise vector for stage 1 of 10 and run
 the linear layer (noisy activations, LoRA-down, NVFP4 contraction, LoRA-up
-epilogue).  The weights are quantized once before timing (the pages load
-the quantized model once); the quantizer is timed on its own.  Six copies
+epilogue).  The noise vectors do not depend on the activations, so they
+are drawn a few steps ahead on a second stream while earlier steps run.
+The weights are quantized once before timing (the pages load the
+quantized model once); the quantizer is timed on its own.  Six copies
 of the quantized weights (684 MB) are used in rotation so that the 256 MB
 Infinity Cache cannot serve them; inputs are resident in HBM before the
 timed region.
@@ -70,6 +72,14 @@ def main_kernel_bytes(m, n, k, r):
 def linear_flops(m, n, k, r):
     return 2.0 * m * n * k + 2.0 * m * r * (k + n)
 
+
+# Noise ring of the decode step: slots, steps sampled ahead, refill period.
+# Slot safety: a refill at step i writes the slots of steps i + AHEAD - EVERY
+# + 1 .. i + AHEAD after steps <= i - EVERY finished; the steps that may
+# still read a slot are i - EVERY + 1 .. i + AHEAD - EVERY, so RING must
+# exceed AHEAD + EVERY - 1.
+NOISE_RING, NOISE_AHEAD, NOISE_EVERY = 12, 6, 4
+assert NOISE_RING > NOISE_AHEAD + NOISE_EVERY - 1
 
 # Sources of the decode contraction kernel timed for the roofline; the
 # committed counter summary is only used while their digest is unchanged.
@@ -236,13 +246,46 @@ def main():
               f"({main_kernel_bytes(M, ly['n'], ly['k'], R):.0f} algorithmic B each)")
         return
 
+    # The AQN noise of a forward pass does not depend on its activations, so a
+    # second stream (default priority) samples the noise vectors a few steps
+    # ahead into a ring of slots, and each step waits only for its own slot.
+    # Every NOISE_EVERY steps the main stream marks its progress and the host,
+    # before refilling slots, waits for the mark of NOISE_EVERY steps earlier:
+    # no slot is rewritten while a queued step may still read it.  (A wait of
+    # the side stream on an event of the main stream, each step, serialised
+    # the queues on this runtime.)
+    side = torch.cuda.Stream(device=dev)
+    zring = [[torch.empty(ly["k"], dtype=torch.float32, device=dev) for ly in layers]
+             for _ in range(NOISE_RING)]
+    z_ready = [torch.cuda.Event() for _ in range(NOISE_RING)]
+    marks = {}
+
+    def sample(j):
+        sl = j % NOISE_RING
+        for li, ly in enumerate(layers):
+            q.qerl_aqn_sample(ly["L"].seed, 0, 2 * j + li, sigma, ly["k"],
+                              out=zring[sl][li], stream=side)
+        z_ready[sl].record(side)
+
     def step(i):
+        sl = i % NOISE_RING
+        stream.wait_event(z_ready[sl])
         for li, ly in enumerate(layers):
             codes, scales = ly["rot"][i % copies]
-            q.qerl_aqn_sample(ly["L"].seed, 0, 2 * i + li, sigma, ly["k"], out=ly["z"])
             q.qerl_linear_decode(ly["x"], codes, scales, ly["S"], ly["a"], ly["b"],
-                                 cfg.lora_scale, ly["z"], workspace=ly["ws"], y=ly["y"])
+                                 cfg.lora_scale, zring[sl][li], workspace=ly["ws"], y=ly["y"])
+        if i % NOISE_EVERY == NOISE_EVERY - 1:
+            mark = torch.cuda.Event()
+            mark.record(stream)
+            marks[i] = mark
+            old = marks.pop(i - NOISE_EVERY, None)
+            if old is not None:
+                old.synchronize()        # steps <= i - NOISE_EVERY are done
+            for j in range(i + NOISE_AHEAD - NOISE_EVERY + 1, i + NOISE_AHEAD + 1):
+                sample(j)
 
+    for j in range(NOISE_AHEAD):
+        sample(j)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -257,7 +300,7 @@ def main():
 
     # ---- dominant kernel alone: gate/up contraction, HIP events on its stream
     ly = layers[0]
-    q.qerl_linear_prepare(ly["x"], ly["n"], ly["a"], cfg.lora_scale, ly["z"], ly["ws"])
+    q.qerl_linear_prepare(ly["x"], ly["n"], ly["a"], cfg.lora_scale, zring[0][0], ly["ws"])
     reps = max(20, args.steps)
     for i in range(5):
         c, s = ly["rot"][i % copies]

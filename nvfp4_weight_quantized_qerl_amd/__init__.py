@@ -74,9 +74,11 @@ def qerl_aqn_sigma(sigma_start, sigma_end, num_stages, stage):
     return out.value
 
 
-def qerl_aqn_sample(seed, stream_id, call_id, sigma, d, device="cuda", out=None):
+def qerl_aqn_sample(seed, stream_id, call_id, sigma, d, device="cuda", out=None, stream=None):
+    """stream: a torch.cuda.Stream to enqueue on (default: the current one)."""
     z = out if out is not None else torch.empty(d, dtype=torch.float32, device=device)
-    _check(lib.qerl_aqn_sample(seed, stream_id, call_id, sigma, d, _ptr(z), _stream(z.device)),
+    hs = _stream(z.device) if stream is None else ctypes.c_void_p(stream.cuda_stream)
+    _check(lib.qerl_aqn_sample(seed, stream_id, call_id, sigma, d, _ptr(z), hs),
            "qerl_aqn_sample")
     return z
 
