@@ -26,154 +26,110 @@ struct FinishArgs {
   const float* __restrict__ ypart;      // [split, rows, n] fp32 partial sums of acc
   const float* __restrict__ gscale;
   const uint16_t* __restrict__ t;       // [rows, rpad16] bf16 s x_t A^T of this chunk
-  const float* __restrict__ tpart;      // [kchunks, mpad, rpad32] (chunk rows), or null
   const uint16_t* __restrict__ lora_b;  // [n, r] bf16
   uint16_t* __restrict__ y;             // [m_valid, n] rows of this chunk
-  int64_t n, tpart_stride;
-  int split, rows, m_valid, r, rpad16, rpad32, kchunks, lora_vec;
+  int64_t n;
+  int split, rows, m_valid, r, rpad16, lora_vec, vec4;
 };
 
-constexpr int kFinishRows = 4;  // token rows per thread
+constexpr int kFinishBatch = 16;   // partial sums loaded together per thread
 
 // y[m, j] = bf16(S * sum_s ypart[s, m, j] + sum_i t[m, i] B[j, i]): the
 // epilogue of a split-K contraction [QeRL summary, §3.4, Eq. 6 (S) and
-// Eq. 2 (LoRA side branch)].  The splits are summed in split order.  One
-// thread per output column j and kFinishRows token rows; t of those rows
-// sits in LDS, either read from t or, when the prepare step left only the
-// chunk partials, summed from them here in chunk order and rounded to
-// bf16.  Every thread issues its partial-sum loads before the LDS staging.
+// Eq. 2 (LoRA side branch)].  The splits are summed in split order, then
+// scaled, then the LoRA term is added in i order.  One thread per token row
+// and four consecutive columns; every load of a thread is independent of
+// the others, so a thread waits about one memory latency per batch of
+// kFinishBatch splits.
 __global__ __launch_bounds__(256) void splitk_finish(FinishArgs a) {
-  __shared__ float t_lds[kFinishRows * 128];
-  const int m0 = blockIdx.y * kFinishRows;
-  const int64_t col = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const bool live = col < a.n;
-  const int mrows = min(kFinishRows, a.m_valid - m0);
-  float acc[kFinishRows];
+  const int64_t groups = (a.n + 3) / 4;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= groups * a.m_valid) return;
+  const int m = (int)(idx / groups);
+  const int64_t col = (idx - (int64_t)m * groups) * 4;
+  const int ncol = (int)min<int64_t>(4, a.n - col);
+  const bool vec = a.vec4 && ncol == 4;
+  const float* src = a.ypart + (int64_t)m * a.n + col;
+  const int64_t sstride = (int64_t)a.rows * a.n;
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int s0 = 0; s0 < a.split; s0 += kFinishBatch) {
+    float4 part[kFinishBatch];
 #pragma unroll
-  for (int mm = 0; mm < kFinishRows; ++mm) acc[mm] = 0.0f;
-  if (live) {
-    const float* src = a.ypart + (int64_t)m0 * a.n + col;
-    const int64_t sstride = (int64_t)a.rows * a.n;
-#pragma unroll 4
-    for (int s = 0; s < a.split; ++s) {
-#pragma unroll
-      for (int mm = 0; mm < kFinishRows; ++mm)
-        if (mm < mrows) acc[mm] += src[s * sstride + (int64_t)mm * a.n];
-    }
-  }
-  // The LoRA B row of this column, loaded before the LDS staging when it is
-  // 16-byte aligned and short (r <= 64), so that all global loads of the
-  // thread are in flight together.
-  constexpr int kBPre = 8;
-  const bool bpre = a.lora_vec && a.r <= 8 * kBPre;
-  uint4 bv[kBPre];
-  if (live && bpre) {
-    const uint4* brow4 = reinterpret_cast<const uint4*>(a.lora_b + col * a.r);
-#pragma unroll
-    for (int q = 0; q < kBPre; ++q)
-      bv[q] = 8 * q < a.r ? brow4[q] : make_uint4(0u, 0u, 0u, 0u);
-  }
-  if (a.tpart) {
-    // Items (mm, jj) of t, kFinishRows x r <= 512 of them, 128 per pass:
-    // the two thread halves sum the even and the odd chunks (eight loads
-    // in flight per thread), then the halves are combined in chunk-pair
-    // order and rounded to bf16.
-    __shared__ float half_sum[2][128];
-    const int items = kFinishRows * a.r;
-    const int hf = threadIdx.x >> 7, it = threadIdx.x & 127;
-    for (int base = 0; base < items; base += 128) {
-      const int i = base + it;
-      float v = 0.0f;
-      if (i < items) {
-        const int mm = i / a.r, jj = i % a.r;
-        if (m0 + mm < a.m_valid) {
-          const float* tp = a.tpart + (int64_t)(m0 + mm) * a.rpad32 + jj;
-          float p4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-          int c = hf;
-          for (; c + 14 < a.kchunks; c += 16) {
-#pragma unroll
-            for (int u = 0; u < 8; ++u) p4[u & 3] += tp[(int64_t)(c + 2 * u) * a.tpart_stride];
-          }
-          for (; c < a.kchunks; c += 2) p4[0] += tp[(int64_t)c * a.tpart_stride];
-          v = (p4[0] + p4[1]) + (p4[2] + p4[3]);
+    for (int u = 0; u < kFinishBatch; ++u) {
+      part[u] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      if (s0 + u < a.split) {
+        const float* ps = src + (int64_t)(s0 + u) * sstride;
+        if (vec) {
+          part[u] = *reinterpret_cast<const float4*>(ps);
+        } else {
+          part[u].x = ps[0];
+          if (ncol > 1) part[u].y = ps[1];
+          if (ncol > 2) part[u].z = ps[2];
+          if (ncol > 3) part[u].w = ps[3];
         }
       }
-      half_sum[hf][it] = v;
-      __syncthreads();
-      if (hf == 0 && i < items) {
-        const int mm = i / a.r, jj = i % a.r;
-        t_lds[mm * 128 + jj] = bf16_to_f32(f32_to_bf16_bits(half_sum[0][it] + half_sum[1][it]));
-      }
-      __syncthreads();
     }
-    // Columns jj >= r of t_lds are never read (the LoRA loop stops at r).
-  } else {
-    for (int i = threadIdx.x; i < kFinishRows * 128; i += 256) {
-      const int mm = i / 128, jj = i % 128;
-      t_lds[i] = (m0 + mm < a.m_valid && jj < a.r)
-                     ? bf16_to_f32(a.t[(int64_t)(m0 + mm) * a.rpad16 + jj])
-                     : 0.0f;
+#pragma unroll
+    for (int u = 0; u < kFinishBatch; ++u) {
+      if (s0 + u < a.split) {
+        acc[0] += part[u].x;
+        acc[1] += part[u].y;
+        acc[2] += part[u].z;
+        acc[3] += part[u].w;
+      }
     }
   }
-  __syncthreads();
-  if (!live) return;
   const float S = *a.gscale;
 #pragma unroll
-  for (int mm = 0; mm < kFinishRows; ++mm) acc[mm] *= S;
-  if (bpre) {
+  for (int c = 0; c < 4; ++c) acc[c] *= S;
+  if (a.r > 0) {
+    const uint16_t* trow = a.t + (int64_t)m * a.rpad16;
+#pragma unroll 4
+    for (int i0 = 0; i0 < a.r; i0 += 8) {
+      // t[m, i0 .. i0+7] (t is padded to rpad16 columns with zeros)
+      const uint4 tv = *reinterpret_cast<const uint4*>(trow + i0);
+      const float tf[8] = {bf16_to_f32(tv.x & 0xffffu), bf16_to_f32(tv.x >> 16),
+                           bf16_to_f32(tv.y & 0xffffu), bf16_to_f32(tv.y >> 16),
+                           bf16_to_f32(tv.z & 0xffffu), bf16_to_f32(tv.z >> 16),
+                           bf16_to_f32(tv.w & 0xffffu), bf16_to_f32(tv.w >> 16)};
 #pragma unroll
-    for (int q = 0; q < kBPre; ++q) {
-      if (8 * q >= a.r) break;
-      const uint32_t bw[4] = {bv[q].x, bv[q].y, bv[q].z, bv[q].w};
+      for (int c = 0; c < 4; ++c) {
+        if (c >= ncol) break;
+        const uint16_t* brow = a.lora_b + (col + c) * a.r + i0;
+        float bf[8];
+        if (a.lora_vec) {
+          const uint4 bv = *reinterpret_cast<const uint4*>(brow);
+          const uint32_t bw[4] = {bv.x, bv.y, bv.z, bv.w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float b0 = bf16_to_f32(bw[e] & 0xffffu), b1 = bf16_to_f32(bw[e] >> 16);
+          for (int e = 0; e < 4; ++e) {
+            bf[2 * e] = bf16_to_f32(bw[e] & 0xffffu);
+            bf[2 * e + 1] = bf16_to_f32(bw[e] >> 16);
+          }
+        } else {
 #pragma unroll
-        for (int mm = 0; mm < kFinishRows; ++mm)
-          acc[mm] += t_lds[mm * 128 + 8 * q + 2 * e] * b0 + t_lds[mm * 128 + 8 * q + 2 * e + 1] * b1;
+          for (int e = 0; e < 8; ++e) bf[e] = i0 + e < a.r ? bf16_to_f32(brow[e]) : 0.0f;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[c] += tf[e] * bf[e];
       }
     }
   }
-  const uint16_t* brow = a.lora_b + col * a.r;
-  for (int i0 = bpre ? a.r : 0; i0 < a.r; i0 += 8) {
-    uint32_t bw[4];
-    if (a.lora_vec) {
-      const uint4 v = *reinterpret_cast<const uint4*>(brow + i0);
-      bw[0] = v.x; bw[1] = v.y; bw[2] = v.z; bw[3] = v.w;
-    } else {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t lo = i0 + 2 * q < a.r ? brow[i0 + 2 * q] : 0u;
-        const uint32_t hi = i0 + 2 * q + 1 < a.r ? brow[i0 + 2 * q + 1] : 0u;
-        bw[q] = lo | (hi << 16);
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float b0 = bf16_to_f32(bw[q] & 0xffffu), b1 = bf16_to_f32(bw[q] >> 16);
-#pragma unroll
-      for (int mm = 0; mm < kFinishRows; ++mm)
-        acc[mm] += t_lds[mm * 128 + i0 + 2 * q] * b0 + t_lds[mm * 128 + i0 + 2 * q + 1] * b1;
-    }
+  uint16_t* dst = a.y + (int64_t)m * a.n + col;
+  if (vec) {
+    *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]));
+  } else {
+    for (int c = 0; c < ncol; ++c) dst[c] = f32_to_bf16_bits(acc[c]);
   }
-#pragma unroll
-  for (int mm = 0; mm < kFinishRows; ++mm)
-    if (mm < mrows) a.y[(int64_t)(m0 + mm) * a.n + col] = f32_to_bf16_bits(acc[mm]);
 }
 
-// m0_chunk: first token row of the chunk (for the LoRA-down partials).
-hipError_t launch_finish(const LinearPlan& p, int split, int rows, int m_valid, int64_t m0_chunk,
+hipError_t launch_finish(const LinearPlan& p, int split, int rows, int m_valid,
                          const float* ypart, const float* gscale, const uint16_t* t,
                          const uint16_t* lora_b, int r, int lora_vec, uint16_t* y,
-                         const char* ws, hipStream_t stream) {
+                         hipStream_t stream) {
   FinishArgs f;
   f.ypart = ypart;
   f.gscale = gscale;
   f.t = t;
-  f.tpart = (r > 0 && !prepare_reduces_t(p))
-                ? reinterpret_cast<const float*>(ws + p.off_tpart) + m0_chunk * p.rpad32
-                : nullptr;
-  f.tpart_stride = p.mpad * p.rpad32;
   f.lora_b = lora_b;
   f.y = y;
   f.n = p.n;
@@ -182,12 +138,11 @@ hipError_t launch_finish(const LinearPlan& p, int split, int rows, int m_valid, 
   f.m_valid = m_valid;
   f.r = r;
   f.rpad16 = p.rpad16;
-  f.rpad32 = p.rpad32;
-  f.kchunks = p.kchunks;
   f.lora_vec = lora_vec;
-  const dim3 grid((unsigned)((p.n + 255) / 256),
-                  (unsigned)((m_valid + kFinishRows - 1) / kFinishRows));
-  hipLaunchKernelGGL(splitk_finish, grid, dim3(256), 0, stream, f);
+  f.vec4 = p.n % 4 == 0 && (reinterpret_cast<uintptr_t>(y) & 7) == 0;
+  const int64_t threads = (p.n + 3) / 4 * m_valid;
+  hipLaunchKernelGGL(splitk_finish, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                     stream, f);
   return hipGetLastError();
 }
 
@@ -211,10 +166,8 @@ hipError_t run_decode_lds(const LinearPlan& p, int mt, const uint8_t* codes,
   a.ypart = reinterpret_cast<float*>(ws + p.off_ypart);
   a.n = p.n;
   a.k = p.k;
-  const int64_t nblocks = p.k / 256;
-  const int64_t per = (nblocks + p.dec_split - 1) / p.dec_split;
-  const int split = (int)((nblocks + per - 1) / per);
-  a.blocks_per_split = per;
+  const int split = lds_split(p);
+  a.nblocks = p.k / 256;
   a.m_valid = m_valid;
   a.rows = p.dec_rows;
   a.split = split;
@@ -224,8 +177,8 @@ hipError_t run_decode_lds(const LinearPlan& p, int mt, const uint8_t* codes,
   hipLaunchKernelGGL(kern, dim3((unsigned)p.dec_groups, (unsigned)split), dim3(512), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || split == 1) return e;
-  return launch_finish(p, split, 32 * mt, m_valid, m0_chunk, a.ypart, gscale, t, lora_b, r,
-                       lora_vec, y, ws, stream);
+  return launch_finish(p, split, 32 * mt, m_valid, a.ypart, gscale, t, lora_b, r, lora_vec, y,
+                       stream);
 }
 
 }  // namespace
@@ -272,8 +225,8 @@ hipError_t run_decode_chunks(const LinearPlan& p, const uint8_t* codes,
                          dim3(256), 0, stream, a);
       e = hipGetLastError();
       if (e == hipSuccess && p.dec_split > 1)
-        e = launch_finish(p, p.dec_split, 32 * mt, a.m_valid, m0, a.ypart, gscale, a.t, lora_b,
-                          a.r, a.lora_vec, a.y, ws, stream);
+        e = launch_finish(p, p.dec_split, 32 * mt, a.m_valid, a.ypart, gscale, a.t, lora_b,
+                          a.r, a.lora_vec, a.y, stream);
     }
     if (e != hipSuccess) return e;
     m0 += 32 * mt;

@@ -48,7 +48,7 @@ struct Args {
   uint16_t* y;             // [m_valid, n]
   float* ypart;            // [split, MT*32, n] fp32 partials
   int64_t n, k;
-  int64_t blocks_per_split;  // 256-wide K blocks per split
+  int64_t nblocks;           // 256-wide K blocks (k / 256), spread evenly over the splits
   int m_valid, rows, split, r, rpad16, lora_vec;
 };
 
@@ -149,9 +149,9 @@ __global__ __launch_bounds__(512, 1) void decode_lds(Args a) {
   const int64_t row0 = (int64_t)blockIdx.x * a.rows;
   const int64_t row_end = min(a.n, row0 + (int64_t)a.rows);
   const int split_id = blockIdx.y;
-  const int64_t nblocks = a.k / 256;
-  const int64_t bb = (int64_t)split_id * a.blocks_per_split;
-  const int64_t be = min(nblocks, bb + a.blocks_per_split);
+  // Blocks [bb, be) of this split: the splits differ by at most one block.
+  const int64_t bb = (int64_t)split_id * a.nblocks / a.split;
+  const int64_t be = (int64_t)(split_id + 1) * a.nblocks / a.split;
 
   if (a.r > 0) {
     const int words = XROWS * a.rpad16 / 8;

@@ -73,7 +73,10 @@ void plan_decode(LinearPlan* p, int mt) {
       int64_t s = std::max<int64_t>(1, cu / groups);
       s = std::min<int64_t>(s, std::max<int64_t>(1, units / 4));
       const int64_t wgs = groups * s;
-      const double util = (double)wgs / (double)(cu * cdiv(wgs, cu));
+      // CU occupancy times the share of the streamed 32-row subtiles that
+      // belongs to the workgroup (the rest is loaded and discarded).
+      const double util = (double)wgs / (double)(cu * cdiv(wgs, cu)) *
+                          (double)cand / (double)(32 * cdiv(cand, 32));
       if (util > best + 1e-9 || (util > best - 1e-9 && cand > rows)) {
         best = util;
         rows = cand;
@@ -264,20 +267,8 @@ __global__ __launch_bounds__(256) void treduce_kernel(const float* __restrict__ 
 
 }  // namespace
 
-bool decode_splits_every_chunk(const LinearPlan& p) {
-  if (p.dec_split <= 1) return false;
-  // The LDS-staged kernel re-derives its split from 256-wide blocks.
-  const int64_t nb = p.k / 256;
-  const bool lds = p.k % 256 == 0 && p.dec_nt <= 5;
-  if (lds && nb > 0) {
-    const int64_t per = cdiv(nb, p.dec_split);
-    if (cdiv(nb, per) <= 1) return false;
-  }
-  return true;
-}
-
-bool prepare_reduces_t(const LinearPlan& p) {
-  return p.r > 0 && !(p.m <= 64 && decode_splits_every_chunk(p));
+int lds_split(const LinearPlan& p) {
+  return (int)std::min<int64_t>(p.dec_split, std::max<int64_t>(1, p.k / 256));
 }
 
 hipError_t launch_treduce(const LinearPlan& p, char* ws, hipStream_t stream) {
@@ -319,7 +310,7 @@ hipError_t launch_linear_prepare(const LinearPlan& p, const uint16_t* x,
     default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || !prepare_reduces_t(p)) return e;
+  if (e != hipSuccess) return e;
   return launch_treduce(p, ws, stream);
 }
 

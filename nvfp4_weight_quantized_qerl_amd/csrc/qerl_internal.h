@@ -53,13 +53,12 @@ hipError_t launch_linear_prepare(const LinearPlan& p, const uint16_t* x,
                                  hipStream_t stream);
 
 // LoRA-down reduction: launch_linear_prepare writes the chunk partials
-// s x_t A^T (tpart) and, when prepare_reduces_t(p), also t = bf16(sum of
-// the partials).  Otherwise (every decode chunk splits K) the split-K
-// finishing kernel reduces tpart itself, and any other consumer of t calls
-// launch_treduce first.
-bool decode_splits_every_chunk(const LinearPlan& p);
-bool prepare_reduces_t(const LinearPlan& p);
+// s x_t A^T (tpart) and then t = bf16(sum of the partials) (launch_treduce).
 hipError_t launch_treduce(const LinearPlan& p, char* ws, hipStream_t stream);
+
+// K splits of the LDS-staged decode kernel: the planned split, capped at
+// the number of 256-wide K blocks.
+int lds_split(const LinearPlan& p);
 
 // The contraction kernels read x_t and the LoRA-down t = bf16(s x_t A^T)
 // that launch_linear_prepare left in the workspace.
