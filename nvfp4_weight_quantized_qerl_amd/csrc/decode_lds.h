@@ -95,10 +95,15 @@ __device__ __forceinline__ uint4 load_lora_b(const Args& a, int64_t row, bool li
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-// acc (full K sum of one 32x32 tile) -> S * acc + t B^T -> y.
+// acc (full K sum of one 32x32 tile) -> S * acc + t B^T -> y.  row: the
+// weight row (output column) of this lane; row_end: end of the workgroup's
+// rows.  A tile with all 32 columns and all 32 token rows in range goes out
+// through the wave's LDS scratch (2 KB): written in the MFMA layout, read
+// back as 32 B of one token row per lane, stored with 16-byte stores.
 __device__ __forceinline__ void epilogue_tile(const Args& a, f32x16_t acc, float S, int u,
                                               int64_t row, bool live, int lane,
-                                              const uint16_t* t_lds) {
+                                              const uint16_t* t_lds, int64_t row_end,
+                                              uint16_t* scratch) {
   const int h = lane >> 5, c = lane & 31;
 #pragma unroll
   for (int v = 0; v < 16; ++v) acc[v] *= S;
@@ -109,6 +114,21 @@ __device__ __forceinline__ void epilogue_tile(const Args& a, f32x16_t acc, float
       const uint4 bv = load_lora_b(a, row, live, j0 + 8 * h);
       acc = mfma_bf16(tv, bv, acc);
     }
+  }
+  const int64_t col0 = row - c;                    // first column of the tile
+  if (col0 + 32 <= row_end && 32 * u + 32 <= a.m_valid && a.n % 8 == 0 &&
+      (reinterpret_cast<uintptr_t>(a.y) & 15) == 0) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) scratch[acc_row(v, lane) * 32 + c] = f32_to_bf16_bits(acc[v]);
+    // The same wave reads its own writes back: LDS operations of one wave
+    // complete in order.
+    const int r = lane >> 1, half = lane & 1;
+    const uint4 lo = *reinterpret_cast<const uint4*>(scratch + r * 32 + 16 * half);
+    const uint4 hi = *reinterpret_cast<const uint4*>(scratch + r * 32 + 16 * half + 8);
+    uint16_t* dst = a.y + (int64_t)(32 * u + r) * a.n + col0 + 16 * half;
+    *reinterpret_cast<uint4*>(dst) = lo;
+    *reinterpret_cast<uint4*>(dst + 8) = hi;
+    return;
   }
   if (!live) return;
 #pragma unroll
@@ -312,10 +332,14 @@ __global__ __launch_bounds__(512, 1) void decode_lds(Args a) {
 
   const float S = *a.gscale;
   if (a.split == 1) {
+    // Every slice is free after the last round; wave (q, hf) takes slice
+    // hf * SPH + q (q < 4 <= SPH) as its transpose scratch.
+    uint16_t* scratch = reinterpret_cast<uint16_t*>(slice(hf * SPH + q));
 #pragma unroll
     for (int p = 0; p < NT0 * MT; ++p)
       if (owns(p))
-        epilogue_tile(a, acc[p / MT][p % MT], S, p % MT, tile_row(p), tile_live(p), lane, t_lds);
+        epilogue_tile(a, acc[p / MT][p % MT], S, p % MT, tile_row(p), tile_live(p), lane, t_lds,
+                      row_end, scratch);
     return;
   }
 
