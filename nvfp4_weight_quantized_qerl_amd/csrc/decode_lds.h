@@ -103,16 +103,23 @@ __device__ __forceinline__ uint4 load_lora_b(const Args& a, int64_t row, bool li
 __device__ __forceinline__ void epilogue_tile(const Args& a, f32x16_t acc, float S, int u,
                                               int64_t row, bool live, int lane,
                                               const uint16_t* t_lds, int64_t row_end,
-                                              uint16_t* scratch) {
+                                              uint16_t* scratch, const uint4* bpre) {
   const int h = lane >> 5, c = lane & 31;
 #pragma unroll
   for (int v = 0; v < 16; ++v) acc[v] *= S;
   if (a.r > 0) {
     const uint16_t* trow = t_lds + (32 * u + c) * a.rpad16;
-    for (int j0 = 0; j0 < a.rpad16; j0 += 16) {
-      const uint4 tv = *reinterpret_cast<const uint4*>(trow + j0 + 8 * h);
-      const uint4 bv = load_lora_b(a, row, live, j0 + 8 * h);
-      acc = mfma_bf16(tv, bv, acc);
+    if (bpre) {
+      // r <= 32, B loaded ahead (bpre[1] is zero when r <= 16).
+      acc = mfma_bf16(*reinterpret_cast<const uint4*>(trow + 8 * h), bpre[0], acc);
+      if (a.rpad16 > 16)
+        acc = mfma_bf16(*reinterpret_cast<const uint4*>(trow + 16 + 8 * h), bpre[1], acc);
+    } else {
+      for (int j0 = 0; j0 < a.rpad16; j0 += 16) {
+        const uint4 tv = *reinterpret_cast<const uint4*>(trow + j0 + 8 * h);
+        const uint4 bv = load_lora_b(a, row, live, j0 + 8 * h);
+        acc = mfma_bf16(tv, bv, acc);
+      }
     }
   }
   const int64_t col0 = row - c;                    // first column of the tile
@@ -173,6 +180,7 @@ __global__ __launch_bounds__(512, 1) void decode_lds(Args a) {
   const int64_t bb = (int64_t)split_id * a.nblocks / a.split;
   const int64_t be = (int64_t)(split_id + 1) * a.nblocks / a.split;
 
+  const float S = *a.gscale;     // first needed in the epilogue
   if (a.r > 0) {
     const int words = XROWS * a.rpad16 / 8;
     for (int i = threadIdx.x; i < words; i += 512)
@@ -299,6 +307,28 @@ __global__ __launch_bounds__(512, 1) void decode_lds(Args a) {
                       : reinterpret_cast<float*>(xs1) + (s - 4 * MT) * 1024;
   };
   const int ntile = (hf ? NT1 : NT0) * MT;
+  auto owns = [&](int p) { return p < ntile && q == p % TPR; };
+  auto tile_row = [&](int p) { return row0 + 32 * (tbase + p / MT) + c; };
+  auto tile_live = [&](int p) { return tile_row(p) < row_end; };
+
+  // LoRA B operands of the owned output tiles (r <= 32: two 16-wide
+  // steps), loaded before the cross-wave reduction so that their latency
+  // passes during it.  Wave q owns tiles q, q + TPR, ...: tile p's operands
+  // go to slot p / TPR.
+  constexpr int NOWN = (NT0 * MT + TPR - 1) / TPR;
+  uint4 bpre[NOWN][2];
+  const bool b_pre = a.split == 1 && a.r > 0 && a.rpad16 <= 32;
+  if (b_pre) {
+#pragma unroll
+    for (int p = 0; p < NT0 * MT; ++p) {
+      if (owns(p)) {
+        bpre[p / TPR][0] = load_lora_b(a, tile_row(p), tile_live(p), 8 * h);
+        bpre[p / TPR][1] = a.rpad16 > 16 ? load_lora_b(a, tile_row(p), tile_live(p), 16 + 8 * h)
+                                         : make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+  }
+
 #pragma unroll
   for (int rnd = 0; rnd < ROUNDS; ++rnd) {
 #pragma unroll
@@ -326,11 +356,6 @@ __global__ __launch_bounds__(512, 1) void decode_lds(Args a) {
     }
     __syncthreads();
   }
-  auto owns = [&](int p) { return p < ntile && q == p % TPR; };
-  auto tile_row = [&](int p) { return row0 + 32 * (tbase + p / MT) + c; };
-  auto tile_live = [&](int p) { return tile_row(p) < row_end; };
-
-  const float S = *a.gscale;
   if (a.split == 1) {
     // Every slice is free after the last round; wave (q, hf) takes slice
     // hf * SPH + q (q < 4 <= SPH) as its transpose scratch.
@@ -339,7 +364,7 @@ __global__ __launch_bounds__(512, 1) void decode_lds(Args a) {
     for (int p = 0; p < NT0 * MT; ++p)
       if (owns(p))
         epilogue_tile(a, acc[p / MT][p % MT], S, p % MT, tile_row(p), tile_live(p), lane, t_lds,
-                      row_end, scratch);
+                      row_end, scratch, b_pre ? bpre[p / TPR] : nullptr);
     return;
   }
 

@@ -255,13 +255,17 @@ __global__ __launch_bounds__(256) void treduce_kernel(const float* __restrict__ 
   const int j = (int)(i % rpad16);
   const float* src = tpart + mrow * rpad32 + j;
   const int64_t stride = mpad * rpad32;
+  // Chunk c goes to partial sum c % 4; the loads of a batch of 16 chunks
+  // are all issued before the first add.
   float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  int c = 0;
-  for (; c + 4 <= kchunks; c += 4) {
+  for (int c0 = 0; c0 < kchunks; c0 += 16) {
+    float v[16];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) acc[u] += src[(c + u) * stride];
+    for (int u = 0; u < 16; ++u) v[u] = c0 + u < kchunks ? src[(int64_t)(c0 + u) * stride] : 0.0f;
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      if (c0 + u < kchunks) acc[u & 3] += v[u];
   }
-  for (; c < kchunks; ++c) acc[c & 3] += src[c * stride];
   t[i] = f32_to_bf16_bits((acc[0] + acc[1]) + (acc[2] + acc[3]));
 }
 
