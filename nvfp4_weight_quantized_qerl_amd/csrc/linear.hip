@@ -12,8 +12,9 @@
 // prepare writes x_t = bf16(x * (1 + z)) to the workspace, rows padded to a
 // multiple of 32 with zeros so the contraction kernels need no row masks,
 // and, with a LoRA branch, the LoRA-down t:
-//   prep_kernel (four waves per 32 rows x 512-wide K chunk): x_t and
-//           tpart = x_t A^T over the chunk (bf16 MFMA, fp32);
+//   prep_kernel (four waves per 32 rows x 512-wide K chunk): x_t, read
+//           and written one row per instruction, and tpart = x_t A^T over
+//           the chunk (bf16 MFMA, fp32, operands through LDS);
 //   treduce: t = bf16(sum over chunks of tpart), summed in a fixed order
 //           so the result is deterministic.  When every decode chunk of the
 //           shape splits K, the split-K finishing kernel sums tpart for its
@@ -157,33 +158,34 @@ __device__ __forceinline__ uint4 noisy8(uint4 xv, float4 z0, float4 z1) {
   return xv;
 }
 
-// One workgroup: 32 rows x one 512-wide K chunk, wave w taking the 128
-// channels at 128 w.  Each lane issues all of its loads (8 steps of x, z
-// and RT rows of A) before the first MFMA, so the chunk costs about one
-// memory latency.  The four waves' LoRA-down tiles are summed through LDS
-// and wave 0 writes the chunk's partial tpart[chunk, rows, rpad32].
+// One workgroup: 32 rows x one 512-wide K chunk.
+//   x_t: wave w reads and writes rows 8 w .. 8 w + 7, one row of the chunk
+//        (1 KB) per instruction, lane l holding channels 8 l .. 8 l + 7; the
+//        rows also go to an LDS tile, 16-byte chunk q of row rr stored at
+//        q ^ (rr mod 16) so that the MFMA reads below (lane = row) hit 16
+//        different bank groups per 16 lanes.
+//   LoRA-down: wave w takes the 128 channels at 128 w: eight 32x32x16 MFMAs
+//        per 32 rows of A, operands x_t from the LDS tile and A from global
+//        memory (issued first, so their latency passes under the x_t work).
+// The four waves' LoRA-down tiles are summed through LDS and wave 0 writes
+// the chunk's partial tpart[chunk, rows, rpad32].
 template <int RT>
 __global__ __launch_bounds__(256) void prep_kernel(PrepArgs p) {
   constexpr int STEPS = 8;
+  __shared__ __attribute__((aligned(16))) uint4 xs[32 * 64];
   __shared__ float red[3 * (RT > 0 ? RT : 1) * 16 * 64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int h = lane >> 5, c = lane & 31;
-  const int64_t mrow = (int64_t)blockIdx.x * 32 + c;
-  const int64_t kb = (int64_t)blockIdx.y * kPrepChunk + 128 * wave;
-  const bool live = mrow < p.m;
-  const uint16_t* xrow = p.x + mrow * p.k;
-  uint16_t* xtrow = p.xt + mrow * p.k;
-  uint4 xv[STEPS];
-  float4 z0[STEPS], z1[STEPS];
+  const int64_t kc = (int64_t)blockIdx.y * kPrepChunk;
+  const int64_t row0 = (int64_t)blockIdx.x * 32;
+
+  // A operands of this wave's 128 channels (lane: row j = 32 t + c of A).
+  const int64_t kb = kc + 128 * wave;
   uint4 av[RT > 0 ? RT : 1][STEPS];
-  const float4 zero4 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
 #pragma unroll
   for (int s = 0; s < STEPS; ++s) {
     const int64_t k0 = kb + 16 * s + 8 * h;
     const bool in = kb + 16 * s < p.k;   // k % 16 == 0: the whole step is in range
-    xv[s] = (in && live) ? *reinterpret_cast<const uint4*>(xrow + k0) : make_uint4(0u, 0u, 0u, 0u);
-    z0[s] = (in && p.z) ? *reinterpret_cast<const float4*>(p.z + k0) : zero4;
-    z1[s] = (in && p.z) ? *reinterpret_cast<const float4*>(p.z + k0 + 4) : zero4;
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
       const int j = 32 * t + c;
@@ -191,19 +193,42 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs p) {
                                  : make_uint4(0u, 0u, 0u, 0u);
     }
   }
+
+  // x_t rows, coalesced.
+  const int64_t kl = kc + 8 * lane;       // this lane's channels
+  const bool kin = kl < p.k;              // k % 8 == 0: all eight in range or none
+  float4 z0 = make_float4(0.0f, 0.0f, 0.0f, 0.0f), z1 = z0;
+  if (kin && p.z) {
+    z0 = *reinterpret_cast<const float4*>(p.z + kl);
+    z1 = *reinterpret_cast<const float4*>(p.z + kl + 4);
+  }
+  uint4 xv[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int64_t mrow = row0 + 8 * wave + i;
+    xv[i] = (kin && mrow < p.m) ? *reinterpret_cast<const uint4*>(p.x + mrow * p.k + kl)
+                                : make_uint4(0u, 0u, 0u, 0u);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int rr = 8 * wave + i;
+    const int64_t mrow = row0 + rr;
+    if (mrow < p.m && p.z) xv[i] = noisy8(xv[i], z0, z1);
+    if (kin) *reinterpret_cast<uint4*>(p.xt + mrow * p.k + kl) = xv[i];
+    xs[rr * 64 + (lane ^ (rr & 15))] = xv[i];
+  }
+  if (RT == 0) return;
+  __syncthreads();
+
   f32x16_t acc[RT > 0 ? RT : 1];
 #pragma unroll
   for (int t = 0; t < (RT > 0 ? RT : 1); ++t) acc[t] = zero16();
 #pragma unroll
   for (int s = 0; s < STEPS; ++s) {
-    const int64_t k0 = kb + 16 * s + 8 * h;
-    if (kb + 16 * s >= p.k) break;
-    if (live && p.z) xv[s] = noisy8(xv[s], z0[s], z1[s]);
-    *reinterpret_cast<uint4*>(xtrow + k0) = xv[s];
+    const uint4 xa = xs[c * 64 + ((16 * wave + 2 * s + h) ^ (c & 15))];
 #pragma unroll
-    for (int t = 0; t < RT; ++t) acc[t] = mfma_bf16(xv[s], av[t][s], acc[t]);
+    for (int t = 0; t < RT; ++t) acc[t] = mfma_bf16(xa, av[t][s], acc[t]);
   }
-  if (RT == 0) return;
   if (wave > 0) {
 #pragma unroll
     for (int t = 0; t < RT; ++t)
@@ -218,8 +243,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs p) {
     for (int w = 0; w < 3; ++w)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[t][v] += red[((w * RT + t) * 16 + v) * 64 + lane];
-    float* dst = p.tpart + ((int64_t)blockIdx.y * p.mpad + (int64_t)blockIdx.x * 32) * p.rpad32
-                 + 32 * t + c;
+    float* dst = p.tpart + ((int64_t)blockIdx.y * p.mpad + row0) * p.rpad32 + 32 * t + c;
 #pragma unroll
     for (int v = 0; v < 16; ++v) dst[(int64_t)acc_row(v, lane) * p.rpad32] = p.lora_scale * acc[t][v];
   }
