@@ -25,6 +25,7 @@ Modules
   aqn      the exponential sigma schedule (Eq. 8) and the noise vector
            (Eq. 7) drawn from Philox4x64-10 + Box-Muller.
   linear   y = (x * (1 + z)) W^T + s (x * (1 + z)) A^T B^T in fp64.
+  rmsnorm  the noisy RMSNorm producer (w + z) * x / rms(x) (Eq. 10).
 
 Parity pins (tests/test_oracle_*.py): every function here is checked
 against something other than itself: values printed on the pages

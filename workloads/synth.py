@@ -73,3 +73,12 @@ def make_layer(m, n, k, r, seed, w_std=0.02, outlier_frac=0.0,
     return LayerInputs(x=x, w=w, a=a, b=b, lora_scale=float(lora_scale),
                        stage=int(stage), seed=int(seed),
                        stream_id=int(stream_id), call_id=int(call_id))
+
+
+def norm_inputs(m, d, seed, w_mean=1.0, w_std=0.05):
+    """Inputs of the noisy RMSNorm: x [m, d] ~ N(0, 1) and the RMSNorm
+    scale w [d] ~ N(w_mean, w_std^2), both as bf16 bit patterns."""
+    x = normal_bf16((m, d), 1.0, 1000 * seed + 21)
+    rng = np.random.default_rng(1000 * seed + 22)
+    w = bf16_from_f32((w_mean + w_std * rng.standard_normal(d)).astype(np.float32))
+    return x, w
