@@ -19,8 +19,10 @@ Printed: one JSON line.  `value` = decode weight-stream GB/s (algorithmic
 bytes of the step / step time); `roofline` = the decode contraction kernel
 of the gate/up layer, timed alone with HIP events on its launch stream;
 `prefill` = the 4096-token prefill of the Qwen2.5-7B qkv and down layers
-in TFLOP/s; `quantizer` = bulk quantization GB/s; `cpu_baseline` = the
-oracle on the host cores on a bounded slice of the same step.
+in TFLOP/s; `rmsnorm` = the noisy RMSNorm producer on the 7B hidden size
+(GB/s at 4096 rows, microseconds at 64 rows); `quantizer` = bulk
+quantization GB/s; `cpu_baseline` = the oracle on the host cores on a
+bounded slice of the same step.
 """
 import argparse
 import hashlib
@@ -372,6 +374,39 @@ def main():
                    "gemm_frac_bf16_peak": round(pflops / t_main / 1e12 / BF16_PEAK_TFLOPS, 4),
                    "layers": per_layer}
 
+    # ---- noisy RMSNorm producer (Eq. 10) on the 7B hidden size: the 4096-token
+    # prefill rows (HBM-bound; copies rotated past the Infinity Cache) and the
+    # 64 decode rows (latency-bound)
+    rmsnorm = None
+    if not args.no_prefill:
+        from workloads import norm_inputs
+        rmsnorm = []
+        for m, d, copies_n in ((4096, 3584, 10), (64, 3584, 1)):
+            xs_, ws_ = norm_inputs(m, d, seed=31)
+            wd = to_dev(ws_)
+            xcopies = [to_dev(xs_) for _ in range(copies_n)]
+            ycopies = [torch.empty_like(xcopies[0]) for _ in range(copies_n)]
+            zd = q.qerl_aqn_sample(31, 0, 0, sigma, d, device=dev)
+            run = lambda i: q.qerl_rmsnorm_noisy(xcopies[i % copies_n], wd, zd, 1e-6,
+                                                 out=ycopies[i % copies_n])
+            for i in range(5):
+                run(i)
+            reps = 50
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(reps):
+                run(i)
+            e1.record(stream)
+            e1.synchronize()
+            t = e0.elapsed_time(e1) / 1e3 / reps
+            nbytes = 4 * m * d + 2 * d + 4 * d
+            rmsnorm.append({"workload": f"noisy RMSNorm {m}x{d} (Qwen2.5-7B hidden)",
+                            "us": round(t * 1e6, 2), "GB_per_s": round(nbytes / t / 1e9, 1),
+                            "frac_hbm": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4),
+                            "bytes": nbytes})
+            del xcopies, ycopies
+
     # ---- oracle on the host cores: the same step, weights quantized beforehand
     cpu = None
     if not args.no_cpu:
@@ -390,6 +425,7 @@ def main():
         "roofline": roofline,
         "step_frac_hbm": round(value / HBM_PEAK_GBS, 4),
         "prefill": prefill,
+        "rmsnorm": rmsnorm,
         "quantizer": {"GB_per_s": round(q_bytes / min(qtimes) / 1e9, 1),
                       "elements": q_elems, "bytes_per_elem": 2.5625},
         "cpu_baseline": cpu,

@@ -131,6 +131,26 @@ QERL_API qerl_status qerl_aqn_sample(uint64_t seed, uint64_t stream_id,
                             float* z_out, void* stream);
 
 /*
+ * qerl_rmsnorm_noisy -- the noisy RMSNorm that produces a linear layer's
+ * input [QeRL summary, §3.4 "Noise Merging", Eq. 10]:
+ *     y[i, j] = bf16( (w_j + z_j) * x[i, j] / sqrt(mean_j' x[i, j']^2 + delta) )
+ * The AQN noise z is added to the RMSNorm scale w, which multiplies the
+ * normalised channel j by (1 + z_j / w_j) (Eq. 11); the layer that reads y
+ * then runs with no noise of its own (z == NULL there).  The sum of squares
+ * and the scaling are computed in fp32; y is rounded to nearest even.
+ *   x      device, [m, d] bf16 rows, 16-byte aligned
+ *   m      >= 1 rows
+ *   d      >= 8, d % 8 == 0 (the normalised dimension)
+ *   w      device, [d] bf16 RMSNorm scale, 16-byte aligned
+ *   z      device, [d] float noise, 16-byte aligned; NULL means no noise
+ *   delta  >= 0 and finite (a row of zeros with delta == 0 gives NaN)
+ *   y      device out, [m, d] bf16, 16-byte aligned; may be x itself
+ */
+QERL_API qerl_status qerl_rmsnorm_noisy(const void* x, int64_t m, int64_t d,
+                                        const void* w, const float* z, float delta,
+                                        void* y, void* stream);
+
+/*
  * qerl_linear_workspace_bytes -- bytes of device workspace that
  * qerl_linear_decode / qerl_linear_prefill / qerl_linear_prepare need for
  * these sizes on the current device.  0 if the sizes are invalid.  The

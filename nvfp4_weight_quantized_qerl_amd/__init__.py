@@ -83,6 +83,18 @@ def qerl_aqn_sample(seed, stream_id, call_id, sigma, d, device="cuda", out=None,
     return z
 
 
+def qerl_rmsnorm_noisy(x, w, z=None, delta=1e-6, out=None):
+    """y = bf16((w + z) * x / sqrt(mean(x^2) + delta)) per row of x [m, d]."""
+    x = _bits16(x, "x")
+    w = _bits16(w, "w")
+    m, d = x.shape
+    if out is None:
+        out = torch.empty((m, d), dtype=torch.bfloat16, device=x.device)
+    _check(lib.qerl_rmsnorm_noisy(_ptr(x), m, d, _ptr(w), _ptr(z), float(delta), _ptr(out),
+                                  _stream(x.device)), "qerl_rmsnorm_noisy")
+    return out
+
+
 def qerl_linear_workspace_bytes(m, n, k, r):
     return int(lib.qerl_linear_workspace_bytes(m, n, k, r))
 

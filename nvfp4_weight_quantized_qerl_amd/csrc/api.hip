@@ -55,7 +55,7 @@ const char* qerl_status_string(int status) {
   }
 }
 
-int qerl_abi_version(void) { return 2; }
+int qerl_abi_version(void) { return 3; }
 
 qerl_status qerl_quantize_nvfp4(const void* w_bf16, int64_t n, int64_t k, void* codes,
                                 void* scales, float* gscale, int32_t* nonfinite_flag,
@@ -97,6 +97,18 @@ qerl_status qerl_aqn_sample(uint64_t seed, uint64_t stream_id, uint64_t call_id,
   if (!aligned(z_out, 4)) return QERL_ERR_ALIGN;
   return from_hip(qerl::launch_aqn_sample(seed, stream_id, call_id, sigma, d, z_out,
                                           static_cast<hipStream_t>(stream)));
+}
+
+qerl_status qerl_rmsnorm_noisy(const void* x, int64_t m, int64_t d, const void* w,
+                               const float* z, float delta, void* y, void* stream) {
+  if (!x || !w || !y) return QERL_ERR_NULL;
+  if (m < 1 || d < 8 || d % 8) return QERL_ERR_SHAPE;
+  if (!(delta >= 0.0f) || !std::isfinite(delta)) return QERL_ERR_RANGE;
+  if (!aligned(x, 16) || !aligned(w, 16) || !aligned(y, 16) || (z && !aligned(z, 16)))
+    return QERL_ERR_ALIGN;
+  return from_hip(qerl::launch_rmsnorm_noisy(
+      static_cast<const uint16_t*>(x), m, d, static_cast<const uint16_t*>(w), z, delta,
+      static_cast<uint16_t*>(y), static_cast<hipStream_t>(stream)));
 }
 
 size_t qerl_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t r) {

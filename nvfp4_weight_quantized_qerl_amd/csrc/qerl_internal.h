@@ -22,6 +22,11 @@ hipError_t launch_aqn_sample(uint64_t seed, uint64_t stream_id,
                              uint64_t call_id, double sigma, int64_t d,
                              float* z, hipStream_t stream);
 
+// ------------------------------------------------------------------ rmsnorm
+// y = bf16((w + z) * x / sqrt(mean(x^2) + delta)) per row of x [m, d].
+hipError_t launch_rmsnorm_noisy(const uint16_t* x, int64_t m, int64_t d, const uint16_t* w,
+                                const float* z, float delta, uint16_t* y, hipStream_t stream);
+
 // ------------------------------------------------------------------- linear
 // Workspace layout and launch shapes for one (m, n, k, r).
 struct LinearPlan {

@@ -41,7 +41,7 @@ def test_status_strings():
     for s in range(7):
         assert lib.qerl_status_string(s).decode().startswith("QERL_")
     assert b"unknown" in lib.qerl_status_string(99)
-    assert lib.qerl_abi_version() == 2
+    assert lib.qerl_abi_version() == 3
 
 
 FAKE = ctypes.c_void_p(0x10000)        # aligned, never dereferenced on error
@@ -83,6 +83,22 @@ def test_sample_validation():
     assert f(0, 0, 0, -0.01, 16, FAKE, None) == 4
     assert f(0, 0, 0, float("nan"), 16, FAKE, None) == 4
     assert f(0, 0, 0, 0.01, 16, ctypes.c_void_p(0x10002), None) == 3
+
+
+def test_rmsnorm_validation():
+    f = lib.qerl_rmsnorm_noisy
+    assert f(None, 4, 64, FAKE, None, 1e-6, FAKE, None) == 1
+    assert f(FAKE, 4, 64, None, None, 1e-6, FAKE, None) == 1
+    assert f(FAKE, 4, 64, FAKE, None, 1e-6, None, None) == 1
+    assert f(FAKE, 0, 64, FAKE, None, 1e-6, FAKE, None) == 2
+    assert f(FAKE, 4, 4, FAKE, None, 1e-6, FAKE, None) == 2
+    assert f(FAKE, 4, 60, FAKE, None, 1e-6, FAKE, None) == 2
+    assert f(FAKE, 4, 64, FAKE, None, -1.0, FAKE, None) == 4
+    assert f(FAKE, 4, 64, FAKE, None, float("inf"), FAKE, None) == 4
+    assert f(MIS, 4, 64, FAKE, None, 1e-6, FAKE, None) == 3
+    assert f(FAKE, 4, 64, MIS, None, 1e-6, FAKE, None) == 3
+    assert f(FAKE, 4, 64, FAKE, MIS, 1e-6, FAKE, None) == 3
+    assert f(FAKE, 4, 64, FAKE, None, 1e-6, MIS, None) == 3
 
 
 def test_workspace_sizes():
