@@ -29,96 +29,79 @@ struct FinishArgs {
   const uint16_t* __restrict__ lora_b;  // [n, r] bf16
   uint16_t* __restrict__ y;             // [m_valid, n] rows of this chunk
   int64_t n;
-  int split, rows, m_valid, r, rpad16, lora_vec, vec4;
+  int split, rows, m_valid, r, rpad16, lora_vec;
 };
 
-constexpr int kFinishBatch = 16;   // partial sums loaded together per thread
+constexpr int kFinishBatch = 8;    // splits whose partial sums a lane loads together
+
+// LoRA B operand of one MFMA step: B[col, j0 .. j0 + 7] (zeros past r or
+// past the last column).
+__device__ __forceinline__ uint4 finish_b(const FinishArgs& a, int64_t col, int j0) {
+  if (col >= a.n || j0 >= a.r) return make_uint4(0u, 0u, 0u, 0u);
+  const uint16_t* src = a.lora_b + col * a.r + j0;
+  if (a.lora_vec) return *reinterpret_cast<const uint4*>(src);
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t lo = (j0 + 2 * i < a.r) ? src[2 * i] : 0u;
+    const uint32_t hi = (j0 + 2 * i + 1 < a.r) ? src[2 * i + 1] : 0u;
+    w[i] = lo | (hi << 16);
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
 
 // y[m, j] = bf16(S * sum_s ypart[s, m, j] + sum_i t[m, i] B[j, i]): the
 // epilogue of a split-K contraction [QeRL summary, §3.4, Eq. 6 (S) and
-// Eq. 2 (LoRA side branch)].  The splits are summed in split order, then
-// scaled, then the LoRA term is added in i order.  One thread per token row
-// and four consecutive columns; every load of a thread is independent of
-// the others, so a thread waits about one memory latency per batch of
-// kFinishBatch splits.
+// Eq. 2 (LoRA side branch)].  One wave per 32 x 32 output tile (32 token
+// rows x 32 columns), held in the 32x32x16 MFMA accumulator layout: lane l
+// owns column l % 32 of the tile.  The splits are summed in split order
+// (all loads of a batch of kFinishBatch splits issued first, each load two
+// rows x 128 bytes), then scaled by S, then t B^T is added by MFMAs whose
+// operands are read straight from t and B, so B is read once per 32 token
+// rows.
 __global__ __launch_bounds__(256) void splitk_finish(FinishArgs a) {
-  const int64_t groups = (a.n + 3) / 4;
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= groups * a.m_valid) return;
-  const int m = (int)(idx / groups);
-  const int64_t col = (idx - (int64_t)m * groups) * 4;
-  const int ncol = (int)min<int64_t>(4, a.n - col);
-  const bool vec = a.vec4 && ncol == 4;
-  const float* src = a.ypart + (int64_t)m * a.n + col;
+  const int lane = threadIdx.x & 63, c = lane & 31, h = lane >> 5;
+  const int64_t ctiles = (a.n + 31) / 32;
+  const int64_t tile = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (tile >= ctiles * (a.rows / 32)) return;
+  const int u = (int)(tile / ctiles);              // token tile
+  const int64_t col = (tile - (int64_t)u * ctiles) * 32 + c;
+  const bool live = col < a.n;
   const int64_t sstride = (int64_t)a.rows * a.n;
-  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  const float* src = a.ypart + (int64_t)(32 * u) * a.n + col;
+  f32x16_t acc = zero16();
   for (int s0 = 0; s0 < a.split; s0 += kFinishBatch) {
-    float4 part[kFinishBatch];
+    const int nb = min(kFinishBatch, a.split - s0);
+    float part[kFinishBatch][16];
 #pragma unroll
-    for (int u = 0; u < kFinishBatch; ++u) {
-      part[u] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-      if (s0 + u < a.split) {
-        const float* ps = src + (int64_t)(s0 + u) * sstride;
-        if (vec) {
-          part[u] = *reinterpret_cast<const float4*>(ps);
-        } else {
-          part[u].x = ps[0];
-          if (ncol > 1) part[u].y = ps[1];
-          if (ncol > 2) part[u].z = ps[2];
-          if (ncol > 3) part[u].w = ps[3];
-        }
-      }
-    }
+    for (int b = 0; b < kFinishBatch; ++b)
 #pragma unroll
-    for (int u = 0; u < kFinishBatch; ++u) {
-      if (s0 + u < a.split) {
-        acc[0] += part[u].x;
-        acc[1] += part[u].y;
-        acc[2] += part[u].z;
-        acc[3] += part[u].w;
-      }
-    }
+      for (int v = 0; v < 16; ++v)
+        part[b][v] = (b < nb && live)
+                         ? src[(int64_t)(s0 + b) * sstride + (int64_t)acc_row(v, lane) * a.n]
+                         : 0.0f;
+#pragma unroll
+    for (int b = 0; b < kFinishBatch; ++b)
+      if (b < nb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[v] += part[b][v];
   }
   const float S = *a.gscale;
 #pragma unroll
-  for (int c = 0; c < 4; ++c) acc[c] *= S;
+  for (int v = 0; v < 16; ++v) acc[v] *= S;
   if (a.r > 0) {
-    const uint16_t* trow = a.t + (int64_t)m * a.rpad16;
-#pragma unroll 4
-    for (int i0 = 0; i0 < a.r; i0 += 8) {
-      // t[m, i0 .. i0+7] (t is padded to rpad16 columns with zeros)
-      const uint4 tv = *reinterpret_cast<const uint4*>(trow + i0);
-      const float tf[8] = {bf16_to_f32(tv.x & 0xffffu), bf16_to_f32(tv.x >> 16),
-                           bf16_to_f32(tv.y & 0xffffu), bf16_to_f32(tv.y >> 16),
-                           bf16_to_f32(tv.z & 0xffffu), bf16_to_f32(tv.z >> 16),
-                           bf16_to_f32(tv.w & 0xffffu), bf16_to_f32(tv.w >> 16)};
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        if (c >= ncol) break;
-        const uint16_t* brow = a.lora_b + (col + c) * a.r + i0;
-        float bf[8];
-        if (a.lora_vec) {
-          const uint4 bv = *reinterpret_cast<const uint4*>(brow);
-          const uint32_t bw[4] = {bv.x, bv.y, bv.z, bv.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            bf[2 * e] = bf16_to_f32(bw[e] & 0xffffu);
-            bf[2 * e + 1] = bf16_to_f32(bw[e] >> 16);
-          }
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) bf[e] = i0 + e < a.r ? bf16_to_f32(brow[e]) : 0.0f;
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[c] += tf[e] * bf[e];
-      }
+    // A operand: t[32 u + c, j0 + 8 h .. +7] (t has rpad16 zero-padded columns).
+    const uint16_t* trow = a.t + (int64_t)(32 * u + c) * a.rpad16 + 8 * h;
+    for (int j0 = 0; j0 < a.rpad16; j0 += 16) {
+      const uint4 tv = *reinterpret_cast<const uint4*>(trow + j0);
+      acc = mfma_bf16(tv, finish_b(a, col, j0 + 8 * h), acc);
     }
   }
-  uint16_t* dst = a.y + (int64_t)m * a.n + col;
-  if (vec) {
-    *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]));
-  } else {
-    for (int c = 0; c < ncol; ++c) dst[c] = f32_to_bf16_bits(acc[c]);
+  if (!live) return;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int m = 32 * u + acc_row(v, lane);
+    if (m < a.m_valid) a.y[(int64_t)m * a.n + col] = f32_to_bf16_bits(acc[v]);
   }
 }
 
@@ -139,10 +122,8 @@ hipError_t launch_finish(const LinearPlan& p, int split, int rows, int m_valid,
   f.r = r;
   f.rpad16 = p.rpad16;
   f.lora_vec = lora_vec;
-  f.vec4 = p.n % 4 == 0 && (reinterpret_cast<uintptr_t>(y) & 7) == 0;
-  const int64_t threads = (p.n + 3) / 4 * m_valid;
-  hipLaunchKernelGGL(splitk_finish, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
-                     stream, f);
+  const int64_t tiles = (p.n + 31) / 32 * (rows / 32);
+  hipLaunchKernelGGL(splitk_finish, dim3((unsigned)((tiles + 3) / 4)), dim3(256), 0, stream, f);
   return hipGetLastError();
 }
 

@@ -103,17 +103,19 @@ __device__ __forceinline__ uint4 load_lora_b(const Args& a, int64_t row, bool li
 __device__ __forceinline__ void epilogue_tile(const Args& a, f32x16_t acc, float S, int u,
                                               int64_t row, bool live, int lane,
                                               const uint16_t* t_lds, int64_t row_end,
-                                              uint16_t* scratch, const uint4* bpre) {
+                                              uint16_t* scratch, bool b_pre, uint4 b0,
+                                              uint4 b1) {
   const int h = lane >> 5, c = lane & 31;
 #pragma unroll
   for (int v = 0; v < 16; ++v) acc[v] *= S;
   if (a.r > 0) {
     const uint16_t* trow = t_lds + (32 * u + c) * a.rpad16;
-    if (bpre) {
-      // r <= 32, B loaded ahead (bpre[1] is zero when r <= 16).
-      acc = mfma_bf16(*reinterpret_cast<const uint4*>(trow + 8 * h), bpre[0], acc);
+    if (b_pre) {
+      // r <= 32, B loaded ahead (b1 is zero when r <= 16).  The operands come
+      // by value: an array whose address is taken would live in scratch.
+      acc = mfma_bf16(*reinterpret_cast<const uint4*>(trow + 8 * h), b0, acc);
       if (a.rpad16 > 16)
-        acc = mfma_bf16(*reinterpret_cast<const uint4*>(trow + 16 + 8 * h), bpre[1], acc);
+        acc = mfma_bf16(*reinterpret_cast<const uint4*>(trow + 16 + 8 * h), b1, acc);
     } else {
       for (int j0 = 0; j0 < a.rpad16; j0 += 16) {
         const uint4 tv = *reinterpret_cast<const uint4*>(trow + j0 + 8 * h);
@@ -364,7 +366,7 @@ __global__ __launch_bounds__(512, 1) void decode_lds(Args a) {
     for (int p = 0; p < NT0 * MT; ++p)
       if (owns(p))
         epilogue_tile(a, acc[p / MT][p % MT], S, p % MT, tile_row(p), tile_live(p), lane, t_lds,
-                      row_end, scratch, b_pre ? bpre[p / TPR] : nullptr);
+                      row_end, scratch, b_pre, bpre[p / TPR][0], bpre[p / TPR][1]);
     return;
   }
 

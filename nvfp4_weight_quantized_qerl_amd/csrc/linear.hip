@@ -49,8 +49,8 @@ constexpr int64_t kPrepChunk = 512;
 
 // Largest weight subtile count NT per wave that the decode kernels hold in
 // registers without spilling, for MT token tiles (from the compiler's
-// resource report).
-int decode_nt_max(int mt) { return mt == 1 ? 6 : (mt == 2 ? 5 : 3); }
+// resource report: the general kernel spills at MT = 4, NT = 3).
+int decode_nt_max(int mt) { return mt == 1 ? 6 : (mt == 2 ? 5 : 2); }
 
 // Decode rows per workgroup and split-K choice for one m tile count.
 void plan_decode(LinearPlan* p, int mt) {
@@ -112,7 +112,11 @@ bool make_linear_plan(int64_t m, int64_t n, int64_t k, int r, LinearPlan* p) {
   p->kchunks = (int)cdiv(k, kPrepChunk);
   // Token tiles per decode launch: 1, 2 or 4 (the instantiated kernels);
   // run_decode_chunks takes smaller chunks for the remainder.
-  const int mt = mtiles >= 4 ? 4 : (mtiles >= 2 ? 2 : 1);
+  // With k % 256 == 0 the LDS-staged kernel (up to two tiles) is used even
+  // for more rows, one 64-row chunk after the other: it streams the weights
+  // fast enough that two passes beat one pass of the general kernel.
+  const int mt_cap = k % 256 == 0 ? 2 : 4;
+  const int mt = std::min(mt_cap, mtiles >= 4 ? 4 : (mtiles >= 2 ? 2 : 1));
   plan_decode(p, mt);
   p->pf_tile_m = 128;
   p->pf_tile_n = 128;
