@@ -112,6 +112,30 @@ QERL_API qerl_status qerl_aqn_sigma(double sigma_start, double sigma_end,
                            int32_t num_stages, int32_t stage,
                            double* sigma_out);
 
+/* Decay schedules of qerl_aqn_sigma_schedule. */
+typedef enum {
+  QERL_SCHEDULE_EXPONENTIAL = 0, /* Eq. 8, as qerl_aqn_sigma              */
+  QERL_SCHEDULE_LINEAR = 1,
+  QERL_SCHEDULE_COSINE = 2,
+  QERL_SCHEDULE_LOGARITHMIC = 3
+} qerl_schedule;
+
+/*
+ * qerl_aqn_sigma_schedule -- host, pure.  sigma at stage k under one of the
+ * four decay schedules the pages compare [QeRL summary, §3.4, "Why
+ * exponential decay" (Fig. 9, Fig. 15)], with t = (k-1)/(K-1):
+ *   EXPONENTIAL  sigma_start (sigma_end / sigma_start)^t          (Eq. 8)
+ *   LINEAR       sigma_start - (sigma_start - sigma_end) t
+ *   COSINE       sigma_end + (sigma_start - sigma_end)(1 + cos(pi t)) / 2
+ *   LOGARITHMIC  sigma_start - (sigma_start - sigma_end) ln(k) / ln(K)
+ * Stage 0 gives 0 and K == 1 gives sigma_start, as for qerl_aqn_sigma.
+ *   mode       a qerl_schedule value (else QERL_ERR_RANGE)
+ *   other arguments and errors as qerl_aqn_sigma
+ */
+QERL_API qerl_status qerl_aqn_sigma_schedule(int32_t mode, double sigma_start,
+                                             double sigma_end, int32_t num_stages,
+                                             int32_t stage, double* sigma_out);
+
 /*
  * qerl_aqn_sample -- the AQN noise vector z ~ N(0, sigma^2 I) of length
  * d (= the layer's input dimension) [QeRL summary, §3.4, Eq. 7], drawn

@@ -74,6 +74,17 @@ def qerl_aqn_sigma(sigma_start, sigma_end, num_stages, stage):
     return out.value
 
 
+SCHEDULES = {"exponential": 0, "linear": 1, "cosine": 2, "logarithmic": 3}
+
+
+def qerl_aqn_sigma_schedule(mode, sigma_start, sigma_end, num_stages, stage):
+    """sigma at stage k of K under the named decay schedule (host)."""
+    out = ctypes.c_double()
+    _check(lib.qerl_aqn_sigma_schedule(SCHEDULES[mode], sigma_start, sigma_end, num_stages,
+                                       stage, ctypes.byref(out)), "qerl_aqn_sigma_schedule")
+    return out.value
+
+
 def qerl_aqn_sample(seed, stream_id, call_id, sigma, d, device="cuda", out=None, stream=None):
     """stream: a torch.cuda.Stream to enqueue on (default: the current one)."""
     z = out if out is not None else torch.empty(d, dtype=torch.float32, device=device)

@@ -55,7 +55,7 @@ const char* qerl_status_string(int status) {
   }
 }
 
-int qerl_abi_version(void) { return 3; }
+int qerl_abi_version(void) { return 4; }
 
 qerl_status qerl_quantize_nvfp4(const void* w_bf16, int64_t n, int64_t k, void* codes,
                                 void* scales, float* gscale, int32_t* nonfinite_flag,
@@ -85,6 +85,40 @@ qerl_status qerl_aqn_sigma(double sigma_start, double sigma_end, int32_t num_sta
     const double ratio = sigma_end / sigma_start;
     *sigma_out = sigma_start *
                  std::pow(ratio, (double)(stage - 1) / (double)(num_stages - 1));
+  }
+  return QERL_OK;
+}
+
+qerl_status qerl_aqn_sigma_schedule(int32_t mode, double sigma_start, double sigma_end,
+                                    int32_t num_stages, int32_t stage, double* sigma_out) {
+  if (!sigma_out) return QERL_ERR_NULL;
+  if (mode < QERL_SCHEDULE_EXPONENTIAL || mode > QERL_SCHEDULE_LOGARITHMIC)
+    return QERL_ERR_RANGE;
+  if (mode == QERL_SCHEDULE_EXPONENTIAL)
+    return qerl_aqn_sigma(sigma_start, sigma_end, num_stages, stage, sigma_out);
+  if (!(sigma_start > 0.0) || !(sigma_end > 0.0) || !std::isfinite(sigma_start) ||
+      !std::isfinite(sigma_end) || num_stages < 1 || stage < 0 || stage > num_stages)
+    return QERL_ERR_RANGE;
+  if (stage == 0) {
+    *sigma_out = 0.0;
+    return QERL_OK;
+  }
+  if (num_stages == 1) {
+    *sigma_out = sigma_start;
+    return QERL_OK;
+  }
+  const double frac = (double)(stage - 1) / (double)(num_stages - 1);
+  const double drop = sigma_start - sigma_end;
+  switch (mode) {
+    case QERL_SCHEDULE_LINEAR:
+      *sigma_out = sigma_start - drop * frac;
+      break;
+    case QERL_SCHEDULE_COSINE:
+      *sigma_out = sigma_end + 0.5 * drop * (1.0 + std::cos(M_PI * frac));
+      break;
+    default:  // QERL_SCHEDULE_LOGARITHMIC
+      *sigma_out = sigma_start - drop * (std::log((double)stage) / std::log((double)num_stages));
+      break;
   }
   return QERL_OK;
 }

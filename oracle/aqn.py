@@ -58,6 +58,41 @@ def sigma(sigma_start, sigma_end, num_stages, stage):
     return sigma_start * ratio ** ((stage - 1) / (num_stages - 1))
 
 
+SCHEDULES = ("exponential", "linear", "cosine", "logarithmic")
+
+
+def sigma_schedule(mode, sigma_start, sigma_end, num_stages, stage):
+    """sigma at stage k under one of the four decay schedules the pages
+    compare [QeRL summary, §3.4, "Why exponential decay" (Fig. 9, Fig. 15)];
+    with t = (k - 1) / (K - 1):
+      exponential  sigma_start (sigma_end / sigma_start)^t          (Eq. 8)
+      linear       sigma_start - (sigma_start - sigma_end) t
+      cosine       sigma_end + (sigma_start - sigma_end) (1 + cos(pi t)) / 2
+      logarithmic  sigma_start - (sigma_start - sigma_end) log(k) / log(K)
+    sigma(0) = 0 and K = 1 gives sigma_start, as for Eq. 8."""
+    if mode not in SCHEDULES:
+        raise ValueError(f"unknown schedule {mode!r}")
+    if mode == "exponential":
+        return sigma(sigma_start, sigma_end, num_stages, stage)
+    sigma_start, sigma_end = float(sigma_start), float(sigma_end)
+    num_stages, stage = int(num_stages), int(stage)
+    if num_stages < 1 or not 0 <= stage <= num_stages:
+        raise ValueError("need K >= 1 and 0 <= k <= K")
+    if not (sigma_start > 0 and sigma_end > 0):
+        raise ValueError("sigma_start and sigma_end must be positive")
+    if stage == 0:
+        return 0.0
+    if num_stages == 1:
+        return sigma_start
+    t = (stage - 1) / (num_stages - 1)
+    span = sigma_start - sigma_end
+    if mode == "linear":
+        return sigma_start - span * t
+    if mode == "cosine":
+        return sigma_end + 0.5 * span * (1.0 + math.cos(math.pi * t))
+    return sigma_start - span * math.log(stage) / math.log(num_stages)
+
+
 def _mulhilo(a, b):
     p = a * b
     return (p >> 64) & MASK64, p & MASK64

@@ -41,7 +41,7 @@ def test_status_strings():
     for s in range(7):
         assert lib.qerl_status_string(s).decode().startswith("QERL_")
     assert b"unknown" in lib.qerl_status_string(99)
-    assert lib.qerl_abi_version() == 3
+    assert lib.qerl_abi_version() == 4
 
 
 FAKE = ctypes.c_void_p(0x10000)        # aligned, never dereferenced on error
@@ -74,6 +74,23 @@ def test_sigma_matches_oracle_and_validates():
     assert lib.qerl_aqn_sigma(1e-2, 5e-4, 0, 0, ctypes.byref(out)) == 4
     assert lib.qerl_aqn_sigma(1e-2, 5e-4, 10, 1, None) == 1
     assert q.qerl_aqn_sigma(1e-2, 5e-4, 10, 1) == 1e-2
+
+
+def test_sigma_schedules_match_oracle_and_validate():
+    for mode in aqn.SCHEDULES:
+        for K in (1, 2, 3, 10, 37):
+            for k in range(K + 1):
+                got = q.qerl_aqn_sigma_schedule(mode, 1e-2, 5e-4, K, k)
+                want = aqn.sigma_schedule(mode, 1e-2, 5e-4, K, k)
+                # a difference of terms of size sigma_start: a few ulps of it
+                assert abs(got - want) <= 1e-15 * 1e-2, (mode, K, k, got, want)
+    out = ctypes.c_double()
+    f = lib.qerl_aqn_sigma_schedule
+    assert f(4, 1e-2, 5e-4, 10, 1, ctypes.byref(out)) == 4
+    assert f(-1, 1e-2, 5e-4, 10, 1, ctypes.byref(out)) == 4
+    assert f(1, 1e-2, 5e-4, 10, 11, ctypes.byref(out)) == 4
+    assert f(2, 0.0, 5e-4, 10, 1, ctypes.byref(out)) == 4
+    assert f(3, 1e-2, 5e-4, 10, 1, None) == 1
 
 
 def test_sample_validation():

@@ -115,3 +115,45 @@ def test_sample_is_sigma_times_normal_in_fp32():
     assert z.dtype == np.float32
     assert np.array_equal(z, (sig * n).astype(np.float32))
     assert np.all(aqn.sample(0, 0, 0, 0.0, 256) == 0.0)
+
+
+# ---- the four decay schedules compared on the pages (linear, exponential,
+# cosine, logarithmic) [QeRL summary, §3.4, "Why exponential decay"]
+
+def test_every_schedule_runs_from_start_to_end():
+    for mode in aqn.SCHEDULES:
+        for K in (2, 5, 10):
+            assert aqn.sigma_schedule(mode, 1e-2, 5e-4, K, 1) == pytest.approx(1e-2, rel=1e-15)
+            assert aqn.sigma_schedule(mode, 1e-2, 5e-4, K, K) == pytest.approx(5e-4, rel=1e-13)
+            assert aqn.sigma_schedule(mode, 1e-2, 5e-4, K, 0) == 0.0
+        assert aqn.sigma_schedule(mode, 1e-2, 5e-4, 1, 1) == 1e-2
+
+
+def test_schedules_decrease_monotonically():
+    for mode in aqn.SCHEDULES:
+        vals = [aqn.sigma_schedule(mode, 1e-2, 5e-4, 10, k) for k in range(1, 11)]
+        assert all(a > b for a, b in zip(vals, vals[1:])), mode
+
+
+def test_schedule_midpoints():
+    s0, s1 = 1e-2, 5e-4
+    mean = 0.5 * (s0 + s1)
+    # K = 9: stage 5 is half way in t = (k-1)/(K-1); linear and cosine pass
+    # through the arithmetic mean there, exponential through the geometric
+    # mean; the logarithmic schedule is half way at k = 3 (ln 3 / ln 9 = 1/2).
+    assert aqn.sigma_schedule("linear", s0, s1, 9, 5) == pytest.approx(mean, rel=1e-15)
+    assert aqn.sigma_schedule("cosine", s0, s1, 9, 5) == pytest.approx(mean, rel=1e-15)
+    assert aqn.sigma_schedule("exponential", s0, s1, 9, 5) == pytest.approx((s0 * s1) ** 0.5, rel=1e-14)
+    assert aqn.sigma_schedule("logarithmic", s0, s1, 9, 3) == pytest.approx(mean, rel=1e-14)
+
+
+def test_linear_schedule_steps_are_equal_and_log_drops_fastest():
+    lin = [aqn.sigma_schedule("linear", 1e-2, 5e-4, 10, k) for k in range(1, 11)]
+    steps = [a - b for a, b in zip(lin, lin[1:])]
+    assert max(steps) - min(steps) < 1e-17
+    assert steps[0] == pytest.approx((1e-2 - 5e-4) / 9, rel=1e-12)
+    # the first step is largest for the logarithmic schedule (sharp initial drop)
+    first = {m: 1e-2 - aqn.sigma_schedule(m, 1e-2, 5e-4, 10, 2) for m in aqn.SCHEDULES}
+    assert max(first, key=first.get) == "logarithmic"
+    # the cosine schedule starts flat: its first step is the smallest
+    assert min(first, key=first.get) == "cosine"
