@@ -46,12 +46,14 @@ def parse():
     ap.add_argument("--copies", type=int, default=6)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
-    ap.add_argument("--profile", nargs="?", const="decode", choices=("decode", "prefill"),
+    ap.add_argument("--profile", nargs="?", const="decode", choices=("decode", "prefill", "rmsnorm"),
                     help="profiling pass for rocprofv3, no timing and no JSON line: "
                          "'decode' runs one plain device copy of COPY_BYTES (counter "
                          "calibration) and PROFILE_LAUNCHES gate/up decode contractions; "
                          "'prefill' runs one prepare and three prefill GEMMs on each of "
-                         "the 7B qkv and down layers at M=4096")
+                         "the 7B qkv and down layers at M=4096; 'rmsnorm' runs one "
+                         "plain device copy (counter calibration) and 20 noisy RMSNorms "
+                         "of 4096 x 3584 rows on rotated inputs")
     return ap.parse_args()
 
 
@@ -131,6 +133,28 @@ def profile_prefill(q, pc, make_layer, to_dev, dev):
     print("profile pass done: prefill_7b qkv and down, 3 GEMMs each")
 
 
+def profile_rmsnorm(q, to_dev, dev, m=4096, d=3584, copies=10, launches=20):
+    """Profiling pass of the noisy RMSNorm: one plain copy of COPY_BYTES
+    (counter calibration), then `launches` calls on rotated input copies."""
+    import torch
+    from workloads import norm_inputs
+    src = torch.empty(COPY_BYTES // 2, dtype=torch.int16, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    x, w = norm_inputs(m, d, seed=31)
+    wd = to_dev(w)
+    xs = [to_dev(x) for _ in range(copies)]
+    ys = [torch.empty_like(xs[0]) for _ in range(copies)]
+    z = q.qerl_aqn_sample(31, 0, 0, 1e-2, d, device=dev)
+    for i in range(launches):
+        q.qerl_rmsnorm_noisy(xs[i % copies], wd, z, 1e-6, out=ys[i % copies])
+    torch.cuda.synchronize()
+    print(f"profile pass done: copy {COPY_BYTES} B, {launches} noisy RMSNorms {m}x{d}")
+
+
 def oracle_step_rate(cfg, layers, M, R, min_seconds=10.0, max_reps=20):
     """The oracle running the decode step on the host: per layer, sample z,
     dequantize the NVFP4 weight and evaluate the fp64 linear layer with the
@@ -193,6 +217,9 @@ def main():
 
     if args.profile == "prefill":
         profile_prefill(q, CONFIGS["prefill_7b"], make_layer, to_dev, dev)
+        return
+    if args.profile == "rmsnorm":
+        profile_rmsnorm(q, to_dev, dev)
         return
 
     cfg = CONFIGS["decode_7b_mlp"]

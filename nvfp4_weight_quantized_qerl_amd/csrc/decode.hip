@@ -32,7 +32,7 @@ struct FinishArgs {
   int split, rows, m_valid, r, rpad16, lora_vec;
 };
 
-constexpr int kFinishBatch = 8;    // splits whose partial sums a lane loads together
+constexpr int kFinishBatch = 16;   // splits whose partial sums a thread loads together
 
 // LoRA B operand of one MFMA step: B[col, j0 .. j0 + 7] (zeros past r or
 // past the last column).
@@ -52,56 +52,92 @@ __device__ __forceinline__ uint4 finish_b(const FinishArgs& a, int64_t col, int 
 
 // y[m, j] = bf16(S * sum_s ypart[s, m, j] + sum_i t[m, i] B[j, i]): the
 // epilogue of a split-K contraction [QeRL summary, §3.4, Eq. 6 (S) and
-// Eq. 2 (LoRA side branch)].  One wave per 32 x 32 output tile (32 token
-// rows x 32 columns), held in the 32x32x16 MFMA accumulator layout: lane l
-// owns column l % 32 of the tile.  The splits are summed in split order
-// (all loads of a batch of kFinishBatch splits issued first, each load two
-// rows x 128 bytes), then scaled by S, then t B^T is added by MFMAs whose
-// operands are read straight from t and B, so B is read once per 32 token
-// rows.
+// Eq. 2 (LoRA side branch)].  One workgroup per 32 x 32 output tile (32
+// token rows x 32 columns).  First every thread sums the splits of one
+// token row and four columns in split order (16-byte loads, kFinishBatch
+// splits in flight) into an LDS copy of the tile; then wave 0 reads the
+// tile in the 32x32x16 MFMA accumulator layout (lane l: column l % 32),
+// scales it by S and adds t B^T with MFMAs whose operands it loaded at the
+// start, so B is read once per 32 token rows.
 __global__ __launch_bounds__(256) void splitk_finish(FinishArgs a) {
+  __shared__ float sums[32][33];
   const int lane = threadIdx.x & 63, c = lane & 31, h = lane >> 5;
+  const int wave = threadIdx.x >> 6;
   const int64_t ctiles = (a.n + 31) / 32;
-  const int64_t tile = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (tile >= ctiles * (a.rows / 32)) return;
-  const int u = (int)(tile / ctiles);              // token tile
-  const int64_t col = (tile - (int64_t)u * ctiles) * 32 + c;
-  const bool live = col < a.n;
-  const int64_t sstride = (int64_t)a.rows * a.n;
-  const float* src = a.ypart + (int64_t)(32 * u) * a.n + col;
-  f32x16_t acc = zero16();
-  for (int s0 = 0; s0 < a.split; s0 += kFinishBatch) {
-    const int nb = min(kFinishBatch, a.split - s0);
-    float part[kFinishBatch][16];
-#pragma unroll
-    for (int b = 0; b < kFinishBatch; ++b)
-#pragma unroll
-      for (int v = 0; v < 16; ++v)
-        part[b][v] = (b < nb && live)
-                         ? src[(int64_t)(s0 + b) * sstride + (int64_t)acc_row(v, lane) * a.n]
-                         : 0.0f;
-#pragma unroll
-    for (int b = 0; b < kFinishBatch; ++b)
-      if (b < nb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[v] += part[b][v];
-  }
-  const float S = *a.gscale;
-#pragma unroll
-  for (int v = 0; v < 16; ++v) acc[v] *= S;
-  if (a.r > 0) {
-    // A operand: t[32 u + c, j0 + 8 h .. +7] (t has rpad16 zero-padded columns).
+  const int u = (int)(blockIdx.x / ctiles);                  // token tile
+  const int64_t col0 = (int64_t)(blockIdx.x - (int64_t)u * ctiles) * 32;
+
+  // LoRA operands of wave 0 (r <= 128: at most eight 16-wide steps).
+  uint4 tv[8], bv[8];
+  if (wave == 0 && a.r > 0) {
     const uint16_t* trow = a.t + (int64_t)(32 * u + c) * a.rpad16 + 8 * h;
-    for (int j0 = 0; j0 < a.rpad16; j0 += 16) {
-      const uint4 tv = *reinterpret_cast<const uint4*>(trow + j0);
-      acc = mfma_bf16(tv, finish_b(a, col, j0 + 8 * h), acc);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      tv[i] = make_uint4(0u, 0u, 0u, 0u);
+      bv[i] = make_uint4(0u, 0u, 0u, 0u);
+      if (16 * i < a.rpad16) {
+        tv[i] = *reinterpret_cast<const uint4*>(trow + 16 * i);
+        bv[i] = finish_b(a, col0 + c, 16 * i + 8 * h);
+      }
     }
   }
-  if (!live) return;
+
+  // Split sums: thread -> token row rr, columns cq .. cq + 3 of the tile.
+  const int rr = threadIdx.x >> 3, cq = 4 * (threadIdx.x & 7);
+  const int64_t col = col0 + cq;
+  const int ncol = (int)max<int64_t>(0, min<int64_t>(4, a.n - col));
+  const bool vec = ncol == 4 && a.n % 4 == 0;
+  const float* src = a.ypart + (int64_t)(32 * u + rr) * a.n + col;
+  const int64_t sstride = (int64_t)a.rows * a.n;
+  float4 acc4 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  for (int s0 = 0; s0 < a.split; s0 += kFinishBatch) {
+    float4 part[kFinishBatch];
+#pragma unroll
+    for (int b = 0; b < kFinishBatch; ++b) {
+      part[b] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      if (s0 + b < a.split) {
+        const float* ps = src + (int64_t)(s0 + b) * sstride;
+        if (vec) {
+          part[b] = *reinterpret_cast<const float4*>(ps);
+        } else {
+          if (ncol > 0) part[b].x = ps[0];
+          if (ncol > 1) part[b].y = ps[1];
+          if (ncol > 2) part[b].z = ps[2];
+          if (ncol > 3) part[b].w = ps[3];
+        }
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < kFinishBatch; ++b) {
+      if (s0 + b < a.split) {
+        acc4.x += part[b].x;
+        acc4.y += part[b].y;
+        acc4.z += part[b].z;
+        acc4.w += part[b].w;
+      }
+    }
+  }
+  sums[rr][cq] = acc4.x;
+  sums[rr][cq + 1] = acc4.y;
+  sums[rr][cq + 2] = acc4.z;
+  sums[rr][cq + 3] = acc4.w;
+  __syncthreads();
+  if (wave != 0) return;
+
+  const float S = *a.gscale;
+  f32x16_t acc;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc[v] = S * sums[acc_row(v, lane)][c];
+  if (a.r > 0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (16 * i < a.rpad16) acc = mfma_bf16(tv[i], bv[i], acc);
+  }
+  if (col0 + c >= a.n) return;
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
     const int m = 32 * u + acc_row(v, lane);
-    if (m < a.m_valid) a.y[(int64_t)m * a.n + col] = f32_to_bf16_bits(acc[v]);
+    if (m < a.m_valid) a.y[(int64_t)m * a.n + col0 + c] = f32_to_bf16_bits(acc[v]);
   }
 }
 
@@ -123,7 +159,7 @@ hipError_t launch_finish(const LinearPlan& p, int split, int rows, int m_valid,
   f.rpad16 = p.rpad16;
   f.lora_vec = lora_vec;
   const int64_t tiles = (p.n + 31) / 32 * (rows / 32);
-  hipLaunchKernelGGL(splitk_finish, dim3((unsigned)((tiles + 3) / 4)), dim3(256), 0, stream, f);
+  hipLaunchKernelGGL(splitk_finish, dim3((unsigned)tiles), dim3(256), 0, stream, f);
   return hipGetLastError();
 }
 
