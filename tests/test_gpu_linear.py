@@ -116,15 +116,24 @@ def test_zero_weight_gives_lora_only():
     assert linear.max_rel_error(g.run(), ref) <= TOL
 
 
-def test_deterministic_and_prepared_halves():
-    L = make_layer(64, 96, 8192, 32, seed=23, stage=1)
+@pytest.mark.parametrize("m,n,k,r", [
+    (64, 96, 8192, 32),      # K split: the finishing kernel forms t from the partials
+    (32, 16384, 512, 8),     # unsplit: the contraction kernel forms t
+    (50, 16384, 256, 16),    # ragged m, unsplit
+    (128, 96, 2048, 40),     # two 64-row chunks, r not a multiple of 16 or 32
+    (3, 96, 768, 8),         # one 32-row tile
+])
+def test_deterministic_and_prepared_halves(m, n, k, r):
+    # The whole call forms t inside the contraction (or the split-K finish)
+    # from the chunk partials; the prepared halves reduce it in a separate
+    # kernel first.  Both sum in the same order: the outputs are identical.
+    L = make_layer(m, n, k, r, seed=23, stage=1)
     g = GpuLayer(L)
     y1, y2 = g.run(), g.run()
     assert np.array_equal(y1, y2)
-    m, k = L.x.shape
-    ws = q.workspace(m, 96, k, 32, "cuda:0")
-    q.qerl_linear_prepare(g.x, 96, g.a, L.lora_scale, g.z, ws)
-    y = torch.empty((m, 96), dtype=torch.bfloat16, device="cuda:0")
+    ws = q.workspace(m, n, k, r, "cuda:0")
+    q.qerl_linear_prepare(g.x, n, g.a, L.lora_scale, g.z, ws)
+    y = torch.empty((m, n), dtype=torch.bfloat16, device="cuda:0")
     for _ in range(3):       # repeated contractions from one prepared workspace
         q.qerl_linear_decode_prepared(m, g.codes, g.scales, g.S, k, g.b, y, ws)
         torch.cuda.synchronize()
