@@ -26,6 +26,7 @@ Modules
            (Eq. 7) drawn from Philox4x64-10 + Box-Muller.
   linear   y = (x * (1 + z)) W^T + s (x * (1 + z)) A^T B^T in fp64.
   rmsnorm  the noisy RMSNorm producer (w + z) * x / rms(x) (Eq. 10).
+  swiglu   SiLU(gate) * up between the gate/up and down layers.
 
 Parity pins (tests/test_oracle_*.py): every function here is checked
 against something other than itself: values printed on the pages
