@@ -18,6 +18,8 @@ timed region.
 Printed: one JSON line.  `value` = decode weight-stream GB/s (algorithmic
 bytes of the step / step time); `roofline` = the decode contraction kernel
 of the gate/up layer, timed alone with HIP events on its launch stream;
+`mlp_chain` = the same weights run as one chained feed-forward block (noisy
+RMSNorm -> gate/up -> SiLU(gate) * up -> down) per step;
 `prefill` = the 4096-token prefill of the Qwen2.5-7B qkv and down layers
 in TFLOP/s; `rmsnorm` = the noisy RMSNorm producer on the 7B hidden size
 (GB/s at 4096 rows, microseconds at 64 rows); `quantizer` = bulk
@@ -46,6 +48,7 @@ def parse():
     ap.add_argument("--copies", type=int, default=6)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-chain", action="store_true")
     ap.add_argument("--profile", nargs="?", const="decode", choices=("decode", "prefill", "rmsnorm"),
                     help="profiling pass for rocprofv3, no timing and no JSON line: "
                          "'decode' runs one plain device copy of COPY_BYTES (counter "
@@ -327,6 +330,53 @@ def main():
     step_bytes = sum(linear_bytes(M, ly["n"], ly["k"], R) for ly in layers)
     value = step_bytes / (dt / args.steps) / 1e9
 
+    # ---- the same 7B weights as one chained decode feed-forward block: noisy
+    # RMSNorm (Eq. 10, noise of the gate/up group) -> fused gate/up layer (no
+    # noise of its own) -> SiLU(gate) * up -> down layer (its own noise).  The
+    # two noise vectors are drawn before timing (the step above draws them on
+    # a second stream, off its critical path).
+    chain = None
+    if not args.no_chain:
+        from workloads import norm_inputs
+        gu_l, dn_l = layers
+        d_model, d_inter = gu_l["k"], dn_l["k"]
+        xres_bits, wn_bits = norm_inputs(M, d_model, seed=41)
+        xres, wnorm = to_dev(xres_bits), to_dev(wn_bits)
+        z_gu = q.qerl_aqn_sample(41, 0, 0, sigma, d_model, device=dev)
+        z_dn = q.qerl_aqn_sample(41, 0, 1, sigma, d_inter, device=dev)
+        h = torch.empty((M, d_model), dtype=torch.bfloat16, device=dev)
+        act = torch.empty((M, d_inter), dtype=torch.bfloat16, device=dev)
+
+        def chain_step(i):
+            cg, sg = gu_l["rot"][i % copies]
+            cd, sd = dn_l["rot"][i % copies]
+            q.qerl_rmsnorm_noisy(xres, wnorm, z_gu, 1e-6, out=h)
+            q.qerl_linear_decode(h, cg, sg, gu_l["S"], gu_l["a"], gu_l["b"], cfg.lora_scale,
+                                 None, workspace=gu_l["ws"], y=gu_l["y"])
+            q.qerl_swiglu(gu_l["y"], out=act)
+            q.qerl_linear_decode(act, cd, sd, dn_l["S"], dn_l["a"], dn_l["b"], cfg.lora_scale,
+                                 z_dn, workspace=dn_l["ws"], y=dn_l["y"])
+
+        for i in range(args.warmup):
+            chain_step(i)
+        c0 = torch.cuda.Event(enable_timing=True)
+        c1 = torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        for i in range(args.steps):
+            chain_step(i)
+        c1.record(stream)
+        c1.synchronize()
+        t_chain = c0.elapsed_time(c1) / 1e3 / args.steps
+        chain_bytes = (4 * M * d_model + 6 * d_model
+                       + linear_bytes(M, gu_l["n"], d_model, R) - 4 * d_model
+                       + 6 * M * d_inter
+                       + linear_bytes(M, dn_l["n"], d_inter, R))
+        chain = {"workload": "decode_7b_mlp chained: noisy RMSNorm -> gate/up -> SiLU(gate)*up "
+                             "-> down, M=64",
+                 "us_per_step": round(t_chain * 1e6, 2),
+                 "GB_per_s": round(chain_bytes / t_chain / 1e9, 1),
+                 "frac_hbm": round(chain_bytes / t_chain / 1e9 / HBM_PEAK_GBS, 4)}
+
     # ---- dominant kernel alone: gate/up contraction, HIP events on its stream
     ly = layers[0]
     q.qerl_linear_prepare(ly["x"], ly["n"], ly["a"], cfg.lora_scale, zring[0][0], ly["ws"])
@@ -453,6 +503,7 @@ def main():
         "step_frac_hbm": round(value / HBM_PEAK_GBS, 4),
         "prefill": prefill,
         "rmsnorm": rmsnorm,
+        "mlp_chain": chain,
         "quantizer": {"GB_per_s": round(q_bytes / min(qtimes) / 1e9, 1),
                       "elements": q_elems, "bytes_per_elem": 2.5625},
         "cpu_baseline": cpu,

@@ -175,6 +175,23 @@ QERL_API qerl_status qerl_rmsnorm_noisy(const void* x, int64_t m, int64_t d,
                                         void* y, void* stream);
 
 /*
+ * qerl_swiglu -- the gated activation between the fused gate/up layer and
+ * the down layer of the Qwen2.5 feed-forward block (W_gate, W_up, W_down
+ * [QeRL summary, §3.4 "Layer coverage"]; the gating itself is the model's,
+ * not stated on the pages):
+ *     out[i, j] = bf16( SiLU(gate_up[i, j]) * gate_up[i, d + j] ),
+ *     SiLU(g) = g / (1 + exp(-g)), computed in fp32.
+ *   gate_up  device, [m, 2 d] bf16 (the fused layer's output: gate in
+ *            columns 0 .. d-1, up in d .. 2d-1), 16-byte aligned
+ *   m        >= 1
+ *   d        >= 8, d % 8 == 0
+ *   out      device out, [m, d] bf16, 16-byte aligned; must not overlap
+ *            gate_up
+ */
+QERL_API qerl_status qerl_swiglu(const void* gate_up, int64_t m, int64_t d, void* out,
+                                 void* stream);
+
+/*
  * qerl_linear_workspace_bytes -- bytes of device workspace that
  * qerl_linear_decode / qerl_linear_prefill / qerl_linear_prepare need for
  * these sizes on the current device.  0 if the sizes are invalid.  The

@@ -106,6 +106,18 @@ def qerl_rmsnorm_noisy(x, w, z=None, delta=1e-6, out=None):
     return out
 
 
+def qerl_swiglu(gate_up, out=None):
+    """bf16(SiLU(gate) * up) from the fused gate/up output [m, 2 d]."""
+    gu = _bits16(gate_up, "gate_up")
+    m, d2 = gu.shape
+    if d2 % 2:
+        raise ValueError("gate_up must have an even number of columns")
+    if out is None:
+        out = torch.empty((m, d2 // 2), dtype=torch.bfloat16, device=gu.device)
+    _check(lib.qerl_swiglu(_ptr(gu), m, d2 // 2, _ptr(out), _stream(gu.device)), "qerl_swiglu")
+    return out
+
+
 def qerl_linear_workspace_bytes(m, n, k, r):
     return int(lib.qerl_linear_workspace_bytes(m, n, k, r))
 

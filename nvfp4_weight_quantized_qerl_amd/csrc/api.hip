@@ -55,7 +55,7 @@ const char* qerl_status_string(int status) {
   }
 }
 
-int qerl_abi_version(void) { return 4; }
+int qerl_abi_version(void) { return 5; }
 
 qerl_status qerl_quantize_nvfp4(const void* w_bf16, int64_t n, int64_t k, void* codes,
                                 void* scales, float* gscale, int32_t* nonfinite_flag,
@@ -143,6 +143,15 @@ qerl_status qerl_rmsnorm_noisy(const void* x, int64_t m, int64_t d, const void* 
   return from_hip(qerl::launch_rmsnorm_noisy(
       static_cast<const uint16_t*>(x), m, d, static_cast<const uint16_t*>(w), z, delta,
       static_cast<uint16_t*>(y), static_cast<hipStream_t>(stream)));
+}
+
+qerl_status qerl_swiglu(const void* gate_up, int64_t m, int64_t d, void* out, void* stream) {
+  if (!gate_up || !out) return QERL_ERR_NULL;
+  if (m < 1 || d < 8 || d % 8) return QERL_ERR_SHAPE;
+  if (!aligned(gate_up, 16) || !aligned(out, 16)) return QERL_ERR_ALIGN;
+  return from_hip(qerl::launch_swiglu(static_cast<const uint16_t*>(gate_up), m, d,
+                                      static_cast<uint16_t*>(out),
+                                      static_cast<hipStream_t>(stream)));
 }
 
 size_t qerl_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t r) {

@@ -27,6 +27,10 @@ hipError_t launch_aqn_sample(uint64_t seed, uint64_t stream_id,
 hipError_t launch_rmsnorm_noisy(const uint16_t* x, int64_t m, int64_t d, const uint16_t* w,
                                 const float* z, float delta, uint16_t* y, hipStream_t stream);
 
+// out = bf16(SiLU(gate) * up) from the fused gate/up output [m, 2 d].
+hipError_t launch_swiglu(const uint16_t* gu, int64_t m, int64_t d, uint16_t* out,
+                         hipStream_t stream);
+
 // ------------------------------------------------------------------- linear
 // Workspace layout and launch shapes for one (m, n, k, r).
 struct LinearPlan {

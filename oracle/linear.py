@@ -39,7 +39,14 @@ def noisy_input(x_bits, z):
 
 def linear(x_bits, w_hat, z=None, a_bits=None, b_bits=None, lora_scale=0.0):
     """y [M, N] fp64 = x_t W_hat^T + s (x_t A^T) B^T."""
-    xt = noisy_input(x_bits, z)
+    return linear_values(bf16_bits_to_f64(x_bits), w_hat, z, a_bits, b_bits, lora_scale)
+
+
+def linear_values(x, w_hat, z=None, a_bits=None, b_bits=None, lora_scale=0.0):
+    """The same layer for activations given as fp64 values (a chain of
+    layers evaluated without rounding in between)."""
+    x = np.asarray(x, dtype=np.float64)
+    xt = x if z is None else x * (1.0 + np.asarray(z, dtype=np.float32).astype(np.float64))
     y = xt @ np.asarray(w_hat, dtype=np.float64).T
     if a_bits is not None and b_bits is not None and np.size(a_bits):
         a = bf16_bits_to_f64(a_bits)

@@ -41,7 +41,7 @@ def test_status_strings():
     for s in range(7):
         assert lib.qerl_status_string(s).decode().startswith("QERL_")
     assert b"unknown" in lib.qerl_status_string(99)
-    assert lib.qerl_abi_version() == 4
+    assert lib.qerl_abi_version() == 5
 
 
 FAKE = ctypes.c_void_p(0x10000)        # aligned, never dereferenced on error
@@ -116,6 +116,13 @@ def test_rmsnorm_validation():
     assert f(FAKE, 4, 64, MIS, None, 1e-6, FAKE, None) == 3
     assert f(FAKE, 4, 64, FAKE, MIS, 1e-6, FAKE, None) == 3
     assert f(FAKE, 4, 64, FAKE, None, 1e-6, MIS, None) == 3
+
+
+def test_swiglu_validation():
+    f = lib.qerl_swiglu
+    assert f(None, 4, 64, FAKE, None) == 1 and f(FAKE, 4, 64, None, None) == 1
+    assert f(FAKE, 0, 64, FAKE, None) == 2 and f(FAKE, 4, 12, FAKE, None) == 2
+    assert f(MIS, 4, 64, FAKE, None) == 3 and f(FAKE, 4, 64, MIS, None) == 3
 
 
 def test_workspace_sizes():
