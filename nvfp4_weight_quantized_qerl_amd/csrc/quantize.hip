@@ -16,7 +16,9 @@
 //            with a global atomic max of the fp32 bit pattern
 //   scale    one thread: non-finite flag, S = RN_fp32(amax / 2688)
 //   encode   one thread per 16-element block (blocks are contiguous in
-//            memory because k % 16 == 0)
+//            memory because k % 16 == 0), grid-stride; each workgroup
+//            first tabulates the element keys of all 126 nonzero block-scale
+//            codes (they depend only on the code and S)
 //
 // Exactness of `encode` (no rounding can change a decision):
 //  * q = amax_b / (6 S) in fp64.  amax_b has 8 significant bits and 6 S at
@@ -32,6 +34,8 @@
 //    lower.  A tie at the midpoint between codes i and i+1 goes to the
 //    even one of the two, so the crossing test is "> thr" for even i and
 //    ">= thr" for odd i.
+#include <algorithm>
+
 #include "qerl_device.h"
 #include "qerl_internal.h"
 
@@ -51,15 +55,15 @@ __global__ __launch_bounds__(256) void qz_amax(const uint4* __restrict__ w,
     const uint32_t d = max(v.w & 0x7fffu, (v.w >> 16) & 0x7fffu);
     m = max(m, max(max(a, b), max(c, d)));
   };
-  // Four independent 16-byte loads per thread in flight per iteration.
+  // Eight independent 16-byte loads per thread in flight per iteration.
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  for (; i + 3 * stride < nvec; i += 4 * stride) {
-    const uint4 v0 = w[i], v1 = w[i + stride], v2 = w[i + 2 * stride], v3 = w[i + 3 * stride];
-    fold(v0);
-    fold(v1);
-    fold(v2);
-    fold(v3);
+  for (; i + 7 * stride < nvec; i += 8 * stride) {
+    uint4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = w[i + u * stride];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) fold(v[u]);
   }
   for (; i < nvec; i += stride) fold(w[i]);
 #pragma unroll
@@ -112,56 +116,67 @@ __device__ __forceinline__ int32_t bf16_key(double thr, bool ge) {
   return (int32_t)kb - ((ge && exact) ? 1 : 0);
 }
 
+// Element keys of every block-scale code, once per workgroup: key_tab[c][t]
+// for E4M3 codes c = 1..126 and E2M1 midpoints t (code 0 never reads them).
+// The keys depend only on c and S, so the fp64 work is done 127 times per
+// workgroup instead of once per block.
+constexpr int kCodes = 127;
+
+__device__ __forceinline__ void build_keys(int16_t (*key_tab)[8], double S) {
+  constexpr double mids[7] = {0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0};
+  for (int i = threadIdx.x; i < kCodes * 7; i += blockDim.x) {
+    const int c = i / 7, t = i - 7 * (i / 7);
+    if (c == 0) continue;
+    const double unit = (double)e4m3_to_f32((uint32_t)c) * S;   // exact
+    key_tab[c][t] = (int16_t)bf16_key(mids[t] * unit, (t & 1) != 0);
+  }
+}
+
+// Grid-stride over 16-element blocks; each thread encodes one block per
+// iteration (blocks are contiguous in memory because k % 16 == 0).
 __global__ __launch_bounds__(256) void qz_encode(const uint4* __restrict__ w,
                                                  int64_t nblocks,
                                                  const float* __restrict__ gscale,
                                                  uint2* __restrict__ codes,
                                                  uint8_t* __restrict__ scales) {
-  const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (b >= nblocks) return;
-  const uint4 lo = w[2 * b], hi = w[2 * b + 1];
-  const uint32_t words[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-  uint32_t mag[16];
-  uint32_t amax_b = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    mag[2 * i] = words[i] & 0x7fffu;
-    mag[2 * i + 1] = (words[i] >> 16) & 0x7fffu;
-    amax_b = max(amax_b, max(mag[2 * i], mag[2 * i + 1]));
-  }
+  __shared__ int16_t key_tab[kCodes][8];
   const float S = *gscale;
-  uint32_t scode = 0;
-  if (S > 0.0f && amax_b != 0) {
-    const double q = (double)bf16_to_f32(amax_b) / (6.0 * (double)S);
-    scode = e4m3_rne_code(q);
-  }
-  int32_t key[7];
-  if (scode == 0) {
+  build_keys(key_tab, (double)S);
+  __syncthreads();
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nblocks; b += stride) {
+    const uint4 lo = w[2 * b], hi = w[2 * b + 1];
+    const uint32_t words[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    uint32_t mag[16];
+    uint32_t amax_b = 0;
 #pragma unroll
-    for (int i = 0; i < 7; ++i) key[i] = 0x7fff;   // nothing exceeds
-  } else {
-    const double unit = (double)e4m3_to_f32(scode) * (double)S;   // exact
-    key[0] = bf16_key(0.25 * unit, false);
-    key[1] = bf16_key(0.75 * unit, true);
-    key[2] = bf16_key(1.25 * unit, false);
-    key[3] = bf16_key(1.75 * unit, true);
-    key[4] = bf16_key(2.5 * unit, false);
-    key[5] = bf16_key(3.5 * unit, true);
-    key[6] = bf16_key(5.0 * unit, false);
-  }
-  uint32_t packed[2] = {0u, 0u};
+    for (int i = 0; i < 8; ++i) {
+      mag[2 * i] = words[i] & 0x7fffu;
+      mag[2 * i + 1] = (words[i] >> 16) & 0x7fffu;
+      amax_b = max(amax_b, max(mag[2 * i], mag[2 * i + 1]));
+    }
+    uint32_t scode = 0;
+    if (S > 0.0f && amax_b != 0) {
+      const double q = (double)bf16_to_f32(amax_b) / (6.0 * (double)S);
+      scode = e4m3_rne_code(q);
+    }
+    int32_t key[7];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int32_t a = (int32_t)mag[i];
-    uint32_t c = 0;
+    for (int t = 0; t < 7; ++t) key[t] = scode ? (int32_t)key_tab[scode][t] : 0x7fff;
+    uint32_t packed[2] = {0u, 0u};
 #pragma unroll
-    for (int t = 0; t < 7; ++t) c += (a > key[t]) ? 1u : 0u;
-    const uint32_t sign = (words[i >> 1] >> ((i & 1) ? 31 : 15)) & 1u;
-    c |= sign << 3;
-    packed[i >> 3] |= c << (4 * (i & 7));
+    for (int i = 0; i < 16; ++i) {
+      const int32_t a = (int32_t)mag[i];
+      uint32_t c = 0;
+#pragma unroll
+      for (int t = 0; t < 7; ++t) c += (a > key[t]) ? 1u : 0u;
+      const uint32_t sign = (words[i >> 1] >> ((i & 1) ? 31 : 15)) & 1u;
+      c |= sign << 3;
+      packed[i >> 3] |= c << (4 * (i & 7));
+    }
+    codes[b] = make_uint2(packed[0], packed[1]);
+    scales[b] = (uint8_t)scode;
   }
-  codes[b] = make_uint2(packed[0], packed[1]);
-  scales[b] = (uint8_t)scode;
 }
 
 }  // namespace
@@ -180,7 +195,9 @@ hipError_t launch_quantize(const uint16_t* w, int64_t n, int64_t k,
   hipLaunchKernelGGL(qz_amax, dim3((unsigned)grid), dim3(256), 0, stream,
                      reinterpret_cast<const uint4*>(w), nvec, slot);
   hipLaunchKernelGGL(qz_scale, dim3(1), dim3(1), 0, stream, slot, flag);
-  const int64_t eg = (nblocks + 255) / 256;
+  // Enough workgroups to fill the chip a few times over; each builds its
+  // key table once and then loops over its blocks.
+  const int64_t eg = std::min<int64_t>((nblocks + 255) / 256, (int64_t)device_cu_count() * 8);
   hipLaunchKernelGGL(qz_encode, dim3((unsigned)eg), dim3(256), 0, stream,
                      reinterpret_cast<const uint4*>(w), nblocks,
                      (const float*)gscale, reinterpret_cast<uint2*>(codes),
