@@ -74,3 +74,30 @@ def max_rel_error(y, y_ref):
     den = np.maximum(np.abs(y_ref), rms)
     den = np.where(den == 0.0, 1.0, den)
     return float(np.max(np.abs(y - y_ref) / den))
+
+
+def backward(dy, x_bits, w_hat, z=None, a_bits=None, b_bits=None, lora_scale=0.0):
+    """Gradients of the layer through the frozen NVFP4 weight, fp64.
+
+    The rollout's log-probabilities are taken on the same quantized model
+    and only the LoRA factors (and the RMSNorm scales) are trained
+    [QeRL summary, §3.4 "Low-Rank Adaptation" and Algorithm 1's inner
+    updates]: W_hat gets no gradient, the input does (it flows on to the
+    layers below).  With x_t = x (.) (1 + z), t = x_t A^T and g = dy B:
+        dx = (dy W_hat + s g A) (.) (1 + z)
+        dA = s g^T x_t          dB = s dy^T t
+    dy [M, N] fp64 values; returns (dx [M, K], dA [r, K], dB [N, r]) (the
+    last two None without a LoRA branch)."""
+    dy = np.asarray(dy, dtype=np.float64)
+    x = bf16_bits_to_f64(x_bits)
+    zz = np.zeros(x.shape[1]) if z is None else np.asarray(z, dtype=np.float32).astype(np.float64)
+    xt = x * (1.0 + zz)
+    dxt = dy @ np.asarray(w_hat, dtype=np.float64)
+    if a_bits is None or b_bits is None or not np.size(a_bits):
+        return dxt * (1.0 + zz), None, None
+    a = bf16_bits_to_f64(a_bits)
+    b = bf16_bits_to_f64(b_bits)
+    s = float(lora_scale)
+    g = dy @ b
+    dxt = dxt + s * (g @ a)
+    return dxt * (1.0 + zz), s * (g.T @ xt), s * (dy.T @ (xt @ a.T))

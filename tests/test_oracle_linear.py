@@ -4,6 +4,7 @@ merging, zero-noise / zero-LoRA reductions)."""
 from fractions import Fraction
 
 import numpy as np
+import pytest
 
 from oracle import aqn, formats, linear, nvfp4
 from workloads import make_layer
@@ -77,3 +78,41 @@ def test_max_rel_error_metric():
     y = y_ref.copy()
     y[2] = 0.01
     assert linear.max_rel_error(y, y_ref) == 0.01 / rms
+
+
+# ---- backward through the frozen NVFP4 weight: the layer is linear in x,
+# in A and in B separately, so each gradient must satisfy the adjoint
+# identity <dy, f(direction)> = <gradient, direction> against the forward
+# oracle (a different formula from the one the backward evaluates).
+
+def test_backward_adjoint_identities():
+    from workloads import bf16_from_f32
+    L = make_layer(m=6, n=40, k=64, r=4, seed=31)
+    w_hat = nvfp4.dequantize(*nvfp4.quantize(L.w))
+    z = aqn.sample(31, 0, 0, 0.05, 64)
+    rng = np.random.default_rng(31)
+    dy = rng.standard_normal((6, 40))
+    dx, da, db = linear.backward(dy, L.x, w_hat, z, L.a, L.b, 2.0)
+    # x direction: y(v) for a bf16 direction v (y is linear in x)
+    v = bf16_from_f32(rng.standard_normal((6, 64)).astype(np.float32))
+    yv = linear.linear(v, w_hat, z, L.a, L.b, 2.0)
+    assert np.sum(dy * yv) == pytest.approx(np.sum(dx * formats.bf16_bits_to_f64(v)), rel=1e-12)
+    # A direction: y(A + V) - y(A) = s x_t V^T B^T
+    V = bf16_from_f32(0.02 * rng.standard_normal((4, 64)).astype(np.float32))
+    zero_a = np.zeros_like(L.a)
+    dyA = linear.linear(L.x, np.zeros_like(w_hat), z, V, L.b, 2.0) - \
+        linear.linear(L.x, np.zeros_like(w_hat), z, zero_a, L.b, 2.0)
+    assert np.sum(dy * dyA) == pytest.approx(np.sum(da * formats.bf16_bits_to_f64(V)), rel=1e-12)
+    # B direction
+    U = bf16_from_f32(0.01 * rng.standard_normal((40, 4)).astype(np.float32))
+    dyB = linear.linear(L.x, np.zeros_like(w_hat), z, L.a, U, 2.0)
+    assert np.sum(dy * dyB) == pytest.approx(np.sum(db * formats.bf16_bits_to_f64(U)), rel=1e-12)
+
+
+def test_backward_without_lora_or_noise_is_the_transposed_product():
+    L = make_layer(m=3, n=24, k=32, r=0, seed=32)
+    w_hat = nvfp4.dequantize(*nvfp4.quantize(L.w))
+    dy = np.random.default_rng(32).standard_normal((3, 24))
+    dx, da, db = linear.backward(dy, L.x, w_hat)
+    assert da is None and db is None
+    assert np.array_equal(dx, dy @ w_hat)
