@@ -284,6 +284,39 @@ QERL_API qerl_status qerl_linear_prefill_prepared(
     int64_t n, int64_t k, const void* lora_b, int32_t r, void* y,
     void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * qerl_linear_backward -- gradients of the layer through the frozen NVFP4
+ * weight.  The rollout's log-probabilities are taken on the same quantized
+ * model and only the LoRA factors (and RMSNorm scales) are trained
+ * [QeRL summary, §3.4 "Low-Rank Adaptation"; Algorithm 1, inner updates],
+ * so W_hat gets no gradient.  With x_t = bf16(x (.) (1 + z)) as in the
+ * forward, t = bf16(s x_t A^T) and gs = bf16(s dy B):
+ *     dx = bf16( (dy W_hat + gs A) (.) (1 + z) )      [m, k]
+ *     dA = gs^T x_t   (fp32, [r, k])     dB = dy^T t   (fp32, [n, r])
+ * Sums in fp32.
+ *   dy           device, [m, n] bf16 output gradient, 16-byte aligned
+ *   m            >= 1
+ *   codes, scales, gscale   the layer's NVFP4 weight [n, k]
+ *   n, k         >= 16, multiples of 16
+ *   x            device, [m, k] bf16 forward input, 16-byte aligned
+ *   lora_a, lora_b, r, lora_scale, z   as in qerl_linear_decode
+ *   dx           device out, [m, k] bf16
+ *   da, db       device out, fp32 [r, k] and [n, r]; either may be NULL
+ *                (not computed); both ignored without a LoRA branch
+ *   workspace    at least qerl_linear_backward_workspace_bytes(m, n, k, r)
+ *                bytes, 256-byte aligned
+ */
+QERL_API size_t qerl_linear_backward_workspace_bytes(int64_t m, int64_t n, int64_t k,
+                                                     int32_t r);
+
+QERL_API qerl_status qerl_linear_backward(const void* dy, int64_t m, const void* codes,
+                                          const void* scales, const float* gscale,
+                                          int64_t n, int64_t k, const void* x,
+                                          const void* lora_a, const void* lora_b, int32_t r,
+                                          float lora_scale, const float* z, void* dx,
+                                          float* da, float* db, void* workspace,
+                                          size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

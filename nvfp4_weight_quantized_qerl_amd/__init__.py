@@ -193,3 +193,32 @@ def qerl_linear_prefill_prepared(m, codes, scales, gscale, k, lora_b, y, workspa
     """Contraction half of qerl_linear_prefill from a prepared workspace."""
     return _prepared("qerl_linear_prefill_prepared", m, codes, scales, gscale, k, lora_b, y,
                      workspace)
+
+
+def qerl_linear_backward(dy, x, codes, scales, gscale, lora_a=None, lora_b=None,
+                         lora_scale=0.0, z=None, want_lora_grads=True, workspace=None):
+    """(dx, dA, dB) of the layer through the frozen NVFP4 weight; dA and dB
+    are fp32 (None without a LoRA branch or when not wanted)."""
+    dy = _bits16(dy, "dy")
+    x = _bits16(x, "x")
+    m, n = dy.shape
+    k = x.shape[1]
+    r = 0 if lora_a is None else int(lora_a.shape[0])
+    la = None if lora_a is None else _bits16(lora_a, "lora_a")
+    lb = None if lora_b is None else _bits16(lora_b, "lora_b")
+    nbytes = lib.qerl_linear_backward_workspace_bytes(m, n, k, r)
+    if nbytes == 0:
+        raise ValueError("invalid backward sizes")
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dy.device)
+    dx = torch.empty((m, k), dtype=torch.bfloat16, device=dy.device)
+    da = db = None
+    if r and want_lora_grads:
+        da = torch.empty((r, k), dtype=torch.float32, device=dy.device)
+        db = torch.empty((n, r), dtype=torch.float32, device=dy.device)
+    _check(lib.qerl_linear_backward(_ptr(dy), m, _ptr(codes), _ptr(scales), _ptr(gscale), n, k,
+                                    _ptr(x), _ptr(la), _ptr(lb), r, float(lora_scale), _ptr(z),
+                                    _ptr(dx), _ptr(da), _ptr(db), _ptr(workspace),
+                                    workspace.numel(), _stream(dy.device)),
+           "qerl_linear_backward")
+    return dx, da, db

@@ -55,7 +55,7 @@ const char* qerl_status_string(int status) {
   }
 }
 
-int qerl_abi_version(void) { return 5; }
+int qerl_abi_version(void) { return 6; }
 
 qerl_status qerl_quantize_nvfp4(const void* w_bf16, int64_t n, int64_t k, void* codes,
                                 void* scales, float* gscale, int32_t* nonfinite_flag,
@@ -152,6 +152,37 @@ qerl_status qerl_swiglu(const void* gate_up, int64_t m, int64_t d, void* out, vo
   return from_hip(qerl::launch_swiglu(static_cast<const uint16_t*>(gate_up), m, d,
                                       static_cast<uint16_t*>(out),
                                       static_cast<hipStream_t>(stream)));
+}
+
+size_t qerl_linear_backward_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t r) {
+  if (m < 1 || n < 16 || n % 16 || k < 16 || k % 16 || r < 0 || r > 128) return 0;
+  return qerl::make_backward_plan(m, n, k, r).total;
+}
+
+qerl_status qerl_linear_backward(const void* dy, int64_t m, const void* codes,
+                                 const void* scales, const float* gscale, int64_t n, int64_t k,
+                                 const void* x, const void* lora_a, const void* lora_b,
+                                 int32_t r, float lora_scale, const float* z, void* dx,
+                                 float* da, float* db, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  if (!dy || !codes || !scales || !gscale || !x || !dx || !workspace) return QERL_ERR_NULL;
+  if (r > 0 && (!lora_a) != (!lora_b)) return QERL_ERR_NULL;
+  if (m < 1 || n < 16 || n % 16 || k < 16 || k % 16) return QERL_ERR_SHAPE;
+  if (r < 0 || r > 128 || !std::isfinite(lora_scale)) return QERL_ERR_RANGE;
+  const int32_t r_eff = (r > 0 && lora_a && lora_b) ? r : 0;
+  if (!aligned(dy, 16) || !aligned(x, 16) || !aligned(codes, 16) || !aligned(gscale, 4) ||
+      !aligned(dx, 2) || (z && !aligned(z, 16)) || (r_eff && !aligned(lora_a, 16)) ||
+      (da && !aligned(da, 4)) || (db && !aligned(db, 4)) || !aligned(workspace, 256))
+    return QERL_ERR_ALIGN;
+  const qerl::BackwardPlan plan = qerl::make_backward_plan(m, n, k, r_eff);
+  if (workspace_bytes < plan.total) return QERL_ERR_WORKSPACE;
+  return from_hip(qerl::launch_linear_backward(
+      plan, static_cast<const uint16_t*>(dy), static_cast<const uint8_t*>(codes),
+      static_cast<const uint8_t*>(scales), gscale, static_cast<const uint16_t*>(x),
+      static_cast<const uint16_t*>(r_eff ? lora_a : nullptr),
+      static_cast<const uint16_t*>(r_eff ? lora_b : nullptr), lora_scale, z,
+      static_cast<uint16_t*>(dx), r_eff ? da : nullptr, r_eff ? db : nullptr,
+      static_cast<char*>(workspace), static_cast<hipStream_t>(stream)));
 }
 
 size_t qerl_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t r) {

@@ -142,7 +142,7 @@ struct PrepArgs {
   const uint16_t* __restrict__ x;
   const float* __restrict__ z;
   const uint16_t* __restrict__ a;
-  uint16_t* __restrict__ xt;
+  uint16_t* __restrict__ xt;     // null: x_t is not written (only the LoRA-down partials)
   float* __restrict__ tpart;
   int64_t m, mpad, k;
   int r, rpad32;
@@ -218,7 +218,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs p) {
     const int rr = 8 * wave + i;
     const int64_t mrow = row0 + rr;
     if (mrow < p.m && p.z) xv[i] = noisy8(xv[i], z0, z1);
-    if (kin) *reinterpret_cast<uint4*>(p.xt + mrow * p.k + kl) = xv[i];
+    if (kin && p.xt) *reinterpret_cast<uint4*>(p.xt + mrow * p.k + kl) = xv[i];
     xs[rr * 64 + (lane ^ (rr & 15))] = xv[i];
   }
   if (RT == 0) return;
@@ -301,6 +301,39 @@ __global__ __launch_bounds__(256) void treduce_kernel(const float* __restrict__ 
 
 int lds_split(const LinearPlan& p) {
   return (int)std::min<int64_t>(p.dec_split, std::max<int64_t>(1, p.k / 256));
+}
+
+hipError_t launch_lora_down(const uint16_t* x, int64_t m, int64_t mpad, int64_t k,
+                            const uint16_t* a_rk, int r, float scale, float* tpart,
+                            uint16_t* t, hipStream_t stream) {
+  PrepArgs a;
+  a.x = x;
+  a.z = nullptr;
+  a.a = a_rk;
+  a.xt = nullptr;
+  a.tpart = tpart;
+  a.m = m;
+  a.mpad = mpad;
+  a.k = k;
+  a.r = r;
+  a.rpad32 = (int)rup(r, 32);
+  a.lora_scale = scale;
+  const int kchunks = (int)cdiv(k, kPrepChunk);
+  const dim3 grid((unsigned)(mpad / 32), (unsigned)kchunks);
+  switch (a.rpad32 / 32) {
+    case 1: hipLaunchKernelGGL(prep_kernel<1>, grid, dim3(256), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL(prep_kernel<2>, grid, dim3(256), 0, stream, a); break;
+    case 3: hipLaunchKernelGGL(prep_kernel<3>, grid, dim3(256), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL(prep_kernel<4>, grid, dim3(256), 0, stream, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int rpad16 = (int)rup(r, 16);
+  const int64_t total = mpad * rpad16;
+  hipLaunchKernelGGL(treduce_kernel, dim3((unsigned)cdiv(total, 256)), dim3(256), 0, stream,
+                     tpart, t, mpad, a.rpad32, rpad16, kchunks);
+  return hipGetLastError();
 }
 
 hipError_t launch_treduce(const LinearPlan& p, char* ws, hipStream_t stream) {

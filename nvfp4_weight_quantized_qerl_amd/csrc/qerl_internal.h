@@ -61,6 +61,13 @@ hipError_t launch_linear_prepare(const LinearPlan& p, const uint16_t* x,
                                  float lora_scale, char* ws,
                                  hipStream_t stream);
 
+// t = bf16(scale x a_rk^T) for x [m, k] (rows m..mpad-1 read as zero) and
+// a_rk [r, k]: the LoRA-down kernels on any operands (partials [ceil(k/512),
+// mpad, rup(r,32)] fp32 in tpart, t [mpad, rup(r,16)] bf16).
+hipError_t launch_lora_down(const uint16_t* x, int64_t m, int64_t mpad, int64_t k,
+                            const uint16_t* a_rk, int r, float scale, float* tpart,
+                            uint16_t* t, hipStream_t stream);
+
 // LoRA-down reduction: launch_linear_prepare writes the chunk partials
 // s x_t A^T (tpart) and then t = bf16(sum of the partials) (launch_treduce).
 hipError_t launch_treduce(const LinearPlan& p, char* ws, hipStream_t stream);
@@ -87,5 +94,21 @@ hipError_t launch_linear_prefill_main(const LinearPlan& p, const uint8_t* codes,
                                       const uint8_t* scales, const float* gscale,
                                       const uint16_t* lora_b, uint16_t* y, char* ws,
                                       hipStream_t stream);
+
+// ----------------------------------------------------------------- backward
+// Workspace of the backward: the forward's prepare plan (x_t, t) followed by
+// B^T [r, n], the partials of s dy B and gs = bf16(s dy B) [mpad, rpad16].
+struct BackwardPlan {
+  LinearPlan fwd;
+  size_t off_bt, off_gpart, off_gs, total;
+};
+
+BackwardPlan make_backward_plan(int64_t m, int64_t n, int64_t k, int r);
+
+hipError_t launch_linear_backward(const BackwardPlan& b, const uint16_t* dy, const uint8_t* codes,
+                                  const uint8_t* scales, const float* gscale, const uint16_t* x,
+                                  const uint16_t* lora_a, const uint16_t* lora_b, float lora_scale,
+                                  const float* z, uint16_t* dx, float* da, float* db, char* ws,
+                                  hipStream_t stream);
 
 }  // namespace qerl

@@ -33,7 +33,7 @@ def test_every_declared_symbol_is_exported():
     assert sorted(_lib.SIGNATURES) == names
     for name in names:
         if name not in ("qerl_status_string", "qerl_abi_version",
-                        "qerl_linear_workspace_bytes"):
+                        "qerl_linear_workspace_bytes", "qerl_linear_backward_workspace_bytes"):
             assert hasattr(q, name), name
 
 
@@ -41,7 +41,7 @@ def test_status_strings():
     for s in range(7):
         assert lib.qerl_status_string(s).decode().startswith("QERL_")
     assert b"unknown" in lib.qerl_status_string(99)
-    assert lib.qerl_abi_version() == 5
+    assert lib.qerl_abi_version() == 6
 
 
 FAKE = ctypes.c_void_p(0x10000)        # aligned, never dereferenced on error
@@ -123,6 +123,28 @@ def test_swiglu_validation():
     assert f(None, 4, 64, FAKE, None) == 1 and f(FAKE, 4, 64, None, None) == 1
     assert f(FAKE, 0, 64, FAKE, None) == 2 and f(FAKE, 4, 12, FAKE, None) == 2
     assert f(MIS, 4, 64, FAKE, None) == 3 and f(FAKE, 4, 64, MIS, None) == 3
+
+
+def test_backward_validation_and_workspace():
+    wsb = lib.qerl_linear_backward_workspace_bytes
+    assert wsb(0, 64, 64, 8) == 0 and wsb(4, 24, 64, 8) == 0 and wsb(4, 64, 24, 8) == 0
+    assert wsb(4, 64, 64, 129) == 0
+    big = wsb(4096, 3584, 18944, 32)
+    assert big >= 4096 * 18944 * 2 and big < 3584 * 18944 // 2 + 4096 * 18944 * 4
+    f = lib.qerl_linear_backward
+    args = [FAKE, 4, FAKE, FAKE, FAKE, 64, 64, FAKE, None, None, 0, 2.0, None, FAKE, None,
+            None, FAKE, 1 << 30, None]
+    def call(**kw):
+        a = list(args)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    assert call(a0=None) == 1 and call(a7=None) == 1 and call(a13=None) == 1
+    assert call(a8=FAKE, a10=4) == 1                      # A without B
+    assert call(a1=0) == 2 and call(a5=24) == 2 and call(a6=8) == 2
+    assert call(a10=129) == 4 and call(a11=float("nan")) == 4
+    assert call(a0=MIS) == 3 and call(a7=MIS) == 3 and call(a16=MIS) == 3
+    assert call(a17=16) == 5
 
 
 def test_workspace_sizes():
