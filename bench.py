@@ -404,6 +404,7 @@ def main():
     # ---- prefill (Qwen2.5-7B qkv and down, 4096 tokens): TFLOP/s, for the
     # whole call (prepare + GEMM) and for the GEMM kernel alone
     prefill = None
+    backward = None
     if not args.no_prefill:
         pc = CONFIGS["prefill_7b"]
         psig = q.qerl_aqn_sigma(pc.sigma_start, pc.sigma_end, pc.num_stages, pc.stage)
@@ -443,6 +444,29 @@ def main():
             t_main += tm
             pflops += fl
             del x, a, b, codes, scales, ws, y
+        # backward through the frozen NVFP4 weight of the 7B down layer at the
+        # same 4096 tokens: dx, dA and dB
+        s_dn = pc.layers[1]
+        L = make_layer(pc.m, s_dn.n, s_dn.k, pc.r, seed=12, stage=pc.stage, call_id=1)
+        x, w, a, b = to_dev(L.x), to_dev(L.w), to_dev(L.a), to_dev(L.b)
+        codes, scales, S, _ = q.qerl_quantize_nvfp4(w)
+        del w
+        z = q.qerl_aqn_sample(L.seed, 0, 1, psig, s_dn.k, device=dev)
+        from workloads import normal_bf16
+        dy = to_dev(normal_bf16((pc.m, s_dn.n), 1.0, 12050))
+        bws = torch.empty(q.lib.qerl_linear_backward_workspace_bytes(pc.m, s_dn.n, s_dn.k, pc.r),
+                          dtype=torch.uint8, device=dev)
+        tb = timed(lambda: q.qerl_linear_backward(dy, x, codes, scales, S, a, b, pc.lora_scale,
+                                                  z, workspace=bws), reps=3)
+        mm, nn, kk, rr = pc.m, s_dn.n, s_dn.k, pc.r
+        bflops = (2.0 * mm * nn * kk          # dy W_hat
+                  + 2.0 * mm * rr * kk * 3     # t = x_t A^T, gs A, dA
+                  + 2.0 * mm * nn * rr * 2)    # gs = dy B, dB
+        backward = {"workload": f"backward of the 7B down layer: dy {mm}x{nn}, W {nn}x{kk} "
+                                f"NVFP4, r={rr} (dx, dA, dB)",
+                    "ms": round(1e3 * tb, 3), "tflops": round(bflops / tb / 1e12, 1),
+                    "frac_bf16_peak": round(bflops / tb / 1e12 / BF16_PEAK_TFLOPS, 4)}
+        del x, a, b, codes, scales, dy, bws
         prefill = {"workload": "prefill_7b (qkv 4608x3584 + down 3584x18944, M=4096, r=32)",
                    "tflops": round(pflops / t_full / 1e12, 1),
                    "gemm_tflops": round(pflops / t_main / 1e12, 1),
@@ -504,6 +528,7 @@ def main():
         "prefill": prefill,
         "rmsnorm": rmsnorm,
         "mlp_chain": chain,
+        "backward": backward,
         "quantizer": {"GB_per_s": round(q_bytes / min(qtimes) / 1e9, 1),
                       "elements": q_elems, "bytes_per_elem": 2.5625},
         "cpu_baseline": cpu,

@@ -8,8 +8,9 @@
 //     dA = gs^T x_t                                   [r, k] fp32
 //     dB = dy^T t                                     [n, r] fp32
 // Launches: the forward's prepare (x_t and t), a transpose of B, the
-// LoRA-down kernels on (dy, B^T) for gs, the dx contraction below, and one
-// accumulation kernel each for dA and dB.
+// LoRA-down kernels on (dy, B^T) for gs, the dx contraction below, and for
+// each of dA and dB an accumulation over 256-row chunks plus a reduction of
+// the chunks in order.
 //
 // dx contraction (bwd_dx<MT>): a workgroup of four waves owns 32 MT token
 // rows x 128 output columns (input channels k); wave w the columns
@@ -19,7 +20,11 @@
 // stored transposed, [k][n] with rows padded to 40 elements (80 B) so that
 // the MFMA operand reads (lane = column k, eight consecutive n) of 16 lanes
 // hit 16 different bank groups, and runs two 32x32x16 bf16 MFMAs per token
-// tile with dy read straight from global memory (lane = token row).
+// tile.  The dy tile of the step is copied to LDS with 16-byte loads (rows
+// padded to 40 elements like the weight tile, two buffers) and read by the
+// MFMAs with lane = token row.  The codes, scales and dy of the next step
+// are loaded into registers while the current step's MFMAs run; two
+// barriers per step.
 #include <algorithm>
 
 #include "qerl_device.h"
@@ -50,62 +55,88 @@ __global__ __launch_bounds__(256) void bwd_dx(DxArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t wt[kTileK * kLdsRow];
   __shared__ __attribute__((aligned(16))) uint8_t cs[kStepN * 64];
   __shared__ uint8_t ss[kStepN * 8];
+  // dy tile of the step, [32 MT rows][40] bf16, two buffers (step parity)
+  __shared__ __attribute__((aligned(16))) uint16_t dys[2][32 * MT * kLdsRow];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c = lane & 31, h = lane >> 5;
   const int64_t k0 = (int64_t)blockIdx.x * kTileK;
   const int64_t m0 = (int64_t)blockIdx.y * 32 * MT;
   const int64_t kbytes = a.k / 2, kscales = a.k / 16;
-  // copy roles: thread -> weight row n0 + tid / 8, 8 code bytes at (tid % 8) * 8
-  const int cr = tid >> 3, cb = (tid & 7) * 8;
+  // copy roles: thread -> weight row tid / 8 of the step, 8 code bytes at (tid % 8) * 8
+  const int lr = tid >> 3, lb = (tid & 7) * 8;
+  // dequantization roles: thread -> row tid % 32, 16 columns at 16 (tid / 32); rows
+  // vary fastest across the lanes so the transposed LDS writes spread over the banks
+  const int dr = tid & 31, db = (tid >> 5) * 8;
   f32x16_t acc[MT];
 #pragma unroll
   for (int u = 0; u < MT; ++u) acc[u] = zero16();
 
-  for (int64_t n0 = 0; n0 < a.n; n0 += kStepN) {
-    // stage codes and scales of rows n0 .. n0 + 31, columns k0 .. k0 + 127
-    {
-      const int64_t row = n0 + cr;
-      const int64_t byte0 = k0 / 2 + cb;            // 8 bytes = 16 columns
-      uint2 v = make_uint2(0u, 0u);
-      if (row < a.n && 2 * byte0 < a.k)
-        v = *reinterpret_cast<const uint2*>(a.codes + row * kbytes + byte0);
-      *reinterpret_cast<uint2*>(cs + cr * 64 + cb) = v;
-      if (tid < kStepN * 8) {
-        const int srow = tid >> 3, sblk = tid & 7;
-        const int64_t blk = k0 / 16 + sblk;
-        const int64_t row2 = n0 + srow;
-        ss[srow * 8 + sblk] = (row2 < a.n && blk < kscales) ? a.scales[row2 * kscales + blk] : 0;
-      }
+  // Global operands of one step, held in registers one step ahead: the
+  // dy tile goes 16 bytes per thread-chunk (row ch / 4, columns 8 (ch % 4)).
+  constexpr int DYCH = 32 * MT * 4;               // 16-byte chunks of the dy tile
+  constexpr int DYPT = (DYCH + 255) / 256;        // chunks per thread
+  uint2 cv;
+  uint8_t sv;
+  uint4 dv[DYPT];
+  auto load_step = [&](int64_t n0) {
+    const int64_t row = n0 + lr;
+    const int64_t byte0 = k0 / 2 + lb;            // 8 bytes = 16 columns
+    cv = make_uint2(0u, 0u);
+    if (row < a.n && 2 * byte0 < a.k)
+      cv = *reinterpret_cast<const uint2*>(a.codes + row * kbytes + byte0);
+    const int srow = tid >> 3, sblk = tid & 7;
+    const int64_t blk = k0 / 16 + sblk, row2 = n0 + srow;
+    sv = (row2 < a.n && blk < kscales) ? a.scales[row2 * kscales + blk] : 0;
+#pragma unroll
+    for (int i = 0; i < DYPT; ++i) {
+      const int ch = tid + 256 * i;
+      dv[i] = make_uint4(0u, 0u, 0u, 0u);
+      const int64_t mrow = m0 + (ch >> 2), nn = n0 + 8 * (ch & 3);
+      if (ch < DYCH && mrow < a.m && nn < a.n)
+        dv[i] = *reinterpret_cast<const uint4*>(a.dy + mrow * a.n + nn);
+    }
+  };
+
+  load_step(0);
+  int par = 0;
+  for (int64_t n0 = 0; n0 < a.n; n0 += kStepN, par ^= 1) {
+    // Every wave has finished the previous step's MFMAs (which read wt and
+    // the other dy buffer) and dequantization (which read cs) before it
+    // passes the barrier below; this dy buffer was last read two steps ago.
+    *reinterpret_cast<uint2*>(cs + lr * 64 + lb) = cv;
+    ss[tid] = sv;
+    uint16_t* dyb = dys[par];
+#pragma unroll
+    for (int i = 0; i < DYPT; ++i) {
+      const int ch = tid + 256 * i;
+      if (ch < DYCH) *reinterpret_cast<uint4*>(dyb + (ch >> 2) * kLdsRow + 8 * (ch & 3)) = dv[i];
     }
     __syncthreads();
-    // dequantize: thread -> row cr, 16 columns cb*2 .. cb*2 + 15 (one scale block)
     {
-      const uint2 v = *reinterpret_cast<const uint2*>(cs + cr * 64 + cb);
-      const float sb = e4m3_to_f32(ss[cr * 8 + (cb >> 3)]);
+      const uint2 v = *reinterpret_cast<const uint2*>(cs + dr * 64 + db);
+      const float sb = e4m3_to_f32(ss[dr * 8 + (db >> 3)]);
       const uint4 lo = dequant8_bf16(v.x, sb), hi = dequant8_bf16(v.y, sb);
       const uint32_t wds[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int col = 2 * cb + 2 * e;
-        wt[col * kLdsRow + cr] = (uint16_t)(wds[e] & 0xffffu);
-        wt[(col + 1) * kLdsRow + cr] = (uint16_t)(wds[e] >> 16);
+        const int col = 2 * db + 2 * e;
+        wt[col * kLdsRow + dr] = (uint16_t)(wds[e] & 0xffffu);
+        wt[(col + 1) * kLdsRow + dr] = (uint16_t)(wds[e] >> 16);
       }
     }
     __syncthreads();
+    if (n0 + kStepN < a.n) load_step(n0 + kStepN);
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const uint4 b = *reinterpret_cast<const uint4*>(wt + (32 * wave + c) * kLdsRow + 16 * s + 8 * h);
-      const int64_t nn = n0 + 16 * s + 8 * h;
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const uint4 b = *reinterpret_cast<const uint4*>(wt + (32 * wave + c) * kLdsRow + 16 * s2 + 8 * h);
 #pragma unroll
       for (int u = 0; u < MT; ++u) {
-        const int64_t mrow = m0 + 32 * u + c;
-        uint4 av = make_uint4(0u, 0u, 0u, 0u);
-        if (mrow < a.m && nn < a.n) av = *reinterpret_cast<const uint4*>(a.dy + mrow * a.n + nn);
+        const uint4 av = *reinterpret_cast<const uint4*>(dyb + (32 * u + c) * kLdsRow + 16 * s2 + 8 * h);
         acc[u] = mfma_bf16(av, b, acc[u]);
       }
     }
-    __syncthreads();
   }
+  __syncthreads();
 
   const float S = *a.gscale;
   const int64_t col = k0 + 32 * wave + c;
@@ -138,29 +169,54 @@ __global__ __launch_bounds__(256) void bwd_dx(DxArgs a) {
   }
 }
 
-// out[c, j] (strides oc, oj) = sum_i p[i, c] q[i, j] over the m rows i, for
-// columns c of p [m, cols] (row stride ldp) and j < r of q [.., ldq] bf16;
-// one thread per column, 32 values of j per launch row (blockIdx.y).
+// part[mc][j][c] = sum over the rows i of chunk mc (kOuterRows rows) of
+// p[i, c] q[i, j], for columns c of p [m, cols] (row stride ldp) and j < r
+// of q [.., ldq] (bf16; j in the 32-wide group blockIdx.y).  One thread per
+// column; the chunk's q rows are staged once in LDS as fp32 and read as
+// broadcasts.  outer_reduce sums the chunks in chunk order.
+constexpr int kOuterRows = 256;
+
 __global__ __launch_bounds__(256) void outer_acc(const uint16_t* __restrict__ p, int64_t ldp,
                                                  const uint16_t* __restrict__ q, int64_t ldq,
                                                  int64_t m, int64_t cols, int r,
-                                                 float* __restrict__ out, int64_t oc,
-                                                 int64_t oj) {
+                                                 float* __restrict__ part) {
+  __shared__ float qs[kOuterRows][32];
   const int64_t cidx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int j0 = 32 * blockIdx.y;
+  const int64_t i0 = (int64_t)blockIdx.z * kOuterRows;
+  const int rows = (int)min<int64_t>(kOuterRows, m - i0);
+  for (int e = threadIdx.x; e < kOuterRows * 32; e += 256) {
+    const int i = e >> 5, j = e & 31;
+    qs[i][j] = (i < rows && j0 + j < r) ? bf16_to_f32(q[(i0 + i) * ldq + j0 + j]) : 0.0f;
+  }
+  __syncthreads();
   if (cidx >= cols) return;
   float acc[32];
 #pragma unroll
   for (int j = 0; j < 32; ++j) acc[j] = 0.0f;
-  for (int64_t i = 0; i < m; ++i) {
-    const float pv = bf16_to_f32(p[i * ldp + cidx]);
-    const uint16_t* qr = q + i * ldq + j0;
+  const uint16_t* pc = p + i0 * ldp + cidx;
+  for (int i = 0; i < rows; ++i) {
+    const float pv = bf16_to_f32(pc[(int64_t)i * ldp]);
 #pragma unroll
-    for (int j = 0; j < 32; ++j) acc[j] += pv * bf16_to_f32(j0 + j < r ? qr[j] : 0u);
+    for (int j = 0; j < 32; ++j) acc[j] += pv * qs[i][j];
   }
+  float* dst = part + ((int64_t)blockIdx.z * r) * cols + cidx;
 #pragma unroll
   for (int j = 0; j < 32; ++j)
-    if (j0 + j < r) out[cidx * oc + (int64_t)(j0 + j) * oj] = acc[j];
+    if (j0 + j < r) dst[(int64_t)(j0 + j) * cols] = acc[j];
+}
+
+// out[c * oc + j * oj] = sum over chunks mc (in order) of part[mc][j][c].
+__global__ __launch_bounds__(256) void outer_reduce(const float* __restrict__ part, int mchunks,
+                                                    int64_t cols, int r, float* __restrict__ out,
+                                                    int64_t oc, int64_t oj) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= cols * r) return;
+  const int j = (int)(e / cols);
+  const int64_t c = e - (int64_t)j * cols;
+  float sum = 0.0f;
+  for (int mc = 0; mc < mchunks; ++mc) sum += part[((int64_t)mc * r + j) * cols + c];
+  out[c * oc + (int64_t)j * oj] = sum;
 }
 
 __global__ __launch_bounds__(256) void transpose_b(const uint16_t* __restrict__ b, int64_t n,
@@ -190,6 +246,8 @@ BackwardPlan make_backward_plan(int64_t m, int64_t n, int64_t k, int r) {
   b.off_bt = take(r ? (size_t)r * n * 2 : 0);
   b.off_gpart = take(r ? (size_t)((n + 511) / 512) * mpad * rpad32 * 4 : 0);
   b.off_gs = take(r ? (size_t)mpad * rpad16 * 2 : 0);
+  b.mchunks = (int)((m + kOuterRows - 1) / kOuterRows);
+  b.off_opart = take(r ? (size_t)b.mchunks * r * std::max(n, k) * 4 : 0);
   b.total = off;
   return b;
 }
@@ -242,20 +300,30 @@ hipError_t launch_linear_backward(const BackwardPlan& b, const uint16_t* dy, con
     hipLaunchKernelGGL(bwd_dx<1>, dim3((unsigned)ktiles, (unsigned)mtiles), dim3(256), 0, stream,
                        a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  float* opart = reinterpret_cast<float*>(ws + b.off_opart);
+  auto outer = [&](const uint16_t* pp, int64_t ldp, const uint16_t* qq, int64_t ldq,
+                   int64_t cols, float* out, int64_t oc, int64_t oj) {
+    hipLaunchKernelGGL(outer_acc,
+                       dim3((unsigned)((cols + 255) / 256), (unsigned)((r + 31) / 32),
+                            (unsigned)b.mchunks),
+                       dim3(256), 0, stream, pp, ldp, qq, ldq, p.m, cols, r, opart);
+    hipError_t e2 = hipGetLastError();
+    if (e2 != hipSuccess) return e2;
+    hipLaunchKernelGGL(outer_reduce, dim3((unsigned)((cols * r + 255) / 256)), dim3(256), 0,
+                       stream, opart, b.mchunks, cols, r, out, oc, oj);
+    return hipGetLastError();
+  };
   if (r && da) {
     // dA[j, col] = sum_i gs[i, j] x_t[i, col]
-    hipLaunchKernelGGL(outer_acc, dim3((unsigned)((p.k + 255) / 256), (unsigned)((r + 31) / 32)),
-                       dim3(256), 0, stream, reinterpret_cast<const uint16_t*>(ws + p.off_xt),
-                       p.k, gs, (int64_t)p.rpad16, p.m, p.k, r, da, (int64_t)1, p.k);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    e = outer(reinterpret_cast<const uint16_t*>(ws + p.off_xt), p.k, gs, (int64_t)p.rpad16, p.k,
+              da, (int64_t)1, p.k);
+    if (e != hipSuccess) return e;
   }
   if (r && db) {
     // dB[col, j] = sum_i dy[i, col] t[i, j]
-    hipLaunchKernelGGL(outer_acc, dim3((unsigned)((p.n + 255) / 256), (unsigned)((r + 31) / 32)),
-                       dim3(256), 0, stream, dy, p.n,
-                       reinterpret_cast<const uint16_t*>(ws + p.off_t), (int64_t)p.rpad16, p.m,
-                       p.n, r, db, (int64_t)r, (int64_t)1);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    e = outer(dy, p.n, reinterpret_cast<const uint16_t*>(ws + p.off_t), (int64_t)p.rpad16, p.n,
+              db, (int64_t)r, (int64_t)1);
+    if (e != hipSuccess) return e;
   }
   return hipSuccess;
 }

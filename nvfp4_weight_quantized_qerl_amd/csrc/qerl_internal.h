@@ -100,7 +100,8 @@ hipError_t launch_linear_prefill_main(const LinearPlan& p, const uint8_t* codes,
 // B^T [r, n], the partials of s dy B and gs = bf16(s dy B) [mpad, rpad16].
 struct BackwardPlan {
   LinearPlan fwd;
-  size_t off_bt, off_gpart, off_gs, total;
+  int mchunks;         // 256-row chunks of the dA / dB sums over the tokens
+  size_t off_bt, off_gpart, off_gs, off_opart, total;
 };
 
 BackwardPlan make_backward_plan(int64_t m, int64_t n, int64_t k, int r);
