@@ -49,14 +49,16 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-chain", action="store_true")
-    ap.add_argument("--profile", nargs="?", const="decode", choices=("decode", "prefill", "rmsnorm"),
+    ap.add_argument("--profile", nargs="?", const="decode",
+                    choices=("decode", "prefill", "rmsnorm", "backward"),
                     help="profiling pass for rocprofv3, no timing and no JSON line: "
                          "'decode' runs one plain device copy of COPY_BYTES (counter "
                          "calibration) and PROFILE_LAUNCHES gate/up decode contractions; "
                          "'prefill' runs one prepare and three prefill GEMMs on each of "
                          "the 7B qkv and down layers at M=4096; 'rmsnorm' runs one "
                          "plain device copy (counter calibration) and 20 noisy RMSNorms "
-                         "of 4096 x 3584 rows on rotated inputs")
+                         "of 4096 x 3584 rows on rotated inputs; 'backward' runs three "
+                         "backward calls (dx, dA, dB) of the 7B down layer at M=4096")
     return ap.parse_args()
 
 
@@ -158,6 +160,25 @@ def profile_rmsnorm(q, to_dev, dev, m=4096, d=3584, copies=10, launches=20):
     print(f"profile pass done: copy {COPY_BYTES} B, {launches} noisy RMSNorms {m}x{d}")
 
 
+def profile_backward(q, pc, make_layer, to_dev, dev, calls=3):
+    """Profiling pass of the backward: `calls` qerl_linear_backward calls
+    (dx, dA, dB) of the 7B down layer at M=4096, r=32."""
+    import torch
+    from workloads import normal_bf16
+    s_dn = pc.layers[1]
+    L = make_layer(pc.m, s_dn.n, s_dn.k, pc.r, seed=12, stage=pc.stage, call_id=1)
+    x, w, a, b = to_dev(L.x), to_dev(L.w), to_dev(L.a), to_dev(L.b)
+    codes, scales, S, _ = q.qerl_quantize_nvfp4(w)
+    del w
+    psig = q.qerl_aqn_sigma(pc.sigma_start, pc.sigma_end, pc.num_stages, pc.stage)
+    z = q.qerl_aqn_sample(L.seed, 0, 1, psig, s_dn.k, device=dev)
+    dy = to_dev(normal_bf16((pc.m, s_dn.n), 1.0, 12050))
+    for _ in range(calls):
+        q.qerl_linear_backward(dy, x, codes, scales, S, a, b, pc.lora_scale, z)
+    torch.cuda.synchronize()
+    print(f"profile pass done: {calls} backward calls of the 7B down layer at M={pc.m}")
+
+
 def oracle_step_rate(cfg, layers, M, R, min_seconds=10.0, max_reps=20):
     """The oracle running the decode step on the host: per layer, sample z,
     dequantize the NVFP4 weight and evaluate the fp64 linear layer with the
@@ -223,6 +244,9 @@ def main():
         return
     if args.profile == "rmsnorm":
         profile_rmsnorm(q, to_dev, dev)
+        return
+    if args.profile == "backward":
+        profile_backward(q, CONFIGS["prefill_7b"], make_layer, to_dev, dev)
         return
 
     cfg = CONFIGS["decode_7b_mlp"]
