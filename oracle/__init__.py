@@ -27,6 +27,7 @@ Modules
   linear   y = (x * (1 + z)) W^T + s (x * (1 + z)) A^T B^T in fp64.
   rmsnorm  the noisy RMSNorm producer (w + z) * x / rms(x) (Eq. 10).
   swiglu   SiLU(gate) * up between the gate/up and down layers.
+  mxfp4    the MXFP4 variant (E8M0 scale per 32) and its NVFP4-layout form.
 
 Parity pins (tests/test_oracle_*.py): every function here is checked
 against something other than itself: values printed on the pages
