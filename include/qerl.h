@@ -112,6 +112,43 @@ QERL_API qerl_status qerl_aqn_sigma(double sigma_start, double sigma_end,
                            int32_t num_stages, int32_t stage,
                            double* sigma_out);
 
+/*
+ * qerl_quantize_mxfp4 -- the MXFP4 variant of the weight format [QeRL
+ * summary, §3.4, the formats compared beside NVFP4: E2M1 elements sharing
+ * an E8M0 scale per 32]; the scale rule is the OCP Microscaling v1.0 one:
+ *   X = 2^(floor(log2 amax_b) - 2) per 32 contiguous elements of a row,
+ *   stored as the byte exponent + 127 (clamped to 0..254; 0 for a zero block),
+ *   code = sign | RNE_E2M1(|w| / X), ties to even, saturating at 6.
+ * Codes pack as for NVFP4 (two per byte, the even k in the low nibble).
+ *   w_bf16          device, [n, k] bf16, 16-byte aligned
+ *   n, k            n >= 1, k >= 32, k % 32 == 0
+ *   codes           device out, [n, k/2] bytes, 16-byte aligned
+ *   scales_e8m0     device out, [n, k/32] bytes
+ *   nonfinite_flag  device out, nullable: 1 if w holds an inf or a NaN
+ *                   (the outputs are then unspecified), else 0
+ */
+QERL_API qerl_status qerl_quantize_mxfp4(const void* w_bf16, int64_t n, int64_t k, void* codes,
+                                         void* scales_e8m0, int32_t* nonfinite_flag,
+                                         void* stream);
+
+/*
+ * qerl_mxfp4_to_nvfp4 -- the same MXFP4 weight in this library's NVFP4
+ * layout, exactly: gscale = 2^(E_max - 8) (E_max the largest block
+ * exponent) and each 16-element block scale the E4M3 power of two
+ * 2^(e - E_max + 8) of its 32-block exponent e.  The codes are used as they
+ * are, so (codes, scales_e4m3, gscale) go straight to qerl_linear_decode /
+ * qerl_linear_prefill / qerl_linear_backward.  A block more than 17
+ * octaves below the largest has no E4M3 power of two: its scale is written
+ * as 0 and, if any of its codes is nonzero, *range_flag is set to 1.
+ *   codes, scales_e8m0   from qerl_quantize_mxfp4 ([n, k/2], [n, k/32])
+ *   scales_e4m3          device out, [n, k/16] bytes
+ *   gscale               device out, 1 float
+ *   range_flag           device out, nullable
+ */
+QERL_API qerl_status qerl_mxfp4_to_nvfp4(const void* codes, const void* scales_e8m0, int64_t n,
+                                         int64_t k, void* scales_e4m3, float* gscale,
+                                         int32_t* range_flag, void* stream);
+
 /* Decay schedules of qerl_aqn_sigma_schedule. */
 typedef enum {
   QERL_SCHEDULE_EXPONENTIAL = 0, /* Eq. 8, as qerl_aqn_sigma              */

@@ -222,3 +222,28 @@ def qerl_linear_backward(dy, x, codes, scales, gscale, lora_a=None, lora_b=None,
                                     workspace.numel(), _stream(dy.device)),
            "qerl_linear_backward")
     return dx, da, db
+
+
+def qerl_quantize_mxfp4(w):
+    """bf16 W [n, k] -> (codes uint8 [n, k/2], E8M0 scales uint8 [n, k/32],
+    nonfinite flag int32 [1]) on W's device."""
+    w = _bits16(w, "w")
+    n, k = w.shape
+    codes = torch.empty((n, k // 2), dtype=torch.uint8, device=w.device)
+    scales = torch.empty((n, k // 32), dtype=torch.uint8, device=w.device)
+    flag = torch.empty(1, dtype=torch.int32, device=w.device)
+    _check(lib.qerl_quantize_mxfp4(_ptr(w), n, k, _ptr(codes), _ptr(scales), _ptr(flag),
+                                   _stream(w.device)), "qerl_quantize_mxfp4")
+    return codes, scales, flag
+
+
+def qerl_mxfp4_to_nvfp4(codes, scales_e8m0):
+    """(E4M3 scales [n, k/16], gscale [1], range flag [1]) expressing the MXFP4
+    weight in the NVFP4 layout the linear calls take (with the same codes)."""
+    n, k = codes.shape[0], codes.shape[1] * 2
+    s4 = torch.empty((n, k // 16), dtype=torch.uint8, device=codes.device)
+    g = torch.empty(1, dtype=torch.float32, device=codes.device)
+    flag = torch.empty(1, dtype=torch.int32, device=codes.device)
+    _check(lib.qerl_mxfp4_to_nvfp4(_ptr(codes), _ptr(scales_e8m0), n, k, _ptr(s4), _ptr(g),
+                                   _ptr(flag), _stream(codes.device)), "qerl_mxfp4_to_nvfp4")
+    return s4, g, flag

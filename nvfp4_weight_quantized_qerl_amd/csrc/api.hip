@@ -55,7 +55,7 @@ const char* qerl_status_string(int status) {
   }
 }
 
-int qerl_abi_version(void) { return 6; }
+int qerl_abi_version(void) { return 7; }
 
 qerl_status qerl_quantize_nvfp4(const void* w_bf16, int64_t n, int64_t k, void* codes,
                                 void* scales, float* gscale, int32_t* nonfinite_flag,
@@ -87,6 +87,29 @@ qerl_status qerl_aqn_sigma(double sigma_start, double sigma_end, int32_t num_sta
                  std::pow(ratio, (double)(stage - 1) / (double)(num_stages - 1));
   }
   return QERL_OK;
+}
+
+qerl_status qerl_quantize_mxfp4(const void* w_bf16, int64_t n, int64_t k, void* codes,
+                                void* scales_e8m0, int32_t* nonfinite_flag, void* stream) {
+  if (!w_bf16 || !codes || !scales_e8m0) return QERL_ERR_NULL;
+  if (n < 1 || k < 32 || k % 32) return QERL_ERR_SHAPE;
+  if (!aligned(w_bf16, 16) || !aligned(codes, 16) || (nonfinite_flag && !aligned(nonfinite_flag, 4)))
+    return QERL_ERR_ALIGN;
+  return from_hip(qerl::launch_quantize_mxfp4(
+      static_cast<const uint16_t*>(w_bf16), n, k, static_cast<uint8_t*>(codes),
+      static_cast<uint8_t*>(scales_e8m0), nonfinite_flag, static_cast<hipStream_t>(stream)));
+}
+
+qerl_status qerl_mxfp4_to_nvfp4(const void* codes, const void* scales_e8m0, int64_t n, int64_t k,
+                                void* scales_e4m3, float* gscale, int32_t* range_flag,
+                                void* stream) {
+  if (!codes || !scales_e8m0 || !scales_e4m3 || !gscale) return QERL_ERR_NULL;
+  if (n < 1 || k < 32 || k % 32) return QERL_ERR_SHAPE;
+  if (!aligned(codes, 16) || !aligned(gscale, 4) || (range_flag && !aligned(range_flag, 4)))
+    return QERL_ERR_ALIGN;
+  return from_hip(qerl::launch_mxfp4_to_nvfp4(
+      static_cast<const uint8_t*>(codes), static_cast<const uint8_t*>(scales_e8m0), n, k,
+      static_cast<uint8_t*>(scales_e4m3), gscale, range_flag, static_cast<hipStream_t>(stream)));
 }
 
 qerl_status qerl_aqn_sigma_schedule(int32_t mode, double sigma_start, double sigma_end,

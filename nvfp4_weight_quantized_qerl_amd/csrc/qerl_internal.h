@@ -17,6 +17,13 @@ hipError_t launch_quantize(const uint16_t* w, int64_t n, int64_t k,
                            uint8_t* codes, uint8_t* scales, float* gscale,
                            int32_t* flag, hipStream_t stream);
 
+// MXFP4 (E8M0 scale per 32): quantize, and re-express the scales in the
+// NVFP4 layout (E4M3 per 16 + FP32 S) so the NVFP4 kernels run it exactly.
+hipError_t launch_quantize_mxfp4(const uint16_t* w, int64_t n, int64_t k, uint8_t* codes,
+                                 uint8_t* scales, int32_t* flag, hipStream_t stream);
+hipError_t launch_mxfp4_to_nvfp4(const uint8_t* codes, const uint8_t* s8, int64_t n, int64_t k,
+                                 uint8_t* s4, float* gscale, int32_t* flag, hipStream_t stream);
+
 // -------------------------------------------------------------------- noise
 hipError_t launch_aqn_sample(uint64_t seed, uint64_t stream_id,
                              uint64_t call_id, double sigma, int64_t d,

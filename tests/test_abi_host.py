@@ -41,7 +41,7 @@ def test_status_strings():
     for s in range(7):
         assert lib.qerl_status_string(s).decode().startswith("QERL_")
     assert b"unknown" in lib.qerl_status_string(99)
-    assert lib.qerl_abi_version() == 6
+    assert lib.qerl_abi_version() == 7
 
 
 FAKE = ctypes.c_void_p(0x10000)        # aligned, never dereferenced on error
@@ -145,6 +145,17 @@ def test_backward_validation_and_workspace():
     assert call(a10=129) == 4 and call(a11=float("nan")) == 4
     assert call(a0=MIS) == 3 and call(a7=MIS) == 3 and call(a16=MIS) == 3
     assert call(a17=16) == 5
+
+
+def test_mxfp4_validation():
+    f = lib.qerl_quantize_mxfp4
+    assert f(None, 4, 64, FAKE, FAKE, None, None) == 1
+    assert f(FAKE, 4, 48, FAKE, FAKE, None, None) == 2 and f(FAKE, 0, 64, FAKE, FAKE, None, None) == 2
+    assert f(MIS, 4, 64, FAKE, FAKE, None, None) == 3
+    g = lib.qerl_mxfp4_to_nvfp4
+    assert g(FAKE, FAKE, 4, 64, FAKE, None, None, None) == 1
+    assert g(FAKE, FAKE, 4, 16, FAKE, FAKE, None, None) == 2
+    assert g(MIS, FAKE, 4, 64, FAKE, FAKE, None, None) == 3
 
 
 def test_workspace_sizes():
