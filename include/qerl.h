@@ -322,6 +322,28 @@ QERL_API qerl_status qerl_linear_prefill_prepared(
     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * qerl_linear_decode_mxfp4 / qerl_linear_decode_prepared_mxfp4 -- the
+ * same operations and arguments as qerl_linear_decode /
+ * qerl_linear_decode_prepared, for an MXFP4 weight in the NVFP4 layout
+ * (qerl_mxfp4_to_nvfp4): every block scale is then a power of two, which
+ * lets the decode kernel form each pair of bf16 weight values with one
+ * scaled-conversion instruction.  The result is bit-identical to the
+ * general call on the same arguments; block scales that are not powers of
+ * two give wrong results.
+ */
+QERL_API qerl_status qerl_linear_decode_mxfp4(const void* x, int64_t m, const void* codes,
+                                              const void* scales, const float* gscale,
+                                              int64_t n, int64_t k, const void* lora_a,
+                                              const void* lora_b, int32_t r, float lora_scale,
+                                              const float* z, void* y, void* workspace,
+                                              size_t workspace_bytes, void* stream);
+
+QERL_API qerl_status qerl_linear_decode_prepared_mxfp4(
+    int64_t m, const void* codes, const void* scales, const float* gscale, int64_t n, int64_t k,
+    const void* lora_b, int32_t r, void* y, void* workspace, size_t workspace_bytes,
+    void* stream);
+
+/*
  * qerl_linear_backward -- gradients of the layer through the frozen NVFP4
  * weight.  The rollout's log-probabilities are taken on the same quantized
  * model and only the LoRA factors (and RMSNorm scales) are trained

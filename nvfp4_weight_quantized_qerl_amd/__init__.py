@@ -247,3 +247,17 @@ def qerl_mxfp4_to_nvfp4(codes, scales_e8m0):
     _check(lib.qerl_mxfp4_to_nvfp4(_ptr(codes), _ptr(scales_e8m0), n, k, _ptr(s4), _ptr(g),
                                    _ptr(flag), _stream(codes.device)), "qerl_mxfp4_to_nvfp4")
     return s4, g, flag
+
+
+def qerl_linear_decode_mxfp4(x, codes, scales, gscale, lora_a=None, lora_b=None, lora_scale=0.0,
+                             z=None, workspace=None, y=None):
+    """qerl_linear_decode for an MXFP4 weight in the NVFP4 layout (power-of-two
+    block scales, from qerl_mxfp4_to_nvfp4)."""
+    return _linear("qerl_linear_decode_mxfp4", x, codes, scales, gscale, lora_a, lora_b,
+                   lora_scale, z, workspace, y)
+
+
+def qerl_linear_decode_prepared_mxfp4(m, codes, scales, gscale, k, lora_b, y, workspace):
+    """qerl_linear_decode_prepared for power-of-two block scales."""
+    return _prepared("qerl_linear_decode_prepared_mxfp4", m, codes, scales, gscale, k, lora_b, y,
+                     workspace)

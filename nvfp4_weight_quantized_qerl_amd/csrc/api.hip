@@ -55,7 +55,7 @@ const char* qerl_status_string(int status) {
   }
 }
 
-int qerl_abi_version(void) { return 7; }
+int qerl_abi_version(void) { return 8; }
 
 qerl_status qerl_quantize_nvfp4(const void* w_bf16, int64_t n, int64_t k, void* codes,
                                 void* scales, float* gscale, int32_t* nonfinite_flag,
@@ -218,7 +218,8 @@ static qerl_status linear_full(bool prefill, const void* x, int64_t m, const voi
                                const void* scales, const float* gscale, int64_t n,
                                int64_t k, const void* lora_a, const void* lora_b,
                                int32_t r, float lora_scale, const float* z, void* y,
-                               void* workspace, size_t workspace_bytes, void* stream) {
+                               void* workspace, size_t workspace_bytes, void* stream,
+                               bool pow2 = false) {
   if (!x) return QERL_ERR_NULL;
   if (r > 0 && (!lora_a) != (!lora_b)) return QERL_ERR_NULL;
   const int32_t r_eff = (r > 0 && lora_a && lora_b) ? r : 0;
@@ -229,6 +230,7 @@ static qerl_status linear_full(bool prefill, const void* x, int64_t m, const voi
   if (s != QERL_OK) return s;
   s = check_prepare(x, r_eff ? lora_a : nullptr, r_eff);
   if (s != QERL_OK) return s;
+  plan.pow2_scales = pow2;
   hipStream_t st = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   hipError_t e = qerl::launch_linear_prepare(plan, static_cast<const uint16_t*>(x), z,
@@ -284,12 +286,14 @@ qerl_status qerl_linear_prepare(const void* x, int64_t m, int64_t n, int64_t k,
 static qerl_status linear_prepared(bool prefill, int64_t m, const void* codes,
                                    const void* scales, const float* gscale, int64_t n,
                                    int64_t k, const void* lora_b, int32_t r, void* y,
-                                   void* workspace, size_t workspace_bytes, void* stream) {
+                                   void* workspace, size_t workspace_bytes, void* stream,
+                                   bool pow2 = false) {
   if (r > 0 && !lora_b) return QERL_ERR_NULL;
   qerl::LinearPlan plan;
   qerl_status s = check_linear(nullptr, m, codes, scales, gscale, n, k, r, 1.0f, nullptr, y,
                                workspace, workspace_bytes, &plan);
   if (s != QERL_OK) return s;
+  plan.pow2_scales = pow2;
   const uint8_t* c = static_cast<const uint8_t*>(codes);
   const uint8_t* sc = static_cast<const uint8_t*>(scales);
   const uint16_t* b = r > 0 ? static_cast<const uint16_t*>(lora_b) : nullptr;
@@ -316,6 +320,24 @@ qerl_status qerl_linear_prefill_prepared(int64_t m, const void* codes, const voi
                                          void* stream) {
   return linear_prepared(true, m, codes, scales, gscale, n, k, lora_b, r, y, workspace,
                          workspace_bytes, stream);
+}
+
+qerl_status qerl_linear_decode_mxfp4(const void* x, int64_t m, const void* codes,
+                                     const void* scales, const float* gscale, int64_t n,
+                                     int64_t k, const void* lora_a, const void* lora_b,
+                                     int32_t r, float lora_scale, const float* z, void* y,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  return linear_full(false, x, m, codes, scales, gscale, n, k, lora_a, lora_b, r, lora_scale, z,
+                     y, workspace, workspace_bytes, stream, true);
+}
+
+qerl_status qerl_linear_decode_prepared_mxfp4(int64_t m, const void* codes, const void* scales,
+                                              const float* gscale, int64_t n, int64_t k,
+                                              const void* lora_b, int32_t r, void* y,
+                                              void* workspace, size_t workspace_bytes,
+                                              void* stream) {
+  return linear_prepared(false, m, codes, scales, gscale, n, k, lora_b, r, y, workspace,
+                         workspace_bytes, stream, true);
 }
 
 }  // extern "C"

@@ -170,7 +170,8 @@ hipError_t run_decode_lds(const LinearPlan& p, int mt, const uint8_t* codes,
                           const uint16_t* lora_b, int r, int lora_vec, const uint16_t* xt,
                           uint16_t* y, int m_valid, int64_t m0_chunk, char* ws,
                           hipStream_t stream) {
-  dlds::Kernel kern = mt == 1 ? dlds::pick_mt1(p.dec_nt) : dlds::pick_mt2(p.dec_nt);
+  dlds::Kernel kern = mt == 1 ? dlds::pick_mt1(p.dec_nt, p.pow2_scales)
+                              : dlds::pick_mt2(p.dec_nt, p.pow2_scales);
   if (!kern) return hipErrorInvalidConfiguration;
   dlds::Args a;
   a.xt = xt;

@@ -147,7 +147,10 @@ __device__ __forceinline__ void epilogue_tile(const Args& a, f32x16_t acc, float
   }
 }
 
-template <int MT, int NT>
+// P2: every block scale is a power of two (an MXFP4 weight in the NVFP4
+// layout), so one v_cvt_scalef32_pk_bf16_fp4 turns two codes straight into
+// their exact bf16 products with the scale; otherwise the general route.
+template <int MT, int NT, bool P2 = false>
 __global__ __launch_bounds__(512, 1) void decode_lds(Args a) {
   constexpr int XROWS = 32 * MT;              // token rows
   constexpr int WROWS = 32 * NT;              // weight rows staged per block
@@ -256,7 +259,8 @@ __global__ __launch_bounds__(512, 1) void decode_lds(Args a) {
     for (int j = 0; j < 4; ++j) {
 #pragma unroll
       for (int t = 0; t < NTH; ++t) {
-        const uint4 b = dequant8_bf16(comp(w[t], j), j < 2 ? sb0[t] : sb1[t]);
+        const uint4 b = P2 ? dequant8_bf16_pow2(comp(w[t], j), j < 2 ? sb0[t] : sb1[t])
+                           : dequant8_bf16(comp(w[t], j), j < 2 ? sb0[t] : sb1[t]);
 #pragma unroll
         for (int u = 0; u < MT; ++u) acc[t][u] = mfma_bf16(xa[j][u], b, acc[t][u]);
       }
@@ -384,20 +388,20 @@ __global__ __launch_bounds__(512, 1) void decode_lds(Args a) {
 
 typedef void (*Kernel)(Args);
 
-template <int MT>
+template <int MT, bool P2 = false>
 Kernel pick_nt(int nt) {
   switch (nt) {
-    case 1: return decode_lds<MT, 1>;
-    case 2: return decode_lds<MT, 2>;
-    case 3: return decode_lds<MT, 3>;
-    case 4: return decode_lds<MT, 4>;
-    case 5: return decode_lds<MT, 5>;
+    case 1: return decode_lds<MT, 1, P2>;
+    case 2: return decode_lds<MT, 2, P2>;
+    case 3: return decode_lds<MT, 3, P2>;
+    case 4: return decode_lds<MT, 4, P2>;
+    case 5: return decode_lds<MT, 5, P2>;
     default: return nullptr;
   }
 }
 
-Kernel pick_mt1(int nt);
-Kernel pick_mt2(int nt);
+Kernel pick_mt1(int nt, bool p2);
+Kernel pick_mt2(int nt, bool p2);
 
 }  // namespace dlds
 }  // namespace qerl

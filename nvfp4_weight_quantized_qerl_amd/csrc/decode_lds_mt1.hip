@@ -4,7 +4,7 @@
 namespace qerl {
 namespace dlds {
 
-Kernel pick_mt1(int nt) { return pick_nt<1>(nt); }
+Kernel pick_mt1(int nt, bool p2) { return p2 ? pick_nt<1, true>(nt) : pick_nt<1>(nt); }
 
 }  // namespace dlds
 }  // namespace qerl

@@ -73,6 +73,18 @@ __device__ __forceinline__ uint4 dequant8_bf16(uint32_t codes, float sb) {
   return r;
 }
 
+// The same for a power-of-two scale sb: v_cvt_scalef32_pk_bf16_fp4 applies
+// the power-of-two part of its scale operand, which is all of sb, so each
+// instruction gives two exact bf16 products (byte i holds codes 2i, 2i+1).
+__device__ __forceinline__ uint4 dequant8_bf16_pow2(uint32_t codes, float sb) {
+  uint4 r;
+  r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sb, 0));
+  r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sb, 1));
+  r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sb, 2));
+  r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sb, 3));
+  return r;
+}
+
 __device__ __forceinline__ f32x16_t mfma_bf16(uint4 a, uint4 b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c,
                                                  0, 0, 0);

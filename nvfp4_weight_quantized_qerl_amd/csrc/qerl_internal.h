@@ -55,6 +55,9 @@ struct LinearPlan {
   int dec_groups;      // row groups = ceil(n / dec_rows)
   int dec_split;       // K splits across workgroups
   int64_t dec_kblk_per_split;  // 64-wide K blocks per split
+  // every block scale is a power of two (MXFP4 in the NVFP4 layout): the
+  // LDS-staged decode kernel may use its single-instruction dequantization
+  bool pow2_scales;
   // prefill main kernel
   int pf_tile_m, pf_tile_n;
   // workspace byte offsets

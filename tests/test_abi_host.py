@@ -41,7 +41,7 @@ def test_status_strings():
     for s in range(7):
         assert lib.qerl_status_string(s).decode().startswith("QERL_")
     assert b"unknown" in lib.qerl_status_string(99)
-    assert lib.qerl_abi_version() == 7
+    assert lib.qerl_abi_version() == 8
 
 
 FAKE = ctypes.c_void_p(0x10000)        # aligned, never dereferenced on error

@@ -82,3 +82,18 @@ def test_mxfp4_layer(m, n, k, r, entry):
     err = linear.max_rel_error(formats.bf16_bits_to_f64(host(y).reshape(m, n)), ref)
     print(f"mxfp4 layer {entry} m={m} n={n} k={k} err={err:.4g}", flush=True)
     assert err <= 2e-2
+
+
+@pytest.mark.parametrize("m,n,k,r", [(64, 37888 // 8, 3584, 32), (50, 1024, 18944, 32), (3, 160, 512, 8)])
+def test_power_of_two_decode_is_bit_identical(m, n, k, r):
+    # the scaled-conversion dequantization gives the same bf16 weights, so the
+    # whole result must match the general decode call bit for bit
+    L = make_layer(m, n, k, r, seed=44, outlier_frac=0.001, stage=1)
+    codes, scales, _ = q.qerl_quantize_mxfp4(dev16(L.w))
+    s4, g, _ = q.qerl_mxfp4_to_nvfp4(codes, scales)
+    z = q.qerl_aqn_sample(L.seed, 0, 0, 1e-2, k, device="cuda:0")
+    args = (dev16(L.x), codes, s4, g, dev16(L.a), dev16(L.b), L.lora_scale, z)
+    y0 = q.qerl_linear_decode(*args)
+    y1 = q.qerl_linear_decode_mxfp4(*args)
+    torch.cuda.synchronize()
+    assert torch.equal(y0.view(torch.int16), y1.view(torch.int16))
