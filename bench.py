@@ -18,6 +18,8 @@ timed region.
 Printed: one JSON line.  `value` = decode weight-stream GB/s (algorithmic
 bytes of the step / step time); `roofline` = the decode contraction kernel
 of the gate/up layer, timed alone with HIP events on its launch stream;
+`mxfp4_decode` = the gate/up contraction on the weight quantized to MXFP4
+(general and power-of-two dequantization);
 `mlp_chain` = the same weights run as one chained feed-forward block (noisy
 RMSNorm -> gate/up -> SiLU(gate) * up -> down) per step;
 `prefill` = the 4096-token prefill of the Qwen2.5-7B qkv and down layers
@@ -401,6 +403,41 @@ def main():
                  "GB_per_s": round(chain_bytes / t_chain / 1e9, 1),
                  "frac_hbm": round(chain_bytes / t_chain / 1e9 / HBM_PEAK_GBS, 4)}
 
+    # ---- the gate/up weight as MXFP4 (E8M0 per 32) in the NVFP4 layout: the
+    # contraction with the general dequantization and with the power-of-two
+    # one, same rotation and workspace as the NVFP4 roofline pass below
+    mx = None
+    if not args.no_chain:
+        gl = layers[0]
+        Lg = make_layer(M, gl["n"], gl["k"], R, seed=1, stage=cfg.stage,
+                        outlier_frac=cfg.outlier_frac, call_id=0)
+        mcodes, ms8, _ = q.qerl_quantize_mxfp4(to_dev(Lg.w))
+        ms4, mg, mflag = q.qerl_mxfp4_to_nvfp4(mcodes, ms8)
+        mrot = [(mcodes, ms4)] + [(mcodes.clone(), ms4.clone()) for _ in range(copies - 1)]
+        q.qerl_linear_prepare(gl["x"], gl["n"], gl["a"], cfg.lora_scale, zring[0][0], gl["ws"])
+        mx = {"workload": "gate/up 37888x3584 MXFP4 weight in the NVFP4 layout, M=64, r=32",
+              "range_flag": int(mflag.item())}
+        mx_bytes = main_kernel_bytes(M, gl["n"], gl["k"], R)
+        # three interleaved rounds, median per variant (box noise is ~±5%)
+        mx_t = {"general_us": [], "pow2_us": []}
+        for _ in range(3):
+            for name, fn in (("general_us", q.qerl_linear_decode_prepared),
+                             ("pow2_us", q.qerl_linear_decode_prepared_mxfp4)):
+                for i in range(5):
+                    fn(M, *mrot[i % copies], mg, gl["k"], gl["b"], gl["y"], gl["ws"])
+                m0 = torch.cuda.Event(enable_timing=True)
+                m1 = torch.cuda.Event(enable_timing=True)
+                m0.record(stream)
+                for i in range(max(20, args.steps)):
+                    fn(M, *mrot[i % copies], mg, gl["k"], gl["b"], gl["y"], gl["ws"])
+                m1.record(stream)
+                m1.synchronize()
+                mx_t[name].append(m0.elapsed_time(m1) * 1e3 / max(20, args.steps))
+        for name, v in mx_t.items():
+            mx[name] = round(sorted(v)[1], 2)
+        mx["pow2_GB_per_s"] = round(mx_bytes / (mx["pow2_us"] * 1e-6) / 1e9, 1)
+        del mrot, mcodes, ms8, ms4
+
     # ---- dominant kernel alone: gate/up contraction, HIP events on its stream
     ly = layers[0]
     q.qerl_linear_prepare(ly["x"], ly["n"], ly["a"], cfg.lora_scale, zring[0][0], ly["ws"])
@@ -553,6 +590,7 @@ def main():
         "rmsnorm": rmsnorm,
         "mlp_chain": chain,
         "backward": backward,
+        "mxfp4_decode": mx,
         "quantizer": {"GB_per_s": round(q_bytes / min(qtimes) / 1e9, 1),
                       "elements": q_elems, "bytes_per_elem": 2.5625},
         "cpu_baseline": cpu,
