@@ -12,10 +12,10 @@
 // each of dA and dB an accumulation over 256-row chunks plus a reduction of
 // the chunks in order.
 //
-// dx contraction (bwd_dx<MT>): a workgroup of four waves owns 32 MT token
-// rows x 128 output columns (input channels k); wave w the columns
+// dx contraction (bwd_dx<MT>): a workgroup of eight waves owns 32 MT token
+// rows x 256 output columns (input channels k); wave w the columns
 // 32 w .. 32 w + 31.  The sum runs over the weight rows n in steps of 32:
-// the workgroup copies the codes (32 rows x 64 B) and scales of the step,
+// the workgroup copies the codes (32 rows x 128 B) and scales of the step,
 // dequantizes them (E2M1 code x E4M3 scale, exact in bf16) into an LDS tile
 // stored transposed, [k][n] with rows padded to 40 elements (80 B) so that
 // the MFMA operand reads (lane = column k, eight consecutive n) of 16 lanes
@@ -33,7 +33,10 @@
 namespace qerl {
 namespace {
 
-constexpr int kTileK = 128;     // output columns per workgroup
+constexpr int kTileK = 256;     // output columns per workgroup (eight waves of 32)
+constexpr int kThreads = 512;
+constexpr int kCodeRow = kTileK / 2;     // code bytes of one weight row of the tile
+constexpr int kScaleRow = kTileK / 16;   // scale bytes of one weight row of the tile
 constexpr int kStepN = 32;      // weight rows per step
 constexpr int kLdsRow = 40;     // padded LDS row (elements) of the transposed tile
 
@@ -51,10 +54,10 @@ struct DxArgs {
 };
 
 template <int MT>
-__global__ __launch_bounds__(256) void bwd_dx(DxArgs a) {
+__global__ __launch_bounds__(kThreads) void bwd_dx(DxArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t wt[kTileK * kLdsRow];
-  __shared__ __attribute__((aligned(16))) uint8_t cs[kStepN * 64];
-  __shared__ uint8_t ss[kStepN * 8];
+  __shared__ __attribute__((aligned(16))) uint8_t cs[kStepN * kCodeRow];
+  __shared__ uint8_t ss[kStepN * kScaleRow];
   // dy tile of the step, [32 MT rows][40] bf16, two buffers (step parity)
   __shared__ __attribute__((aligned(16))) uint16_t dys[2][32 * MT * kLdsRow];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -62,8 +65,9 @@ __global__ __launch_bounds__(256) void bwd_dx(DxArgs a) {
   const int64_t k0 = (int64_t)blockIdx.x * kTileK;
   const int64_t m0 = (int64_t)blockIdx.y * 32 * MT;
   const int64_t kbytes = a.k / 2, kscales = a.k / 16;
-  // copy roles: thread -> weight row tid / 8 of the step, 8 code bytes at (tid % 8) * 8
-  const int lr = tid >> 3, lb = (tid & 7) * 8;
+  // copy roles: thread -> weight row tid / 16 of the step, 8 code bytes at (tid % 16) * 8
+  // (and the scale byte tid % 16 of the same row)
+  const int lr = tid / (kCodeRow / 8), lb = (tid % (kCodeRow / 8)) * 8;
   // dequantization roles: thread -> row tid % 32, 16 columns at 16 (tid / 32); rows
   // vary fastest across the lanes so the transposed LDS writes spread over the banks
   const int dr = tid & 31, db = (tid >> 5) * 8;
@@ -74,7 +78,7 @@ __global__ __launch_bounds__(256) void bwd_dx(DxArgs a) {
   // Global operands of one step, held in registers one step ahead: the
   // dy tile goes 16 bytes per thread-chunk (row ch / 4, columns 8 (ch % 4)).
   constexpr int DYCH = 32 * MT * 4;               // 16-byte chunks of the dy tile
-  constexpr int DYPT = (DYCH + 255) / 256;        // chunks per thread
+  constexpr int DYPT = (DYCH + kThreads - 1) / kThreads;   // chunks per thread
   uint2 cv;
   uint8_t sv;
   uint4 dv[DYPT];
@@ -84,12 +88,12 @@ __global__ __launch_bounds__(256) void bwd_dx(DxArgs a) {
     cv = make_uint2(0u, 0u);
     if (row < a.n && 2 * byte0 < a.k)
       cv = *reinterpret_cast<const uint2*>(a.codes + row * kbytes + byte0);
-    const int srow = tid >> 3, sblk = tid & 7;
+    const int srow = tid / kScaleRow, sblk = tid % kScaleRow;
     const int64_t blk = k0 / 16 + sblk, row2 = n0 + srow;
     sv = (row2 < a.n && blk < kscales) ? a.scales[row2 * kscales + blk] : 0;
 #pragma unroll
     for (int i = 0; i < DYPT; ++i) {
-      const int ch = tid + 256 * i;
+      const int ch = tid + kThreads * i;
       dv[i] = make_uint4(0u, 0u, 0u, 0u);
       const int64_t mrow = m0 + (ch >> 2), nn = n0 + 8 * (ch & 3);
       if (ch < DYCH && mrow < a.m && nn < a.n)
@@ -103,18 +107,18 @@ __global__ __launch_bounds__(256) void bwd_dx(DxArgs a) {
     // Every wave has finished the previous step's MFMAs (which read wt and
     // the other dy buffer) and dequantization (which read cs) before it
     // passes the barrier below; this dy buffer was last read two steps ago.
-    *reinterpret_cast<uint2*>(cs + lr * 64 + lb) = cv;
+    *reinterpret_cast<uint2*>(cs + lr * kCodeRow + lb) = cv;
     ss[tid] = sv;
     uint16_t* dyb = dys[par];
 #pragma unroll
     for (int i = 0; i < DYPT; ++i) {
-      const int ch = tid + 256 * i;
+      const int ch = tid + kThreads * i;
       if (ch < DYCH) *reinterpret_cast<uint4*>(dyb + (ch >> 2) * kLdsRow + 8 * (ch & 3)) = dv[i];
     }
     __syncthreads();
     {
-      const uint2 v = *reinterpret_cast<const uint2*>(cs + dr * 64 + db);
-      const float sb = e4m3_to_f32(ss[dr * 8 + (db >> 3)]);
+      const uint2 v = *reinterpret_cast<const uint2*>(cs + dr * kCodeRow + db);
+      const float sb = e4m3_to_f32(ss[dr * kScaleRow + (db >> 3)]);
       const uint4 lo = dequant8_bf16(v.x, sb), hi = dequant8_bf16(v.y, sb);
       const uint32_t wds[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
 #pragma unroll
@@ -291,14 +295,14 @@ hipError_t launch_linear_backward(const BackwardPlan& b, const uint16_t* dy, con
   const int64_t ktiles = (p.k + kTileK - 1) / kTileK;
   const int64_t mtiles = p.mpad / 32;
   if (mtiles >= 4 && mtiles % 4 == 0)
-    hipLaunchKernelGGL(bwd_dx<4>, dim3((unsigned)ktiles, (unsigned)(mtiles / 4)), dim3(256), 0,
-                       stream, a);
+    hipLaunchKernelGGL(bwd_dx<4>, dim3((unsigned)ktiles, (unsigned)(mtiles / 4)), dim3(kThreads),
+                       0, stream, a);
   else if (mtiles % 2 == 0)
-    hipLaunchKernelGGL(bwd_dx<2>, dim3((unsigned)ktiles, (unsigned)(mtiles / 2)), dim3(256), 0,
-                       stream, a);
+    hipLaunchKernelGGL(bwd_dx<2>, dim3((unsigned)ktiles, (unsigned)(mtiles / 2)), dim3(kThreads),
+                       0, stream, a);
   else
-    hipLaunchKernelGGL(bwd_dx<1>, dim3((unsigned)ktiles, (unsigned)mtiles), dim3(256), 0, stream,
-                       a);
+    hipLaunchKernelGGL(bwd_dx<1>, dim3((unsigned)ktiles, (unsigned)mtiles), dim3(kThreads), 0,
+                       stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   float* opart = reinterpret_cast<float*>(ws + b.off_opart);
   auto outer = [&](const uint16_t* pp, int64_t ldp, const uint16_t* qq, int64_t ldq,
