@@ -225,9 +225,9 @@ def oracle_step_rate(cfg, layers, M, R, min_seconds=10.0, max_reps=20):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not "
-              "supported (the layer would shard by output rows with no exchange; see "
-              "DESIGN.md)", file=sys.stderr)
+        print(f"bench.py: one GPU only; --gpus {args.gpus} is not supported (the layer "
+              "would shard by output rows, with one scalar max of amax before quantizing "
+              "and no other exchange)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

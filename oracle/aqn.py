@@ -14,7 +14,7 @@ sigma_start).
 Noise [QeRL summary, §3.4 "The stochastic noise vector", Eq. 7]:
 Z_noisy ~ N(0, sigma^2 I), a vector of length d = the layer's input
 dimension, drawn afresh for every forward pass.  The pages do not say how
-the normal numbers are produced.  Both sides of this build use
+the normal numbers are produced.  The oracle and the HIP library both use
   * Philox4x64-10, the counter-based generator of Salmon, Moraes, Dror and
     Shaw, "Parallel random numbers: as easy as 1, 2, 3" (SC'11), with
       key     = (seed, stream_id)
