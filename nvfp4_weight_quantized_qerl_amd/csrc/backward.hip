@@ -20,7 +20,8 @@
 // stored transposed, [k][n] with rows padded to 40 elements (80 B) so that
 // the MFMA operand reads (lane = column k, eight consecutive n) of 16 lanes
 // hit 16 different bank groups, and runs two 32x32x16 bf16 MFMAs per token
-// tile.  The dy tile of the step is copied to LDS with 16-byte loads (rows
+// tile.  A dequantizing lane takes two adjacent weight rows, so each of its
+// transposed writes is one dword holding both rows of a column.  The dy tile of the step is copied to LDS with 16-byte loads (rows
 // padded to 40 elements like the weight tile, two buffers) and read by the
 // MFMAs with lane = token row.  The codes, scales and dy of the next step
 // are loaded into registers while the current step's MFMAs run; two
@@ -36,7 +37,9 @@ namespace {
 constexpr int kTileK = 256;     // output columns per workgroup (eight waves of 32)
 constexpr int kThreads = 512;
 constexpr int kCodeRow = kTileK / 2;     // code bytes of one weight row of the tile
+constexpr int kCodeLds = kCodeRow + 4;   // its LDS row: 33 dwords, so rows 2p hit distinct banks
 constexpr int kScaleRow = kTileK / 16;   // scale bytes of one weight row of the tile
+constexpr int kScaleLds = kScaleRow + 4; // its LDS row: 5 dwords, so rows 2p hit distinct banks
 constexpr int kStepN = 32;      // weight rows per step
 constexpr int kLdsRow = 40;     // padded LDS row (elements) of the transposed tile
 
@@ -56,8 +59,8 @@ struct DxArgs {
 template <int MT>
 __global__ __launch_bounds__(kThreads) void bwd_dx(DxArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t wt[kTileK * kLdsRow];
-  __shared__ __attribute__((aligned(16))) uint8_t cs[kStepN * kCodeRow];
-  __shared__ uint8_t ss[kStepN * kScaleRow];
+  __shared__ __attribute__((aligned(16))) uint8_t cs[kStepN * kCodeLds];
+  __shared__ __attribute__((aligned(16))) uint8_t ss[kStepN * kScaleLds];
   // dy tile of the step, [32 MT rows][40] bf16, two buffers (step parity)
   __shared__ __attribute__((aligned(16))) uint16_t dys[2][32 * MT * kLdsRow];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -68,9 +71,12 @@ __global__ __launch_bounds__(kThreads) void bwd_dx(DxArgs a) {
   // copy roles: thread -> weight row tid / 16 of the step, 8 code bytes at (tid % 16) * 8
   // (and the scale byte tid % 16 of the same row)
   const int lr = tid / (kCodeRow / 8), lb = (tid % (kCodeRow / 8)) * 8;
-  // dequantization roles: thread -> row tid % 32, 16 columns at 16 (tid / 32); rows
-  // vary fastest across the lanes so the transposed LDS writes spread over the banks
-  const int dr = tid & 31, db = (tid >> 5) * 8;
+  // dequantization roles: thread -> weight rows 2 pp, 2 pp + 1 and, in each of two
+  // passes, four columns 4 G .. 4 G + 3 with G = 4 (2 wave + pass) + lane / 16;
+  // every transposed write is one dword (the two rows of a column), and the
+  // four 16-lane groups of a wave land in four different 16-bank windows
+  const int pp = lane & 15, gl = lane >> 4;
+  uint32_t* wt32 = reinterpret_cast<uint32_t*>(wt);
   f32x16_t acc[MT];
 #pragma unroll
   for (int u = 0; u < MT; ++u) acc[u] = zero16();
@@ -107,8 +113,10 @@ __global__ __launch_bounds__(kThreads) void bwd_dx(DxArgs a) {
     // Every wave has finished the previous step's MFMAs (which read wt and
     // the other dy buffer) and dequantization (which read cs) before it
     // passes the barrier below; this dy buffer was last read two steps ago.
-    *reinterpret_cast<uint2*>(cs + lr * kCodeRow + lb) = cv;
-    ss[tid] = sv;
+    uint32_t* cdst = reinterpret_cast<uint32_t*>(cs + lr * kCodeLds + lb);
+    cdst[0] = cv.x;
+    cdst[1] = cv.y;
+    ss[(tid / kScaleRow) * kScaleLds + tid % kScaleRow] = sv;
     uint16_t* dyb = dys[par];
 #pragma unroll
     for (int i = 0; i < DYPT; ++i) {
@@ -116,16 +124,25 @@ __global__ __launch_bounds__(kThreads) void bwd_dx(DxArgs a) {
       if (ch < DYCH) *reinterpret_cast<uint4*>(dyb + (ch >> 2) * kLdsRow + 8 * (ch & 3)) = dv[i];
     }
     __syncthreads();
-    {
-      const uint2 v = *reinterpret_cast<const uint2*>(cs + dr * kCodeRow + db);
-      const float sb = e4m3_to_f32(ss[dr * kScaleRow + (db >> 3)]);
-      const uint4 lo = dequant8_bf16(v.x, sb), hi = dequant8_bf16(v.y, sb);
-      const uint32_t wds[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int col = 2 * db + 2 * e;
-        wt[col * kLdsRow + dr] = (uint16_t)(wds[e] & 0xffffu);
-        wt[(col + 1) * kLdsRow + dr] = (uint16_t)(wds[e] >> 16);
+    for (int pass = 0; pass < 2; ++pass) {
+      const int G = 4 * (2 * wave + pass) + gl;       // four columns 4 G .. 4 G + 3
+      const int r0 = 2 * pp;
+      uint32_t lohi[2][2];                           // [row][bf16 pair of columns]
+#pragma unroll
+      for (int rr = 0; rr < 2; ++rr) {
+        const uint32_t c4 = *reinterpret_cast<const uint16_t*>(cs + (r0 + rr) * kCodeLds + 2 * G);
+        const float sb = e4m3_to_f32(ss[(r0 + rr) * kScaleLds + (G >> 2)]);
+        const f32x2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c4, 1.0f, 0);
+        const f32x2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c4, 1.0f, 1);
+        lohi[rr][0] = pack_bf16x2(v0[0] * sb, v0[1] * sb);
+        lohi[rr][1] = pack_bf16x2(v1[0] * sb, v1[1] * sb);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t a0 = (lohi[0][i >> 1] >> (16 * (i & 1))) & 0xffffu;   // row r0
+        const uint32_t a1 = (lohi[1][i >> 1] >> (16 * (i & 1))) & 0xffffu;   // row r0 + 1
+        wt32[((4 * G + i) * kLdsRow + r0) >> 1] = a0 | (a1 << 16);
       }
     }
     __syncthreads();
