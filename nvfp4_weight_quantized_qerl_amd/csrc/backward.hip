@@ -190,41 +190,111 @@ __global__ __launch_bounds__(kThreads) void bwd_dx(DxArgs a) {
   }
 }
 
-// part[mc][j][c] = sum over the rows i of chunk mc (kOuterRows rows) of
-// p[i, c] q[i, j], for columns c of p [m, cols] (row stride ldp) and j < r
-// of q [.., ldq] (bf16; j in the 32-wide group blockIdx.y).  One thread per
-// column; the chunk's q rows are staged once in LDS as fp32 and read as
-// broadcasts.  outer_reduce sums the chunks in chunk order.
+// part[mc][j][c] = sum over the token rows i of chunk mc (kOuterRows rows)
+// of q[i, j] p[i, c], for columns c of p [m, cols] (row stride ldp) and
+// j < r of q [.., ldq] (bf16), by 32x32x16 bf16 MFMAs with the tokens as the
+// contraction.  A workgroup of four waves owns 128 columns (wave w: 32 w ..
+// 32 w + 31) and all 32 RT values of j for one chunk.  Each step stages 32
+// token rows of p and q in LDS as they are stored (16-byte copies, rows padded
+// so that token rows 8 apart fall on different bank halves); the MFMA operands
+// (lane = column or j, eight consecutive tokens) are gathered from there with
+// 2-byte reads.  The next step's rows are loaded while the MFMAs run.
+// outer_reduce sums the chunks in chunk order.
 constexpr int kOuterRows = 256;
+constexpr int kOuterCols = 128;            // columns per workgroup
+constexpr int kOuterLds = kOuterCols + 8;  // LDS row of the p tile (elements)
 
-__global__ __launch_bounds__(256) void outer_acc(const uint16_t* __restrict__ p, int64_t ldp,
-                                                 const uint16_t* __restrict__ q, int64_t ldq,
-                                                 int64_t m, int64_t cols, int r,
-                                                 float* __restrict__ part) {
-  __shared__ float qs[kOuterRows][32];
-  const int64_t cidx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int j0 = 32 * blockIdx.y;
-  const int64_t i0 = (int64_t)blockIdx.z * kOuterRows;
-  const int rows = (int)min<int64_t>(kOuterRows, m - i0);
-  for (int e = threadIdx.x; e < kOuterRows * 32; e += 256) {
-    const int i = e >> 5, j = e & 31;
-    qs[i][j] = (i < rows && j0 + j < r) ? bf16_to_f32(q[(i0 + i) * ldq + j0 + j]) : 0.0f;
+template <int RT>
+__global__ __launch_bounds__(256) void outer_mfma(const uint16_t* __restrict__ p, int64_t ldp,
+                                                  const uint16_t* __restrict__ q, int64_t ldq,
+                                                  int64_t m, int64_t cols, int r,
+                                                  float* __restrict__ part) {
+  constexpr int QW = 32 * RT;              // j values of the q tile
+  constexpr int QLDS = QW + 8;
+  constexpr int QCH = 32 * QW / 8;         // 16-byte chunks of the q tile
+  constexpr int QPT = (QCH + 255) / 256;   // q chunks per thread
+  __shared__ __attribute__((aligned(16))) uint16_t pt[32 * kOuterLds];
+  __shared__ __attribute__((aligned(16))) uint16_t qt[32 * QLDS];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = lane & 31, h = lane >> 5;
+  const int64_t c0 = (int64_t)blockIdx.x * kOuterCols;
+  const int mc = blockIdx.y;
+  const int64_t i0 = (int64_t)mc * kOuterRows;
+  const int64_t iend = min<int64_t>(m, i0 + kOuterRows);
+  // copy roles: p chunk e (e = tid, tid + 256) -> token row e / 16, columns
+  // 8 (e % 16) .. + 7; q chunk e (e = tid + 256 i < QCH) -> token row
+  // e / (QW / 8), j = 8 (e % (QW / 8)) .. + 7
+  uint4 pv[2], qv[QPT];
+  auto load = [&](int64_t s) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int e = tid + 256 * i;
+      const int64_t row = s + (e >> 4), col = c0 + 8 * (e & 15);
+      pv[i] = make_uint4(0u, 0u, 0u, 0u);
+      if (row < iend && col < cols)
+        pv[i] = *reinterpret_cast<const uint4*>(p + row * ldp + col);
+    }
+#pragma unroll
+    for (int i = 0; i < QPT; ++i) {
+      const int e = tid + 256 * i;
+      qv[i] = make_uint4(0u, 0u, 0u, 0u);
+      const int64_t row = s + e / (QW / 8);
+      const int j0 = 8 * (e % (QW / 8));
+      if (e < QCH && row < iend && j0 < r) {
+        const uint4 v = *reinterpret_cast<const uint4*>(q + row * ldq + j0);
+        uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int x = 0; x < 8; ++x)            // j >= r reads as zero
+          if (j0 + x >= r) w[x >> 1] &= (x & 1) ? 0x0000ffffu : 0xffff0000u;
+        qv[i] = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+    }
+  };
+  // Eight bf16 of column col (LDS row stride ld), token rows t0 .. t0 + 7.
+  auto gather = [&](const uint16_t* tile, int ld, int col, int t0) {
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      w[e] = (uint32_t)tile[(t0 + 2 * e) * ld + col] | ((uint32_t)tile[(t0 + 2 * e + 1) * ld + col] << 16);
+    return make_uint4(w[0], w[1], w[2], w[3]);
+  };
+
+  f32x16_t acc[RT];
+#pragma unroll
+  for (int t = 0; t < RT; ++t) acc[t] = zero16();
+  load(i0);
+  for (int64_t s = i0; s < iend; s += 32) {
+    __syncthreads();                           // the previous step's gathers are done
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int e = tid + 256 * i;
+      *reinterpret_cast<uint4*>(pt + (e >> 4) * kOuterLds + 8 * (e & 15)) = pv[i];
+    }
+#pragma unroll
+    for (int i = 0; i < QPT; ++i) {
+      const int e = tid + 256 * i;
+      if (e < QCH) *reinterpret_cast<uint4*>(qt + (e / (QW / 8)) * QLDS + 8 * (e % (QW / 8))) = qv[i];
+    }
+    __syncthreads();
+    if (s + 32 < iend) load(s + 32);
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const uint4 b = gather(pt, kOuterLds, 32 * wave + c, 16 * s2 + 8 * h);
+#pragma unroll
+      for (int t = 0; t < RT; ++t)
+        acc[t] = mfma_bf16(gather(qt, QLDS, 32 * t + c, 16 * s2 + 8 * h), b, acc[t]);
+    }
   }
-  __syncthreads();
-  if (cidx >= cols) return;
-  float acc[32];
+  // D[j][col]: lane l, element v holds col = l % 32, j = acc_row(v, l)
+  const int64_t col = c0 + 32 * wave + c;
+  if (col >= cols) return;
 #pragma unroll
-  for (int j = 0; j < 32; ++j) acc[j] = 0.0f;
-  const uint16_t* pc = p + i0 * ldp + cidx;
-  for (int i = 0; i < rows; ++i) {
-    const float pv = bf16_to_f32(pc[(int64_t)i * ldp]);
+  for (int t = 0; t < RT; ++t)
 #pragma unroll
-    for (int j = 0; j < 32; ++j) acc[j] += pv * qs[i][j];
-  }
-  float* dst = part + ((int64_t)blockIdx.z * r) * cols + cidx;
-#pragma unroll
-  for (int j = 0; j < 32; ++j)
-    if (j0 + j < r) dst[(int64_t)(j0 + j) * cols] = acc[j];
+    for (int v = 0; v < 16; ++v) {
+      const int j = 32 * t + acc_row(v, lane);
+      if (j < r) part[((int64_t)mc * r + j) * cols + col] = acc[t][v];
+    }
 }
 
 // out[c * oc + j * oj] = sum over chunks mc (in order) of part[mc][j][c].
@@ -324,10 +394,13 @@ hipError_t launch_linear_backward(const BackwardPlan& b, const uint16_t* dy, con
   float* opart = reinterpret_cast<float*>(ws + b.off_opart);
   auto outer = [&](const uint16_t* pp, int64_t ldp, const uint16_t* qq, int64_t ldq,
                    int64_t cols, float* out, int64_t oc, int64_t oj) {
-    hipLaunchKernelGGL(outer_acc,
-                       dim3((unsigned)((cols + 255) / 256), (unsigned)((r + 31) / 32),
-                            (unsigned)b.mchunks),
-                       dim3(256), 0, stream, pp, ldp, qq, ldq, p.m, cols, r, opart);
+    const dim3 grid((unsigned)((cols + kOuterCols - 1) / kOuterCols), (unsigned)b.mchunks);
+    switch ((r + 31) / 32) {
+      case 1: hipLaunchKernelGGL(outer_mfma<1>, grid, dim3(256), 0, stream, pp, ldp, qq, ldq, p.m, cols, r, opart); break;
+      case 2: hipLaunchKernelGGL(outer_mfma<2>, grid, dim3(256), 0, stream, pp, ldp, qq, ldq, p.m, cols, r, opart); break;
+      case 3: hipLaunchKernelGGL(outer_mfma<3>, grid, dim3(256), 0, stream, pp, ldp, qq, ldq, p.m, cols, r, opart); break;
+      default: hipLaunchKernelGGL(outer_mfma<4>, grid, dim3(256), 0, stream, pp, ldp, qq, ldq, p.m, cols, r, opart); break;
+    }
     hipError_t e2 = hipGetLastError();
     if (e2 != hipSuccess) return e2;
     hipLaunchKernelGGL(outer_reduce, dim3((unsigned)((cols * r + 255) / 256)), dim3(256), 0,

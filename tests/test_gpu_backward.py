@@ -57,6 +57,8 @@ def run_case(m, n, k, r, seed, noise=True, rows=None):
     (130, 272, 384, 40),     # n % 32 == 16, r not a multiple of 16 or 32
     (64, 512, 1024, 32),     # two token tiles per workgroup
     (256, 1024, 512, 32),    # four token tiles per workgroup
+    (48, 160, 288, 72),      # three 32-wide groups of the LoRA rank in dA / dB
+    (70, 128, 256, 128),     # the largest rank: four groups
 ])
 def test_backward_parity(m, n, k, r):
     run_case(m, n, k, r, seed=m + n)
