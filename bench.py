@@ -52,7 +52,7 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-chain", action="store_true")
     ap.add_argument("--profile", nargs="?", const="decode",
-                    choices=("decode", "prefill", "rmsnorm", "backward"),
+                    choices=("decode", "prefill", "rmsnorm", "backward", "chain", "mxfp4"),
                     help="profiling pass for rocprofv3, no timing and no JSON line: "
                          "'decode' runs one plain device copy of COPY_BYTES (counter "
                          "calibration) and PROFILE_LAUNCHES gate/up decode contractions; "
@@ -60,7 +60,11 @@ def parse():
                          "the 7B qkv and down layers at M=4096; 'rmsnorm' runs one "
                          "plain device copy (counter calibration) and 20 noisy RMSNorms "
                          "of 4096 x 3584 rows on rotated inputs; 'backward' runs three "
-                         "backward calls (dx, dA, dB) of the 7B down layer at M=4096")
+                         "backward calls (dx, dA, dB) of the 7B down layer at M=4096; "
+                         "'chain' runs PROFILE_LAUNCHES chained decode feed-forward steps "
+                         "(noisy RMSNorm, gate/up, SwiGLU, down); 'mxfp4' runs "
+                         "PROFILE_LAUNCHES gate/up contractions on the MXFP4 weight with "
+                         "the general and then with the power-of-two dequantization")
     return ap.parse_args()
 
 
@@ -181,6 +185,54 @@ def profile_backward(q, pc, make_layer, to_dev, dev, calls=3):
     print(f"profile pass done: {calls} backward calls of the 7B down layer at M={pc.m}")
 
 
+def make_chain(q, layers, cfg, to_dev, dev, sigma, copies):
+    """The 7B weights as one chained decode feed-forward block: noisy RMSNorm
+    (Eq. 10, noise of the gate/up group) -> fused gate/up layer (no noise of
+    its own) -> SiLU(gate) * up -> down layer (its own noise).  The two noise
+    vectors are drawn here, before any timing.  Returns (step function,
+    algorithmic bytes of one step)."""
+    from workloads import norm_inputs
+    M, R = cfg.m, cfg.r
+    gu_l, dn_l = layers
+    d_model, d_inter = gu_l["k"], dn_l["k"]
+    xres_bits, wn_bits = norm_inputs(M, d_model, seed=41)
+    xres, wnorm = to_dev(xres_bits), to_dev(wn_bits)
+    z_gu = q.qerl_aqn_sample(41, 0, 0, sigma, d_model, device=dev)
+    z_dn = q.qerl_aqn_sample(41, 0, 1, sigma, d_inter, device=dev)
+    import torch
+    h = torch.empty((M, d_model), dtype=torch.bfloat16, device=dev)
+    act = torch.empty((M, d_inter), dtype=torch.bfloat16, device=dev)
+
+    def chain_step(i):
+        cg, sg = gu_l["rot"][i % copies]
+        cd, sd = dn_l["rot"][i % copies]
+        q.qerl_rmsnorm_noisy(xres, wnorm, z_gu, 1e-6, out=h)
+        q.qerl_linear_decode(h, cg, sg, gu_l["S"], gu_l["a"], gu_l["b"], cfg.lora_scale,
+                             None, workspace=gu_l["ws"], y=gu_l["y"])
+        q.qerl_swiglu(gu_l["y"], out=act)
+        q.qerl_linear_decode(act, cd, sd, dn_l["S"], dn_l["a"], dn_l["b"], cfg.lora_scale,
+                             z_dn, workspace=dn_l["ws"], y=dn_l["y"])
+
+    chain_bytes = (4 * M * d_model + 6 * d_model
+                   + linear_bytes(M, gu_l["n"], d_model, R) - 4 * d_model
+                   + 6 * M * d_inter
+                   + linear_bytes(M, dn_l["n"], d_inter, R))
+    return chain_step, chain_bytes
+
+
+def make_mxfp4(q, gl, cfg, make_layer, to_dev, copies, z):
+    """The gate/up weight quantized to MXFP4 (E8M0 per 32) and re-expressed
+    in the NVFP4 layout, rotated like the NVFP4 copies, with the layer's
+    prepare run on noise z.  Returns (rotation, FP32 scale S, range flag)."""
+    Lg = make_layer(cfg.m, gl["n"], gl["k"], cfg.r, seed=1, stage=cfg.stage,
+                    outlier_frac=cfg.outlier_frac, call_id=0)
+    mcodes, ms8, _ = q.qerl_quantize_mxfp4(to_dev(Lg.w))
+    ms4, mg, mflag = q.qerl_mxfp4_to_nvfp4(mcodes, ms8)
+    mrot = [(mcodes, ms4)] + [(mcodes.clone(), ms4.clone()) for _ in range(copies - 1)]
+    q.qerl_linear_prepare(gl["x"], gl["n"], gl["a"], cfg.lora_scale, z, gl["ws"])
+    return mrot, mg, mflag
+
+
 def oracle_step_rate(cfg, layers, M, R, min_seconds=10.0, max_reps=20):
     """The oracle running the decode step on the host: per layer, sample z,
     dequantize the NVFP4 weight and evaluate the fp64 linear layer with the
@@ -284,6 +336,24 @@ def main():
         del ly["w"]
     torch.cuda.empty_cache()
 
+    if args.profile == "chain":
+        chain_step, _ = make_chain(q, layers, cfg, to_dev, dev, sigma, copies)
+        for i in range(PROFILE_LAUNCHES):
+            chain_step(i)
+        torch.cuda.synchronize()
+        print(f"profile pass done: {PROFILE_LAUNCHES} chained decode feed-forward steps")
+        return
+    if args.profile == "mxfp4":
+        gl = layers[0]
+        z = q.qerl_aqn_sample(gl["L"].seed, 0, 0, sigma, gl["k"], device=dev)
+        mrot, mg, _ = make_mxfp4(q, gl, cfg, make_layer, to_dev, copies, z)
+        for fn in (q.qerl_linear_decode_prepared, q.qerl_linear_decode_prepared_mxfp4):
+            for i in range(PROFILE_LAUNCHES):
+                fn(M, *mrot[i % copies], mg, gl["k"], gl["b"], gl["y"], gl["ws"])
+        torch.cuda.synchronize()
+        print(f"profile pass done: {PROFILE_LAUNCHES} MXFP4 gate/up contractions with each "
+              "dequantization")
+        return
     if args.profile:
         # Plain copy of known size: FETCH_SIZE / WRITE_SIZE of this dispatch
         # calibrate the counters of the contraction kernel below.
@@ -363,26 +433,7 @@ def main():
     # a second stream, off its critical path).
     chain = None
     if not args.no_chain:
-        from workloads import norm_inputs
-        gu_l, dn_l = layers
-        d_model, d_inter = gu_l["k"], dn_l["k"]
-        xres_bits, wn_bits = norm_inputs(M, d_model, seed=41)
-        xres, wnorm = to_dev(xres_bits), to_dev(wn_bits)
-        z_gu = q.qerl_aqn_sample(41, 0, 0, sigma, d_model, device=dev)
-        z_dn = q.qerl_aqn_sample(41, 0, 1, sigma, d_inter, device=dev)
-        h = torch.empty((M, d_model), dtype=torch.bfloat16, device=dev)
-        act = torch.empty((M, d_inter), dtype=torch.bfloat16, device=dev)
-
-        def chain_step(i):
-            cg, sg = gu_l["rot"][i % copies]
-            cd, sd = dn_l["rot"][i % copies]
-            q.qerl_rmsnorm_noisy(xres, wnorm, z_gu, 1e-6, out=h)
-            q.qerl_linear_decode(h, cg, sg, gu_l["S"], gu_l["a"], gu_l["b"], cfg.lora_scale,
-                                 None, workspace=gu_l["ws"], y=gu_l["y"])
-            q.qerl_swiglu(gu_l["y"], out=act)
-            q.qerl_linear_decode(act, cd, sd, dn_l["S"], dn_l["a"], dn_l["b"], cfg.lora_scale,
-                                 z_dn, workspace=dn_l["ws"], y=dn_l["y"])
-
+        chain_step, chain_bytes = make_chain(q, layers, cfg, to_dev, dev, sigma, copies)
         for i in range(args.warmup):
             chain_step(i)
         c0 = torch.cuda.Event(enable_timing=True)
@@ -393,10 +444,6 @@ def main():
         c1.record(stream)
         c1.synchronize()
         t_chain = c0.elapsed_time(c1) / 1e3 / args.steps
-        chain_bytes = (4 * M * d_model + 6 * d_model
-                       + linear_bytes(M, gu_l["n"], d_model, R) - 4 * d_model
-                       + 6 * M * d_inter
-                       + linear_bytes(M, dn_l["n"], d_inter, R))
         chain = {"workload": "decode_7b_mlp chained: noisy RMSNorm -> gate/up -> SiLU(gate)*up "
                              "-> down, M=64",
                  "us_per_step": round(t_chain * 1e6, 2),
@@ -409,12 +456,7 @@ def main():
     mx = None
     if not args.no_chain:
         gl = layers[0]
-        Lg = make_layer(M, gl["n"], gl["k"], R, seed=1, stage=cfg.stage,
-                        outlier_frac=cfg.outlier_frac, call_id=0)
-        mcodes, ms8, _ = q.qerl_quantize_mxfp4(to_dev(Lg.w))
-        ms4, mg, mflag = q.qerl_mxfp4_to_nvfp4(mcodes, ms8)
-        mrot = [(mcodes, ms4)] + [(mcodes.clone(), ms4.clone()) for _ in range(copies - 1)]
-        q.qerl_linear_prepare(gl["x"], gl["n"], gl["a"], cfg.lora_scale, zring[0][0], gl["ws"])
+        mrot, mg, mflag = make_mxfp4(q, gl, cfg, make_layer, to_dev, copies, zring[0][0])
         mx = {"workload": "gate/up 37888x3584 MXFP4 weight in the NVFP4 layout, M=64, r=32",
               "range_flag": int(mflag.item())}
         mx_bytes = main_kernel_bytes(M, gl["n"], gl["k"], R)
@@ -436,7 +478,7 @@ def main():
         for name, v in mx_t.items():
             mx[name] = round(sorted(v)[1], 2)
         mx["pow2_GB_per_s"] = round(mx_bytes / (mx["pow2_us"] * 1e-6) / 1e9, 1)
-        del mrot, mcodes, ms8, ms4
+        del mrot
 
     # ---- dominant kernel alone: gate/up contraction, HIP events on its stream
     ly = layers[0]
