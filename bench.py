@@ -62,7 +62,8 @@ def parse():
                          "of 4096 x 3584 rows on rotated inputs; 'backward' runs three "
                          "backward calls (dx, dA, dB) of the 7B down layer at M=4096; "
                          "'chain' runs PROFILE_LAUNCHES chained decode feed-forward steps "
-                         "(noisy RMSNorm, gate/up, SwiGLU, down); 'mxfp4' runs "
+                         "(noisy RMSNorm, gate/up, down on SwiGLU of the gate/up output); "
+                         "'mxfp4' runs "
                          "PROFILE_LAUNCHES gate/up contractions on the MXFP4 weight with "
                          "the general and then with the power-of-two dequantization")
     return ap.parse_args()
@@ -188,9 +189,10 @@ def profile_backward(q, pc, make_layer, to_dev, dev, calls=3):
 def make_chain(q, layers, cfg, to_dev, dev, sigma, copies):
     """The 7B weights as one chained decode feed-forward block: noisy RMSNorm
     (Eq. 10, noise of the gate/up group) -> fused gate/up layer (no noise of
-    its own) -> SiLU(gate) * up -> down layer (its own noise).  The two noise
-    vectors are drawn here, before any timing.  Returns (step function,
-    algorithmic bytes of one step)."""
+    its own) -> down layer (its own noise) on SiLU(gate) * up, which its
+    prepare forms from the gate/up output (qerl_linear_decode_swiglu).  The
+    two noise vectors are drawn here, before any timing.  Returns (step
+    function, algorithmic bytes of one step)."""
     from workloads import norm_inputs
     M, R = cfg.m, cfg.r
     gu_l, dn_l = layers
@@ -201,7 +203,6 @@ def make_chain(q, layers, cfg, to_dev, dev, sigma, copies):
     z_dn = q.qerl_aqn_sample(41, 0, 1, sigma, d_inter, device=dev)
     import torch
     h = torch.empty((M, d_model), dtype=torch.bfloat16, device=dev)
-    act = torch.empty((M, d_inter), dtype=torch.bfloat16, device=dev)
 
     def chain_step(i):
         cg, sg = gu_l["rot"][i % copies]
@@ -209,13 +210,12 @@ def make_chain(q, layers, cfg, to_dev, dev, sigma, copies):
         q.qerl_rmsnorm_noisy(xres, wnorm, z_gu, 1e-6, out=h)
         q.qerl_linear_decode(h, cg, sg, gu_l["S"], gu_l["a"], gu_l["b"], cfg.lora_scale,
                              None, workspace=gu_l["ws"], y=gu_l["y"])
-        q.qerl_swiglu(gu_l["y"], out=act)
-        q.qerl_linear_decode(act, cd, sd, dn_l["S"], dn_l["a"], dn_l["b"], cfg.lora_scale,
-                             z_dn, workspace=dn_l["ws"], y=dn_l["y"])
+        q.qerl_linear_decode_swiglu(gu_l["y"], cd, sd, dn_l["S"], dn_l["a"], dn_l["b"],
+                                    cfg.lora_scale, z_dn, workspace=dn_l["ws"], y=dn_l["y"])
 
     chain_bytes = (4 * M * d_model + 6 * d_model
                    + linear_bytes(M, gu_l["n"], d_model, R) - 4 * d_model
-                   + 6 * M * d_inter
+                   + 2 * M * d_inter               # the down layer reads gate and up
                    + linear_bytes(M, dn_l["n"], d_inter, R))
     return chain_step, chain_bytes
 
@@ -444,8 +444,8 @@ def main():
         c1.record(stream)
         c1.synchronize()
         t_chain = c0.elapsed_time(c1) / 1e3 / args.steps
-        chain = {"workload": "decode_7b_mlp chained: noisy RMSNorm -> gate/up -> SiLU(gate)*up "
-                             "-> down, M=64",
+        chain = {"workload": "decode_7b_mlp chained: noisy RMSNorm -> gate/up -> down on "
+                             "SiLU(gate)*up (formed in the down layer's prepare), M=64",
                  "us_per_step": round(t_chain * 1e6, 2),
                  "GB_per_s": round(chain_bytes / t_chain / 1e9, 1),
                  "frac_hbm": round(chain_bytes / t_chain / 1e9 / HBM_PEAK_GBS, 4)}

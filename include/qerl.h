@@ -277,6 +277,27 @@ QERL_API qerl_status qerl_linear_decode(const void* x, int64_t m, const void* co
                                void* stream);
 
 /*
+ * qerl_linear_decode_swiglu -- qerl_linear_decode of the down layer of a
+ * gated feed-forward block, taking the fused gate/up output instead of its
+ * activation: the layer input is x = bf16(SiLU(gate) * up), the operation
+ * of qerl_swiglu (Qwen2.5 feed-forward block; W_gate, W_up, W_down
+ * [QeRL summary, §3.4 "Layer coverage"]), formed while the prepare loads
+ * the rows, so the result is bit-identical to qerl_swiglu followed by
+ * qerl_linear_decode and the activation is never written out.
+ *   gate_up      device, [m, 2k] bf16, 16-byte aligned: gate in columns
+ *                0 .. k-1, up in k .. 2k-1
+ * Every other argument, the workspace size and the errors are those of
+ * qerl_linear_decode for the layer (m, n, k, r).
+ */
+QERL_API qerl_status qerl_linear_decode_swiglu(const void* gate_up, int64_t m, const void* codes,
+                                      const void* scales, const float* gscale,
+                                      int64_t n, int64_t k, const void* lora_a,
+                                      const void* lora_b, int32_t r,
+                                      float lora_scale, const float* z, void* y,
+                                      void* workspace, size_t workspace_bytes,
+                                      void* stream);
+
+/*
  * qerl_linear_prefill -- the same operation and arguments as
  * qerl_linear_decode, tuned for large m (prompt prefill): NVFP4 tiles are
  * dequantized into LDS and contracted with bf16 MFMA.

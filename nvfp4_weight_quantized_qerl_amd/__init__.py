@@ -130,9 +130,14 @@ def workspace(m, n, k, r, device="cuda"):
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
-def _linear(fn_name, x, codes, scales, gscale, lora_a, lora_b, lora_scale, z, ws, y):
+def _linear(fn_name, x, codes, scales, gscale, lora_a, lora_b, lora_scale, z, ws, y,
+            gate_up=False):
     x = _bits16(x, "x")
     m, k = x.shape
+    if gate_up:
+        if k % 2:
+            raise ValueError("gate_up needs an even number of columns")
+        k //= 2
     n = codes.shape[0]
     r = 0 if lora_a is None else int(lora_a.shape[0])
     la = None if lora_a is None else _bits16(lora_a, "lora_a")
@@ -153,6 +158,14 @@ def qerl_linear_decode(x, codes, scales, gscale, lora_a=None, lora_b=None, lora_
     """y = bf16(x_t W_hat^T + s (x_t A^T) B^T), x_t = x (1 + z); tuned for small m."""
     return _linear("qerl_linear_decode", x, codes, scales, gscale, lora_a, lora_b,
                    lora_scale, z, workspace, y)
+
+
+def qerl_linear_decode_swiglu(gate_up, codes, scales, gscale, lora_a=None, lora_b=None,
+                              lora_scale=0.0, z=None, workspace=None, y=None):
+    """qerl_linear_decode of x = bf16(SiLU(gate) * up) from the fused gate/up
+    output [m, 2k] (gate first), without writing x."""
+    return _linear("qerl_linear_decode_swiglu", gate_up, codes, scales, gscale, lora_a, lora_b,
+                   lora_scale, z, workspace, y, gate_up=True)
 
 
 def qerl_linear_prefill(x, codes, scales, gscale, lora_a=None, lora_b=None, lora_scale=0.0,

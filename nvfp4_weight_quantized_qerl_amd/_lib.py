@@ -27,6 +27,9 @@ SIGNATURES = {
     "qerl_linear_workspace_bytes": (c_sz, [c_i64, c_i64, c_i64, c_i32]),
     "qerl_linear_decode": (ctypes.c_int, [c_vp, c_i64, c_vp, c_vp, c_vp, c_i64, c_i64, c_vp,
                                           c_vp, c_i32, c_f32, c_vp, c_vp, c_vp, c_sz, c_vp]),
+    "qerl_linear_decode_swiglu": (ctypes.c_int, [c_vp, c_i64, c_vp, c_vp, c_vp, c_i64, c_i64,
+                                                 c_vp, c_vp, c_i32, c_f32, c_vp, c_vp, c_vp,
+                                                 c_sz, c_vp]),
     "qerl_linear_prefill": (ctypes.c_int, [c_vp, c_i64, c_vp, c_vp, c_vp, c_i64, c_i64, c_vp,
                                            c_vp, c_i32, c_f32, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "qerl_linear_prepare": (ctypes.c_int, [c_vp, c_i64, c_i64, c_i64, c_vp, c_i32, c_f32,

@@ -55,7 +55,7 @@ const char* qerl_status_string(int status) {
   }
 }
 
-int qerl_abi_version(void) { return 8; }
+int qerl_abi_version(void) { return 9; }
 
 qerl_status qerl_quantize_nvfp4(const void* w_bf16, int64_t n, int64_t k, void* codes,
                                 void* scales, float* gscale, int32_t* nonfinite_flag,
@@ -219,7 +219,7 @@ static qerl_status linear_full(bool prefill, const void* x, int64_t m, const voi
                                int64_t k, const void* lora_a, const void* lora_b,
                                int32_t r, float lora_scale, const float* z, void* y,
                                void* workspace, size_t workspace_bytes, void* stream,
-                               bool pow2 = false) {
+                               bool pow2 = false, bool swiglu = false) {
   if (!x) return QERL_ERR_NULL;
   if (r > 0 && (!lora_a) != (!lora_b)) return QERL_ERR_NULL;
   const int32_t r_eff = (r > 0 && lora_a && lora_b) ? r : 0;
@@ -235,7 +235,7 @@ static qerl_status linear_full(bool prefill, const void* x, int64_t m, const voi
   char* ws = static_cast<char*>(workspace);
   hipError_t e = qerl::launch_linear_prepare(plan, static_cast<const uint16_t*>(x), z,
                                              static_cast<const uint16_t*>(lora_a),
-                                             lora_scale, ws, st);
+                                             lora_scale, ws, st, swiglu);
   if (e != hipSuccess) return QERL_ERR_HIP;
   const uint8_t* c = static_cast<const uint8_t*>(codes);
   const uint8_t* sc = static_cast<const uint8_t*>(scales);
@@ -253,6 +253,15 @@ qerl_status qerl_linear_decode(const void* x, int64_t m, const void* codes,
                                void* workspace, size_t workspace_bytes, void* stream) {
   return linear_full(false, x, m, codes, scales, gscale, n, k, lora_a, lora_b, r,
                      lora_scale, z, y, workspace, workspace_bytes, stream);
+}
+
+qerl_status qerl_linear_decode_swiglu(const void* gate_up, int64_t m, const void* codes,
+                                      const void* scales, const float* gscale, int64_t n,
+                                      int64_t k, const void* lora_a, const void* lora_b,
+                                      int32_t r, float lora_scale, const float* z, void* y,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  return linear_full(false, gate_up, m, codes, scales, gscale, n, k, lora_a, lora_b, r,
+                     lora_scale, z, y, workspace, workspace_bytes, stream, false, true);
 }
 
 qerl_status qerl_linear_prefill(const void* x, int64_t m, const void* codes,

@@ -22,6 +22,7 @@
 // Without a LoRA branch a single elementwise kernel (xt_kernel) writes x_t.
 #include <algorithm>
 
+#include "qerl_act.h"
 #include "qerl_device.h"
 #include "qerl_internal.h"
 
@@ -139,7 +140,9 @@ bool make_linear_plan(int64_t m, int64_t n, int64_t k, int r, LinearPlan* p) {
 namespace {
 
 struct PrepArgs {
-  const uint16_t* __restrict__ x;
+  const uint16_t* __restrict__ x;  // [m, ldx]; with swiglu, gate in 0 .. k-1 and up in k .. 2k-1
+  int64_t ldx;
+  int swiglu;                      // the layer input is bf16(SiLU(gate) * up)
   const float* __restrict__ z;
   const uint16_t* __restrict__ a;
   uint16_t* __restrict__ xt;     // null: x_t is not written (only the LoRA-down partials)
@@ -210,8 +213,18 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs p) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int64_t mrow = row0 + 8 * wave + i;
-    xv[i] = (kin && mrow < p.m) ? *reinterpret_cast<const uint4*>(p.x + mrow * p.k + kl)
+    xv[i] = (kin && mrow < p.m) ? *reinterpret_cast<const uint4*>(p.x + mrow * p.ldx + kl)
                                 : make_uint4(0u, 0u, 0u, 0u);
+  }
+  if (p.swiglu) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int64_t mrow = row0 + 8 * wave + i;
+      const uint4 up = (kin && mrow < p.m)
+                           ? *reinterpret_cast<const uint4*>(p.x + mrow * p.ldx + p.k + kl)
+                           : make_uint4(0u, 0u, 0u, 0u);
+      xv[i] = swiglu8(xv[i], up);      // rows past m: SiLU(0) * 0 = 0
+    }
   }
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -262,7 +275,8 @@ __global__ __launch_bounds__(256) void xt_kernel(PrepArgs p) {
   const int64_t mrow = i / per_row, k0 = (i % per_row) * 8;
   uint4 xv = make_uint4(0u, 0u, 0u, 0u);
   if (mrow < p.m) {
-    xv = *reinterpret_cast<const uint4*>(p.x + mrow * p.k + k0);
+    xv = *reinterpret_cast<const uint4*>(p.x + mrow * p.ldx + k0);
+    if (p.swiglu) xv = swiglu8(xv, *reinterpret_cast<const uint4*>(p.x + mrow * p.ldx + p.k + k0));
     if (p.z)
       xv = noisy8(xv, *reinterpret_cast<const float4*>(p.z + k0),
                   *reinterpret_cast<const float4*>(p.z + k0 + 4));
@@ -308,6 +322,8 @@ hipError_t launch_lora_down(const uint16_t* x, int64_t m, int64_t mpad, int64_t 
                             uint16_t* t, hipStream_t stream) {
   PrepArgs a;
   a.x = x;
+  a.ldx = k;
+  a.swiglu = 0;
   a.z = nullptr;
   a.a = a_rk;
   a.xt = nullptr;
@@ -348,9 +364,11 @@ hipError_t launch_treduce(const LinearPlan& p, char* ws, hipStream_t stream) {
 hipError_t launch_linear_prepare(const LinearPlan& p, const uint16_t* x,
                                  const float* z, const uint16_t* lora_a,
                                  float lora_scale, char* ws,
-                                 hipStream_t stream) {
+                                 hipStream_t stream, bool swiglu_input) {
   PrepArgs a;
   a.x = x;
+  a.ldx = swiglu_input ? 2 * p.k : p.k;
+  a.swiglu = swiglu_input ? 1 : 0;
   a.z = z;
   a.a = lora_a;
   a.xt = reinterpret_cast<uint16_t*>(ws + p.off_xt);

@@ -1,0 +1,34 @@
+// Gated feed-forward activation shared by the SwiGLU kernel and the
+// prepare kernel that forms the down layer's input from the fused gate/up
+// output (Qwen2.5 feed-forward block; W_gate, W_up, W_down [QeRL summary,
+// §3.4 "Layer coverage"]): both call these helpers, so their results are
+// bit-identical.
+#pragma once
+
+#include "qerl_device.h"
+
+namespace qerl {
+
+// SiLU(g) = g / (1 + exp(-g)) in fp32 with the hardware exponential and
+// reciprocal (each within a few fp32 ulps, far below one bf16 ulp, the
+// precision the result is rounded to).
+__device__ __forceinline__ float silu_f32(float g) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+}
+
+// bf16(SiLU(g) * u) of eight consecutive channels from their gate and up
+// values (bf16 pairs, channel i in half i % 2 of dword i / 2): one rounding.
+__device__ __forceinline__ uint4 swiglu8(uint4 g, uint4 u) {
+  uint4 o;
+  o.x = pack_bf16x2(silu_f32(bf16_to_f32(g.x & 0xffffu)) * bf16_to_f32(u.x & 0xffffu),
+                    silu_f32(bf16_to_f32(g.x >> 16)) * bf16_to_f32(u.x >> 16));
+  o.y = pack_bf16x2(silu_f32(bf16_to_f32(g.y & 0xffffu)) * bf16_to_f32(u.y & 0xffffu),
+                    silu_f32(bf16_to_f32(g.y >> 16)) * bf16_to_f32(u.y >> 16));
+  o.z = pack_bf16x2(silu_f32(bf16_to_f32(g.z & 0xffffu)) * bf16_to_f32(u.z & 0xffffu),
+                    silu_f32(bf16_to_f32(g.z >> 16)) * bf16_to_f32(u.z >> 16));
+  o.w = pack_bf16x2(silu_f32(bf16_to_f32(g.w & 0xffffu)) * bf16_to_f32(u.w & 0xffffu),
+                    silu_f32(bf16_to_f32(g.w >> 16)) * bf16_to_f32(u.w >> 16));
+  return o;
+}
+
+}  // namespace qerl

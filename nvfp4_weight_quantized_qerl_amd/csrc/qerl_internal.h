@@ -66,10 +66,12 @@ struct LinearPlan {
 
 bool make_linear_plan(int64_t m, int64_t n, int64_t k, int r, LinearPlan* p);
 
+// With swiglu_input, x is the fused gate/up output [m, 2k] and the layer
+// input is bf16(SiLU(gate) * up), formed as the rows are loaded.
 hipError_t launch_linear_prepare(const LinearPlan& p, const uint16_t* x,
                                  const float* z, const uint16_t* lora_a,
                                  float lora_scale, char* ws,
-                                 hipStream_t stream);
+                                 hipStream_t stream, bool swiglu_input = false);
 
 // t = bf16(scale x a_rk^T) for x [m, k] (rows m..mpad-1 read as zero) and
 // a_rk [r, k]: the LoRA-down kernels on any operands (partials [ceil(k/512),

@@ -3,9 +3,11 @@
 // [QeRL summary, §3.4 "Layer coverage"]):
 //     out[m, j] = bf16( SiLU(g[m, j]) * u[m, j] ),  SiLU(g) = g / (1 + exp(-g))
 // where g and u are the two halves of the fused gate/up output [m, 2 d]
-// (gate in columns 0 .. d-1, up in d .. 2d-1).  fp32 arithmetic, one
+// (gate in columns 0 .. d-1, up in d .. 2d-1).  fp32 arithmetic (the
+// exponential and the division by the hardware's approximations), one
 // rounding to bf16.  HBM-bound: 6 bytes per output element; each thread
 // handles eight consecutive outputs with 16-byte loads and stores.
+#include "qerl_act.h"
 #include "qerl_device.h"
 #include "qerl_internal.h"
 
@@ -13,8 +15,6 @@ namespace qerl {
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 
 __global__ __launch_bounds__(256) void swiglu_kernel(const uint16_t* __restrict__ gu, int64_t m,
                                                      int64_t d, uint16_t* __restrict__ out) {
@@ -25,12 +25,8 @@ __global__ __launch_bounds__(256) void swiglu_kernel(const uint16_t* __restrict_
     const int64_t row = i / per_row, j = 8 * (i - row * per_row);
     const u32x4 g = *reinterpret_cast<const u32x4*>(gu + row * 2 * d + j);
     const u32x4 u = *reinterpret_cast<const u32x4*>(gu + row * 2 * d + d + j);
-    u32x4 o;
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      o[e] = pack_bf16x2(silu(bf16_to_f32(g[e] & 0xffffu)) * bf16_to_f32(u[e] & 0xffffu),
-                         silu(bf16_to_f32(g[e] >> 16)) * bf16_to_f32(u[e] >> 16));
-    *reinterpret_cast<u32x4*>(out + row * d + j) = o;
+    const uint4 o = swiglu8(__builtin_bit_cast(uint4, g), __builtin_bit_cast(uint4, u));
+    *reinterpret_cast<u32x4*>(out + row * d + j) = __builtin_bit_cast(u32x4, o);
   }
 }
 

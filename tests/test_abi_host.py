@@ -41,7 +41,7 @@ def test_status_strings():
     for s in range(7):
         assert lib.qerl_status_string(s).decode().startswith("QERL_")
     assert b"unknown" in lib.qerl_status_string(99)
-    assert lib.qerl_abi_version() == 8
+    assert lib.qerl_abi_version() == 9
 
 
 FAKE = ctypes.c_void_p(0x10000)        # aligned, never dereferenced on error
@@ -176,17 +176,20 @@ def test_linear_validation():
                          kw.get("n", 64), kw.get("k", 64), kw.get("a", FAKE), kw.get("b", FAKE),
                          kw.get("r", 8), kw.get("s", 2.0), kw.get("z", None), kw.get("y", FAKE),
                          kw.get("ws", FAKE), kw.get("wsb", W), None]
-    assert dec(*args(x=None)) == 1
-    assert dec(*args(y=None)) == 1
-    assert dec(*args(a=None)) == 1          # LoRA A without B
-    assert dec(*args(m=0)) == 2
-    assert dec(*args(k=40)) == 2
-    assert dec(*args(r=200)) == 4
-    assert dec(*args(s=float("inf"))) == 4
-    assert dec(*args(codes=MIS)) == 3
-    assert dec(*args(z=ctypes.c_void_p(0x10004))) == 3
-    assert dec(*args(ws=ctypes.c_void_p(0x10010))) == 3
-    assert dec(*args(wsb=W - 1)) == 5
+    # the SwiGLU-input form validates its (m, n, k, r) layer the same way
+    for dec in (lib.qerl_linear_decode, lib.qerl_linear_decode_swiglu):
+        assert dec(*args(x=None)) == 1
+        assert dec(*args(y=None)) == 1
+        assert dec(*args(a=None)) == 1          # LoRA A without B
+        assert dec(*args(m=0)) == 2
+        assert dec(*args(k=40)) == 2
+        assert dec(*args(r=200)) == 4
+        assert dec(*args(s=float("inf"))) == 4
+        assert dec(*args(x=MIS)) == 3
+        assert dec(*args(codes=MIS)) == 3
+        assert dec(*args(z=ctypes.c_void_p(0x10004))) == 3
+        assert dec(*args(ws=ctypes.c_void_p(0x10010))) == 3
+        assert dec(*args(wsb=W - 1)) == 5
     pre = lib.qerl_linear_prepare
     assert pre(None, 4, 64, 64, None, 0, 1.0, None, FAKE, W, None) == 1
     assert pre(FAKE, 4, 64, 64, None, 8, 1.0, None, FAKE, W, None) == 1

@@ -4,7 +4,8 @@ noisy RMSNorm (Eq. 10) -> fused gate/up layer (no noise of its own) ->
 SiLU(gate) * up -> down layer with its own noise vector.
 
 Bars: SwiGLU outputs are faithful bf16 roundings of the fp64 value (one
-bf16 ulp; fp32 exp and products carry a few 2^-24).  Each call of the chain
+bf16 ulp; the hardware exp and reciprocal and the fp32 products carry a few
+2^-24, against the 2^-8 of a bf16 ulp).  Each call of the chain
 returns bf16 (the interface of every call), so the oracle chain rounds to
 bf16 (nearest even) at the same three points and is otherwise fp64; the
 chain's output is then within the layer tolerance (max error 2e-2 of
@@ -64,7 +65,10 @@ def test_chained_decode_mlp():
     gu = q.qerl_linear_decode(h, cg, sg, Sg, dev16(Lgu.a), dev16(Lgu.b), 2.0, None)
     act = q.qerl_swiglu(gu)
     y = q.qerl_linear_decode(act, cd, sd, Sd, dev16(Ldn.a), dev16(Ldn.b), 2.0, zd)
+    # the same down layer with the activation formed inside its prepare
+    y_fused = q.qerl_linear_decode_swiglu(gu, cd, sd, Sd, dev16(Ldn.a), dev16(Ldn.b), 2.0, zd)
     torch.cuda.synchronize()
+    assert torch.equal(y_fused, y)
     got = formats.bf16_bits_to_f64(host(y).reshape(m, hidden))
     # oracle chain in fp64, each call's output rounded to bf16 as the calls return it
     wg = nvfp4.dequantize(*nvfp4.quantize(Lgu.w))
@@ -81,3 +85,25 @@ def test_chained_decode_mlp():
     print(f"chained mlp max_rel_error={err:.4g} (vs the unrounded fp64 chain: "
           f"{err_unrounded:.4g})", flush=True)
     assert err <= 2e-2
+
+
+@pytest.mark.parametrize("m,n,k,r,noise", [
+    (5, 96, 160, 16, True),       # ragged m, one partial K chunk of the prepare
+    (37, 128, 1024, 0, True),     # no LoRA branch (the elementwise x_t kernel)
+    (64, 256, 512, 40, False),    # two rank groups, no noise
+    (64, 3584, 18944, 32, True),  # the 7B down layer at 64 tokens
+])
+def test_decode_swiglu_is_swiglu_then_decode(m, n, k, r, noise):
+    """qerl_linear_decode_swiglu(gate_up) == qerl_linear_decode(qerl_swiglu(gate_up)),
+    bit for bit: both form bf16(SiLU(g) u) with the same fp32 arithmetic."""
+    print(f"decode_swiglu m={m} n={n} k={k} r={r} noise={noise}", flush=True)
+    L = make_layer(m, n, k, r, seed=90 + m)
+    gu = dev16(normal_bf16((m, 2 * k), 2.0, 91 + m))
+    c, s, S, _ = q.qerl_quantize_nvfp4(dev16(L.w))
+    z = q.qerl_aqn_sample(92, 0, m, 1e-2, k, device="cuda:0") if noise else None
+    a = dev16(L.a) if r else None
+    b = dev16(L.b) if r else None
+    ref = q.qerl_linear_decode(q.qerl_swiglu(gu), c, s, S, a, b, 2.0, z)
+    got = q.qerl_linear_decode_swiglu(gu, c, s, S, a, b, 2.0, z)
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref)
