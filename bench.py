@@ -59,8 +59,9 @@ def parse():
                          "'prefill' runs one prepare and three prefill GEMMs on each of "
                          "the 7B qkv and down layers at M=4096; 'rmsnorm' runs one "
                          "plain device copy (counter calibration) and 20 noisy RMSNorms "
-                         "of 4096 x 3584 rows on rotated inputs; 'backward' runs three "
-                         "backward calls (dx, dA, dB) of the 7B down layer at M=4096; "
+                         "of 4096 x 3584 rows on rotated inputs; 'backward' runs one plain "
+                         "device copy (counter calibration) and three backward calls (dx, "
+                         "dA, dB) of the 7B down layer at M=4096; "
                          "'chain' runs PROFILE_LAUNCHES chained decode feed-forward steps "
                          "(noisy RMSNorm, gate/up, down on SwiGLU of the gate/up output); "
                          "'mxfp4' runs "
@@ -168,10 +169,17 @@ def profile_rmsnorm(q, to_dev, dev, m=4096, d=3584, copies=10, launches=20):
 
 
 def profile_backward(q, pc, make_layer, to_dev, dev, calls=3):
-    """Profiling pass of the backward: `calls` qerl_linear_backward calls
-    (dx, dA, dB) of the 7B down layer at M=4096, r=32."""
+    """Profiling pass of the backward: one plain copy of COPY_BYTES (counter
+    calibration), then `calls` qerl_linear_backward calls (dx, dA, dB) of
+    the 7B down layer at M=4096, r=32."""
     import torch
     from workloads import normal_bf16
+    src = torch.empty(COPY_BYTES // 2, dtype=torch.int16, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
     s_dn = pc.layers[1]
     L = make_layer(pc.m, s_dn.n, s_dn.k, pc.r, seed=12, stage=pc.stage, call_id=1)
     x, w, a, b = to_dev(L.x), to_dev(L.w), to_dev(L.a), to_dev(L.b)
