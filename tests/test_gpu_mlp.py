@@ -92,6 +92,7 @@ def test_chained_decode_mlp():
     (37, 128, 1024, 0, True),     # no LoRA branch (the elementwise x_t kernel)
     (64, 256, 512, 40, False),    # two rank groups, no noise
     (64, 3584, 18944, 32, True),  # the 7B down layer at 64 tokens
+    (130, 64, 272, 8, True),      # two decode chunks of m, k % 256 != 0 (general kernel)
 ])
 def test_decode_swiglu_is_swiglu_then_decode(m, n, k, r, noise):
     """qerl_linear_decode_swiglu(gate_up) == qerl_linear_decode(qerl_swiglu(gate_up)),
