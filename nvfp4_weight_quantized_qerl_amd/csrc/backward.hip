@@ -7,7 +7,7 @@
 //     dx = bf16( (S dy W0 + gs A) (.) (1 + z) )     W_hat = S W0 (Eq. 6)
 //     dA = gs^T x_t                                   [r, k] fp32
 //     dB = dy^T t                                     [n, r] fp32
-// Launches: the forward's prepare (x_t and t), a transpose of B, the
+// Launches: the forward's prepare (t only), a transpose of B, the
 // LoRA-down kernels on (dy, B^T) for gs, the dx contraction below, and for
 // each of dA and dB an accumulation over 256-row chunks plus a reduction of
 // the chunks in order.
@@ -28,6 +28,7 @@
 // barriers per step.
 #include <algorithm>
 
+#include "qerl_act.h"
 #include "qerl_device.h"
 #include "qerl_internal.h"
 
@@ -198,7 +199,10 @@ __global__ __launch_bounds__(kThreads) void bwd_dx(DxArgs a) {
 // token rows of p and q in LDS as they are stored (16-byte copies, rows padded
 // so that token rows 8 apart fall on different bank halves); the MFMA operands
 // (lane = column or j, eight consecutive tokens) are gathered from there with
-// 2-byte reads.  The next step's rows are loaded while the MFMAs run.
+// 2-byte reads.  The next step's rows are loaded while the MFMAs run.  With
+// a noise vector z the p rows are x and the contraction uses
+// x_t = bf16(x (1 + z)), formed as they are loaded (noisy8, the prepare's
+// arithmetic).
 // outer_reduce sums the chunks in chunk order.
 constexpr int kOuterRows = 256;
 constexpr int kOuterCols = 128;            // columns per workgroup
@@ -206,6 +210,7 @@ constexpr int kOuterLds = kOuterCols + 8;  // LDS row of the p tile (elements)
 
 template <int RT>
 __global__ __launch_bounds__(256) void outer_mfma(const uint16_t* __restrict__ p, int64_t ldp,
+                                                  const float* __restrict__ z,
                                                   const uint16_t* __restrict__ q, int64_t ldq,
                                                   int64_t m, int64_t cols, int r,
                                                   float* __restrict__ part) {
@@ -259,6 +264,15 @@ __global__ __launch_bounds__(256) void outer_mfma(const uint16_t* __restrict__ p
     return make_uint4(w[0], w[1], w[2], w[3]);
   };
 
+  // noise of this thread's eight p columns (the same in every step); the
+  // multiply is applied as the prefetched rows are stored, so that the
+  // loads of the next step stay in flight during the MFMAs
+  float4 z0 = make_float4(0.0f, 0.0f, 0.0f, 0.0f), z1 = z0;
+  const int64_t zcol = c0 + 8 * (tid & 15);
+  if (z && zcol < cols) {
+    z0 = *reinterpret_cast<const float4*>(z + zcol);
+    z1 = *reinterpret_cast<const float4*>(z + zcol + 4);
+  }
   f32x16_t acc[RT];
 #pragma unroll
   for (int t = 0; t < RT; ++t) acc[t] = zero16();
@@ -268,7 +282,8 @@ __global__ __launch_bounds__(256) void outer_mfma(const uint16_t* __restrict__ p
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int e = tid + 256 * i;
-      *reinterpret_cast<uint4*>(pt + (e >> 4) * kOuterLds + 8 * (e & 15)) = pv[i];
+      *reinterpret_cast<uint4*>(pt + (e >> 4) * kOuterLds + 8 * (e & 15)) =
+          z ? noisy8(pv[i], z0, z1) : pv[i];
     }
 #pragma unroll
     for (int i = 0; i < QPT; ++i) {
@@ -327,19 +342,25 @@ BackwardPlan make_backward_plan(int64_t m, int64_t n, int64_t k, int r) {
   BackwardPlan b{};
   make_linear_plan(m, n, k, r, &b.fwd);
   const int64_t mpad = b.fwd.mpad;
-  size_t off = rup64((int64_t)b.fwd.total, 256);
+  size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t o = off;
     off = (size_t)rup64((int64_t)(off + bytes), 256);
     return o;
   };
   const int rpad32 = r ? (int)rup64(r, 32) : 0, rpad16 = r ? (int)rup64(r, 16) : 0;
+  // Of the forward's workspace the backward uses only the LoRA-down partials
+  // and t (x_t is formed from x and z where it is needed, and not stored).
+  b.fwd.off_xt = 0;
+  b.fwd.off_ypart = 0;
+  b.fwd.off_tpart = take(r ? (size_t)b.fwd.kchunks * mpad * b.fwd.rpad32 * 4 : 0);
+  b.fwd.off_t = take(r ? (size_t)mpad * b.fwd.rpad16 * 2 : 0);
   b.off_bt = take(r ? (size_t)r * n * 2 : 0);
   b.off_gpart = take(r ? (size_t)((n + 511) / 512) * mpad * rpad32 * 4 : 0);
   b.off_gs = take(r ? (size_t)mpad * rpad16 * 2 : 0);
   b.mchunks = (int)((m + kOuterRows - 1) / kOuterRows);
   b.off_opart = take(r ? (size_t)b.mchunks * r * std::max(n, k) * 4 : 0);
-  b.total = off;
+  b.total = std::max<size_t>(off, 256);   // a size of 0 means invalid sizes
   return b;
 }
 
@@ -351,8 +372,9 @@ hipError_t launch_linear_backward(const BackwardPlan& b, const uint16_t* dy, con
   const LinearPlan& p = b.fwd;
   const int r = (lora_a && lora_b) ? p.r : 0;
   hipError_t e;
-  // x_t and t = s x_t A^T (the forward's prepare)
-  e = launch_linear_prepare(p, x, z, r ? lora_a : nullptr, lora_scale, ws, stream);
+  // t = s x_t A^T (the forward's prepare, without storing x_t: the dA
+  // contraction forms x_t from x and z as it loads them)
+  e = launch_linear_prepare(p, x, z, r ? lora_a : nullptr, lora_scale, ws, stream, false, false);
   if (e != hipSuccess) return e;
   uint16_t* gs = nullptr;
   if (r) {
@@ -392,14 +414,14 @@ hipError_t launch_linear_backward(const BackwardPlan& b, const uint16_t* dy, con
                        stream, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   float* opart = reinterpret_cast<float*>(ws + b.off_opart);
-  auto outer = [&](const uint16_t* pp, int64_t ldp, const uint16_t* qq, int64_t ldq,
-                   int64_t cols, float* out, int64_t oc, int64_t oj) {
+  auto outer = [&](const uint16_t* pp, int64_t ldp, const float* zz, const uint16_t* qq,
+                   int64_t ldq, int64_t cols, float* out, int64_t oc, int64_t oj) {
     const dim3 grid((unsigned)((cols + kOuterCols - 1) / kOuterCols), (unsigned)b.mchunks);
     switch ((r + 31) / 32) {
-      case 1: hipLaunchKernelGGL(outer_mfma<1>, grid, dim3(256), 0, stream, pp, ldp, qq, ldq, p.m, cols, r, opart); break;
-      case 2: hipLaunchKernelGGL(outer_mfma<2>, grid, dim3(256), 0, stream, pp, ldp, qq, ldq, p.m, cols, r, opart); break;
-      case 3: hipLaunchKernelGGL(outer_mfma<3>, grid, dim3(256), 0, stream, pp, ldp, qq, ldq, p.m, cols, r, opart); break;
-      default: hipLaunchKernelGGL(outer_mfma<4>, grid, dim3(256), 0, stream, pp, ldp, qq, ldq, p.m, cols, r, opart); break;
+      case 1: hipLaunchKernelGGL(outer_mfma<1>, grid, dim3(256), 0, stream, pp, ldp, zz, qq, ldq, p.m, cols, r, opart); break;
+      case 2: hipLaunchKernelGGL(outer_mfma<2>, grid, dim3(256), 0, stream, pp, ldp, zz, qq, ldq, p.m, cols, r, opart); break;
+      case 3: hipLaunchKernelGGL(outer_mfma<3>, grid, dim3(256), 0, stream, pp, ldp, zz, qq, ldq, p.m, cols, r, opart); break;
+      default: hipLaunchKernelGGL(outer_mfma<4>, grid, dim3(256), 0, stream, pp, ldp, zz, qq, ldq, p.m, cols, r, opart); break;
     }
     hipError_t e2 = hipGetLastError();
     if (e2 != hipSuccess) return e2;
@@ -408,15 +430,14 @@ hipError_t launch_linear_backward(const BackwardPlan& b, const uint16_t* dy, con
     return hipGetLastError();
   };
   if (r && da) {
-    // dA[j, col] = sum_i gs[i, j] x_t[i, col]
-    e = outer(reinterpret_cast<const uint16_t*>(ws + p.off_xt), p.k, gs, (int64_t)p.rpad16, p.k,
-              da, (int64_t)1, p.k);
+    // dA[j, col] = sum_i gs[i, j] x_t[i, col], x_t = bf16(x (1 + z)) formed on load
+    e = outer(x, p.k, z, gs, (int64_t)p.rpad16, p.k, da, (int64_t)1, p.k);
     if (e != hipSuccess) return e;
   }
   if (r && db) {
     // dB[col, j] = sum_i dy[i, col] t[i, j]
-    e = outer(dy, p.n, reinterpret_cast<const uint16_t*>(ws + p.off_t), (int64_t)p.rpad16, p.n,
-              db, (int64_t)r, (int64_t)1);
+    e = outer(dy, p.n, nullptr, reinterpret_cast<const uint16_t*>(ws + p.off_t),
+              (int64_t)p.rpad16, p.n, db, (int64_t)r, (int64_t)1);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

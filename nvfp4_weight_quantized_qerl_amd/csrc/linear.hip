@@ -152,19 +152,6 @@ struct PrepArgs {
   float lora_scale;
 };
 
-// x_t = bf16(x (1 + z)) of 8 consecutive channels from their noise z0, z1.
-__device__ __forceinline__ uint4 noisy8(uint4 xv, float4 z0, float4 z1) {
-  xv.x = pack_bf16x2(bf16_to_f32(xv.x & 0xffffu) * (1.0f + z0.x),
-                     bf16_to_f32(xv.x >> 16) * (1.0f + z0.y));
-  xv.y = pack_bf16x2(bf16_to_f32(xv.y & 0xffffu) * (1.0f + z0.z),
-                     bf16_to_f32(xv.y >> 16) * (1.0f + z0.w));
-  xv.z = pack_bf16x2(bf16_to_f32(xv.z & 0xffffu) * (1.0f + z1.x),
-                     bf16_to_f32(xv.z >> 16) * (1.0f + z1.y));
-  xv.w = pack_bf16x2(bf16_to_f32(xv.w & 0xffffu) * (1.0f + z1.z),
-                     bf16_to_f32(xv.w >> 16) * (1.0f + z1.w));
-  return xv;
-}
-
 // One workgroup: 32 rows x one 512-wide K chunk.
 //   x_t: wave w reads and writes rows 8 w .. 8 w + 7, one row of the chunk
 //        (1 KB) per instruction, lane l holding channels 8 l .. 8 l + 7; the
@@ -364,14 +351,14 @@ hipError_t launch_treduce(const LinearPlan& p, char* ws, hipStream_t stream) {
 hipError_t launch_linear_prepare(const LinearPlan& p, const uint16_t* x,
                                  const float* z, const uint16_t* lora_a,
                                  float lora_scale, char* ws,
-                                 hipStream_t stream, bool swiglu_input) {
+                                 hipStream_t stream, bool swiglu_input, bool write_xt) {
   PrepArgs a;
   a.x = x;
   a.ldx = swiglu_input ? 2 * p.k : p.k;
   a.swiglu = swiglu_input ? 1 : 0;
   a.z = z;
   a.a = lora_a;
-  a.xt = reinterpret_cast<uint16_t*>(ws + p.off_xt);
+  a.xt = write_xt ? reinterpret_cast<uint16_t*>(ws + p.off_xt) : nullptr;
   a.tpart = reinterpret_cast<float*>(ws + p.off_tpart);
   a.m = p.m;
   a.mpad = p.mpad;
@@ -380,6 +367,7 @@ hipError_t launch_linear_prepare(const LinearPlan& p, const uint16_t* x,
   a.rpad32 = p.rpad32;
   a.lora_scale = lora_scale;
   if (p.r == 0 || !lora_a) {
+    if (!write_xt) return hipSuccess;
     const int64_t threads = p.mpad * p.k / 8;
     hipLaunchKernelGGL(xt_kernel, dim3((unsigned)cdiv(threads, 256)), dim3(256), 0, stream, a);
     return hipGetLastError();

@@ -1,13 +1,30 @@
-// Gated feed-forward activation shared by the SwiGLU kernel and the
-// prepare kernel that forms the down layer's input from the fused gate/up
-// output (Qwen2.5 feed-forward block; W_gate, W_up, W_down [QeRL summary,
-// §3.4 "Layer coverage"]): both call these helpers, so their results are
-// bit-identical.
+// Elementwise helpers shared by several kernels, so that every kernel that
+// forms these values forms them bit-identically:
+//   noisy8   the AQN-noised activations x_t = bf16(x (1 + z)) [QeRL summary,
+//            §3.4, Eq. 12], used by the prepare and by the dA contraction
+//            of the backward;
+//   swiglu8  the gated feed-forward activation bf16(SiLU(gate) up) (Qwen2.5
+//            feed-forward block; W_gate, W_up, W_down [§3.4 "Layer
+//            coverage"]), used by the SwiGLU kernel and by the prepare that
+//            forms the down layer's input from the fused gate/up output.
 #pragma once
 
 #include "qerl_device.h"
 
 namespace qerl {
+
+// x_t = bf16(x (1 + z)) of 8 consecutive channels from their noise z0, z1.
+__device__ __forceinline__ uint4 noisy8(uint4 xv, float4 z0, float4 z1) {
+  xv.x = pack_bf16x2(bf16_to_f32(xv.x & 0xffffu) * (1.0f + z0.x),
+                     bf16_to_f32(xv.x >> 16) * (1.0f + z0.y));
+  xv.y = pack_bf16x2(bf16_to_f32(xv.y & 0xffffu) * (1.0f + z0.z),
+                     bf16_to_f32(xv.y >> 16) * (1.0f + z0.w));
+  xv.z = pack_bf16x2(bf16_to_f32(xv.z & 0xffffu) * (1.0f + z1.x),
+                     bf16_to_f32(xv.z >> 16) * (1.0f + z1.y));
+  xv.w = pack_bf16x2(bf16_to_f32(xv.w & 0xffffu) * (1.0f + z1.z),
+                     bf16_to_f32(xv.w >> 16) * (1.0f + z1.w));
+  return xv;
+}
 
 // SiLU(g) = g / (1 + exp(-g)) in fp32 with the hardware exponential and
 // reciprocal (each within a few fp32 ulps, far below one bf16 ulp, the

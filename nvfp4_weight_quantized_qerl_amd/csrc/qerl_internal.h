@@ -67,11 +67,14 @@ struct LinearPlan {
 bool make_linear_plan(int64_t m, int64_t n, int64_t k, int r, LinearPlan* p);
 
 // With swiglu_input, x is the fused gate/up output [m, 2k] and the layer
-// input is bf16(SiLU(gate) * up), formed as the rows are loaded.
+// input is bf16(SiLU(gate) * up), formed as the rows are loaded.  Without
+// write_xt only t is produced (x_t is not stored; nothing is launched
+// without a LoRA branch).
 hipError_t launch_linear_prepare(const LinearPlan& p, const uint16_t* x,
                                  const float* z, const uint16_t* lora_a,
                                  float lora_scale, char* ws,
-                                 hipStream_t stream, bool swiglu_input = false);
+                                 hipStream_t stream, bool swiglu_input = false,
+                                 bool write_xt = true);
 
 // t = bf16(scale x a_rk^T) for x [m, k] (rows m..mpad-1 read as zero) and
 // a_rk [r, k]: the LoRA-down kernels on any operands (partials [ceil(k/512),
@@ -108,8 +111,9 @@ hipError_t launch_linear_prefill_main(const LinearPlan& p, const uint8_t* codes,
                                       hipStream_t stream);
 
 // ----------------------------------------------------------------- backward
-// Workspace of the backward: the forward's prepare plan (x_t, t) followed by
-// B^T [r, n], the partials of s dy B and gs = bf16(s dy B) [mpad, rpad16].
+// Workspace of the backward: the forward prepare's LoRA-down partials and t
+// (fwd.off_tpart, fwd.off_t; no x_t), then B^T [r, n], the partials of
+// s dy B, gs = bf16(s dy B) [mpad, rpad16] and the dA / dB chunk partials.
 struct BackwardPlan {
   LinearPlan fwd;
   int mchunks;         // 256-row chunks of the dA / dB sums over the tokens
