@@ -1,37 +1,46 @@
 """Benchmark of the NVFP4 + LoRA + AQN linear layer on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--only sweep]
 
-A step is one rollout decode pass through a Qwen2.5-7B-shaped MLP block
-with M = 64 tokens (8 prompts x 8 samples): for each of the fused gate/up
-layer W [37888, 3584] and the down layer W [3584, 18944] (NVFP4, LoRA rank
-32, s = 2), draw the layer's AQN noise vector for stage 1 of 10 and run
-the linear layer (noisy activations, LoRA-down, NVFP4 contraction, LoRA-up
-epilogue).  The noise vectors do not depend on the activations, so they
-are drawn a few steps ahead on a second stream while earlier steps run.
-The weights are quantized once before timing (the pages load the
-quantized model once); the quantizer is timed on its own.  Six copies
-of the quantized weights (684 MB) are used in rotation so that the 256 MB
-Infinity Cache cannot serve them; inputs are resident in HBM before the
-timed region.
+Headline step: one rollout decode pass through a Qwen2.5-32B-shaped model
+(hidden 5120, intermediate 27648, 40 q / 8 kv heads of dim 128): 64 layers x
+{qkv [7168, 5120], o [5120, 5120], gate/up [55296, 5120], down [5120, 27648]}
+of NVFP4 weights (17.55 GB, streamed once per step), M = 128 rollout tokens
+(8 prompts x 16 samples), LoRA rank 64 (s = 2) on every projection, AQN
+stage 1 of 10.  A step draws the step's 256 noise vectors (one per
+projection and layer, call id 256 * step + 4 * layer + projection; four
+batched launches) and runs the 256 linear calls (noisy activations,
+LoRA-down, NVFP4 contraction, LoRA-up epilogue).  The weights are generated
+and quantized on the device once before timing (the pages load the
+quantized model once).  The calls are independent: each projection reads a
+fixed synthetic activation of its input width.
 
-Printed: one JSON line.  `value` = decode weight-stream GB/s (algorithmic
-bytes of the step / step time); `roofline` = the decode contraction kernel
-of the gate/up layer, timed alone with HIP events on its launch stream;
-`mxfp4_decode` = the gate/up contraction on the weight quantized to MXFP4
-(general and power-of-two dequantization);
-`mlp_chain` = the same weights run as one chained feed-forward block (noisy
-RMSNorm -> gate/up -> SiLU(gate) * up -> down) per step;
-`prefill` = the 4096-token prefill of the Qwen2.5-7B qkv and down layers
-in TFLOP/s; `rmsnorm` = the noisy RMSNorm producer on the 7B hidden size
-(GB/s at 4096 rows, microseconds at 64 rows); `quantizer` = bulk
-quantization GB/s; `cpu_baseline` = the oracle on the host cores on a
-bounded slice of the same step.
+Timing: W untimed warm-up steps, then K timed steps with a HIP event
+between consecutive steps on the launch stream; `value` = algorithmic bytes
+of a step / median step time (GB/s), with p10 / p90 beside it.  The same
+protocol (median, p10, p90 of per-iteration events) is used for every
+sub-measurement:
+  `roofline`            the dominant kernel: the gate/up contraction of the
+                        sweep (MFMA-bound at 128 tokens), timed alone;
+  `decode_7b_mlp`       the 7B MLP at 64 tokens (gate/up + down, noise drawn
+                        ahead on a second stream), its gate/up contraction
+                        kernel, the chained feed-forward block and the MXFP4
+                        weight;
+  `prefill_7b`          4096-token prefill of the 7B qkv and down layers, and
+                        the backward of the 7B down layer;
+  `quantize_prefill_14b` bulk quantization of every linear weight of a
+                        Qwen2.5-14B-shaped model (48 layers) and the
+                        16384-token prefill through one layer's o, gate, up,
+                        down;
+  `rmsnorm`             the noisy RMSNorm producer;
+  `cpu_baseline`        the oracle on the host cores on a labelled slice of
+                        the headline step.
 """
 import argparse
 import hashlib
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -41,39 +50,40 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 
+COPY_BYTES = 512 << 20         # calibration copy of the profiling passes
+PROFILE_LAUNCHES = 50          # contractions of a profiling pass
+
+PARTS = ("sweep", "decode7b", "prefill7b", "q14b", "rmsnorm")
+
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--copies", type=int, default=6)
+    ap.add_argument("--copies", type=int, default=6,
+                    help="rotated weight copies of the 7B decode measurements")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--no-prefill", action="store_true")
-    ap.add_argument("--no-chain", action="store_true")
-    ap.add_argument("--profile", nargs="?", const="decode",
-                    choices=("decode", "prefill", "rmsnorm", "backward", "chain", "mxfp4"),
+    ap.add_argument("--only", nargs="+", choices=PARTS, default=None,
+                    help="run only these parts (the headline is always reported when run)")
+    ap.add_argument("--profile", choices=("decode", "sweep32", "prefill", "rmsnorm", "backward",
+                                          "chain", "mxfp4", "quant14b", "prefill14b"),
                     help="profiling pass for rocprofv3, no timing and no JSON line: "
-                         "'decode' runs one plain device copy of COPY_BYTES (counter "
-                         "calibration) and PROFILE_LAUNCHES gate/up decode contractions; "
-                         "'prefill' runs one prepare and three prefill GEMMs on each of "
-                         "the 7B qkv and down layers at M=4096; 'rmsnorm' runs one "
-                         "plain device copy (counter calibration) and 20 noisy RMSNorms "
-                         "of 4096 x 3584 rows on rotated inputs; 'backward' runs one plain "
-                         "device copy (counter calibration) and three backward calls (dx, "
-                         "dA, dB) of the 7B down layer at M=4096; "
-                         "'chain' runs PROFILE_LAUNCHES chained decode feed-forward steps "
-                         "(noisy RMSNorm, gate/up, down on SwiGLU of the gate/up output); "
-                         "'mxfp4' runs "
-                         "PROFILE_LAUNCHES gate/up contractions on the MXFP4 weight with "
-                         "the general and then with the power-of-two dequantization")
+                         "'decode' = one plain copy of COPY_BYTES (counter calibration) and "
+                         "PROFILE_LAUNCHES 7B gate/up contractions at M=64; 'sweep32' = one "
+                         "plain copy, 3 full 32B sweep steps, then PROFILE_LAUNCHES 32B gate/up "
+                         "contractions at M=128; 'prefill' = per 7B layer at M=4096 one prepare "
+                         "and three prefill GEMMs; 'rmsnorm' = one plain copy and 20 noisy "
+                         "RMSNorms 4096x3584; 'backward' = one plain copy and three backward "
+                         "calls of the 7B down layer at M=4096; 'chain' = PROFILE_LAUNCHES "
+                         "chained 7B feed-forward steps; 'mxfp4' = PROFILE_LAUNCHES MXFP4 gate/up "
+                         "contractions with each dequantization; 'quant14b' = one plain copy and "
+                         "one bulk quantization of the 14B model; 'prefill14b' = per 14B layer "
+                         "(o, gate, up, down) at M=16384 one prepare and three prefill GEMMs")
     return ap.parse_args()
 
 
-COPY_BYTES = 512 << 20         # calibration copy of the profiling pass
-PROFILE_LAUNCHES = 50          # gate/up contractions in the profiling pass
-
-
+# ----------------------------------------------------------------- figures
 def linear_bytes(m, n, k, r):
     """Algorithmic bytes of one linear call: NVFP4 codes + scales, x, y,
     LoRA A and B (bf16), noise vector (fp32)."""
@@ -81,8 +91,8 @@ def linear_bytes(m, n, k, r):
 
 
 def main_kernel_bytes(m, n, k, r):
-    """Algorithmic bytes of the decode contraction kernel alone: codes +
-    scales, x_t (bf16), y, the LoRA B factor and t = s x_t A^T (bf16)."""
+    """Algorithmic bytes of the decode contraction alone: codes + scales,
+    x_t (bf16), y, the LoRA B factor and t = s x_t A^T (bf16)."""
     return 0.5625 * n * k + 2 * m * k + 2 * m * n + 2 * r * n + 2 * m * r
 
 
@@ -90,33 +100,74 @@ def linear_flops(m, n, k, r):
     return 2.0 * m * n * k + 2.0 * m * r * (k + n)
 
 
-# Noise ring of the decode step: slots, steps sampled ahead, refill period.
-# Slot safety: a refill at step i writes the slots of steps i + AHEAD - EVERY
-# + 1 .. i + AHEAD after steps <= i - EVERY finished; the steps that may
-# still read a slot are i - EVERY + 1 .. i + AHEAD - EVERY, so RING must
-# exceed AHEAD + EVERY - 1.
-NOISE_RING, NOISE_AHEAD, NOISE_EVERY = 12, 6, 4
-assert NOISE_RING > NOISE_AHEAD + NOISE_EVERY - 1
+def main_kernel_flops(m, n, k, r):
+    """Flops of the contraction alone: x_t W^T and the LoRA-up t B^T."""
+    return 2.0 * m * n * k + 2.0 * m * r * n
 
-# Sources of the decode contraction kernel timed for the roofline; the
-# committed counter summary is only used while their digest is unchanged.
-DECODE_SOURCES = ("decode_lds.h", "qerl_device.h", "decode.hip")
+
+def stats_ms(times_ms):
+    """median / p10 / p90 / mean of per-iteration times (ms)."""
+    import numpy as np
+    a = np.asarray(times_ms, dtype=np.float64)
+    return {"median_ms": round(float(np.median(a)), 5),
+            "p10_ms": round(float(np.percentile(a, 10)), 5),
+            "p90_ms": round(float(np.percentile(a, 90)), 5),
+            "mean_ms": round(float(a.mean()), 5), "iters": int(a.size)}
+
+
+def event_times(fn, iters, stream, warmup=3):
+    """Per-iteration times (ms) of fn(i), i = 0..iters-1, from HIP events
+    recorded between consecutive iterations on `stream` (after `warmup`
+    untimed calls)."""
+    import torch
+    for i in range(warmup):
+        fn(i)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)]
+    ev[0].record(stream)
+    for i in range(iters):
+        fn(i)
+        ev[i + 1].record(stream)
+    ev[-1].synchronize()
+    return [ev[i].elapsed_time(ev[i + 1]) for i in range(iters)]
+
+
+def gpu_clock():
+    """Current shader clock (MHz) as rocm-smi reports it, or None."""
+    try:
+        out = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True,
+                             text=True, timeout=20).stdout
+        data = json.loads(out[out.index("{"):])
+    except Exception:          # rocm-smi missing or unparsable: no clock recorded
+        return None
+    for card in data.values():
+        for key, val in card.items():
+            if "sclk" in key.lower():
+                digits = "".join(ch for ch in str(val) if ch.isdigit())
+                if digits:
+                    return int(digits)
+    return None
+
+
+# Sources of the decode contraction kernels; a committed counter summary is
+# only used while their digest is unchanged.
+DECODE_SOURCES = ("decode_lds.h", "decode_m128.h", "qerl_device.h", "decode.hip")
 
 
 def source_digest(*names):
     h = hashlib.sha256()
     for name in names:
-        with open(os.path.join(ROOT, "nvfp4_weight_quantized_qerl_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        path = os.path.join(ROOT, "nvfp4_weight_quantized_qerl_amd", "csrc", name)
+        if os.path.exists(path):
+            with open(path, "rb") as f:
+                h.update(f.read())
     return h.hexdigest()[:16]
 
 
 def measured_traffic(kernel_key, digest):
     """HBM bytes per launch from the committed rocprofv3 counter summary,
     if it was taken on the current kernel source."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
-        with open(path) as f:
+        with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
             rec = json.load(f).get(kernel_key)
     except (OSError, ValueError):
         return None
@@ -125,73 +176,194 @@ def measured_traffic(kernel_key, digest):
     return rec.get("hbm_bytes_per_launch")
 
 
-def profile_prefill(q, pc, make_layer, to_dev, dev):
-    """Profiling pass of the prefill GEMM: per 7B layer at M=4096, one
-    qerl_linear_prepare and three qerl_linear_prefill_prepared launches."""
+def calibration_copy(dev):
+    """One plain device copy of COPY_BYTES: its FETCH_SIZE / WRITE_SIZE
+    calibrate the counters of the kernels profiled after it."""
     import torch
-    psig = q.qerl_aqn_sigma(pc.sigma_start, pc.sigma_end, pc.num_stages, pc.stage)
-    for i, s in enumerate(pc.layers):
-        L = make_layer(pc.m, s.n, s.k, pc.r, seed=11 + i, stage=pc.stage, call_id=i)
-        x, w, a, b = to_dev(L.x), to_dev(L.w), to_dev(L.a), to_dev(L.b)
-        codes, scales, S, _ = q.qerl_quantize_nvfp4(w)
-        del w
-        z = q.qerl_aqn_sample(L.seed, 0, i, psig, s.k, device=dev)
-        ws = q.workspace(pc.m, s.n, s.k, pc.r, dev)
-        y = torch.empty((pc.m, s.n), dtype=torch.bfloat16, device=dev)
-        q.qerl_linear_prepare(x, s.n, a, pc.lora_scale, z, ws)
-        for _ in range(3):
-            q.qerl_linear_prefill_prepared(pc.m, codes, scales, S, s.k, b, y, ws)
+    src = torch.empty(COPY_BYTES // 2, dtype=torch.int16, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+
+
+def dev_normal(shape, std, gen, dev):
+    """N(0, std^2) drawn in fp32 on the device from a seeded generator and
+    rounded to bf16 (nearest even)."""
+    import torch
+    return (torch.randn(shape, generator=gen, device=dev, dtype=torch.float32)
+            * std).to(torch.bfloat16)
+
+
+# ------------------------------------------------- headline: the 32B sweep
+class Sweep32:
+    """The Qwen2.5-32B decode sweep (64 layers x 4 projections, M=128, r=64),
+    generated and quantized on the device (seeded), with every call bound."""
+
+    def __init__(self, q, cfg, dev, keep_host_layer0=False):
+        import torch
+        self.q, self.cfg, self.dev = q, cfg, dev
+        M, R = cfg.m, cfg.r
+        self.sigma = q.qerl_aqn_sigma(cfg.sigma_start, cfg.sigma_end, cfg.num_stages, cfg.stage)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(4000)
+        self.shapes = cfg.layers                     # qkv, o, gate_up, down
+        self.x = {}
+        for s in self.shapes:
+            if s.k not in self.x:
+                self.x[s.k] = dev_normal((M, s.k), 1.0, gen, dev)
+        self.z = [torch.empty((cfg.n_layers, s.k), dtype=torch.float32, device=dev)
+                  for s in self.shapes]
+        self.ws = [q.workspace(M, s.n, s.k, R, dev) for s in self.shapes]
+        self.y = [torch.empty((M, s.n), dtype=torch.bfloat16, device=dev) for s in self.shapes]
+        self.layers = []                             # [layer][proj] dict
+        self.host_w0 = []
+        flags = []
+        for li in range(cfg.n_layers):
+            row = []
+            for p, s in enumerate(self.shapes):
+                w = dev_normal((s.n, s.k), 0.02, gen, dev)
+                codes, scales, S, flag = q.qerl_quantize_nvfp4(w)
+                flags.append(flag)
+                if li == 0 and keep_host_layer0:
+                    self.host_w0.append(w[:512].view(torch.int16).cpu().numpy().view("uint16"))
+                del w
+                a = dev_normal((R, s.k), 0.02, gen, dev)
+                b = dev_normal((s.n, R), 0.01, gen, dev)
+                row.append(dict(codes=codes, scales=scales, S=S, a=a, b=b))
+            self.layers.append(row)
         torch.cuda.synchronize()
-        del x, a, b, codes, scales, ws, y
-    print("profile pass done: prefill_7b qkv and down, 3 GEMMs each")
+        assert all(int(f.item()) == 0 for f in flags)
+        self.calls = [[q.bind_linear(self.x[s.k], L["codes"], L["scales"], L["S"], L["a"], L["b"],
+                                     cfg.lora_scale, self.z[p][li], self.ws[p], self.y[p])
+                       for p, (s, L) in enumerate(zip(self.shapes, row))]
+                      for li, row in enumerate(self.layers)]
+        self.step_bytes = cfg.n_layers * sum(linear_bytes(M, s.n, s.k, R) for s in self.shapes)
+        self.step_flops = cfg.n_layers * sum(linear_flops(M, s.n, s.k, R) for s in self.shapes)
+        self.weight_bytes = cfg.n_layers * sum(0.5625 * s.n * s.k for s in self.shapes)
+
+    def step(self, i):
+        q, nl = self.q, self.cfg.n_layers
+        for p, s in enumerate(self.shapes):
+            q.qerl_aqn_sample_batch(4000, 0, 256 * i + p, 4, nl, self.sigma, s.k, out=self.z[p])
+        for row in self.calls:
+            for call in row:
+                call()
+
+    def gate_up_contraction(self, li):
+        """The gate/up contraction of layer li from the prepared workspace."""
+        s, L = self.shapes[2], self.layers[li][2]
+        self.q.qerl_linear_decode_prepared(self.cfg.m, L["codes"], L["scales"], L["S"], s.k,
+                                           L["b"], self.y[2], self.ws[2])
+
+    def prepare_gate_up(self):
+        s, L = self.shapes[2], self.layers[0][2]
+        self.q.qerl_aqn_sample(4000, 0, 2, self.sigma, s.k, out=self.z[2][0])
+        self.q.qerl_linear_prepare(self.x[s.k], s.n, L["a"], self.cfg.lora_scale, self.z[2][0],
+                                   self.ws[2])
 
 
-def profile_rmsnorm(q, to_dev, dev, m=4096, d=3584, copies=10, launches=20):
-    """Profiling pass of the noisy RMSNorm: one plain copy of COPY_BYTES
-    (counter calibration), then `launches` calls on rotated input copies."""
+def run_sweep(q, args, dev, stream):
     import torch
-    from workloads import norm_inputs
-    src = torch.empty(COPY_BYTES // 2, dtype=torch.int16, device=dev).fill_(1)
-    dst = torch.empty_like(src)
+    from workloads import CONFIGS
+    cfg = CONFIGS["decode_32b_sweep"]
+    t_setup = time.perf_counter()
+    sw = Sweep32(q, cfg, dev, keep_host_layer0=not args.no_cpu)
+    t_setup = time.perf_counter() - t_setup
+    for i in range(args.warmup):
+        sw.step(i)
     torch.cuda.synchronize()
-    dst.copy_(src)
+    clk0 = gpu_clock()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(args.steps):
+        sw.step(args.warmup + i)
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
-    del src, dst
-    x, w = norm_inputs(m, d, seed=31)
-    wd = to_dev(w)
-    xs = [to_dev(x) for _ in range(copies)]
-    ys = [torch.empty_like(xs[0]) for _ in range(copies)]
-    z = q.qerl_aqn_sample(31, 0, 0, 1e-2, d, device=dev)
-    for i in range(launches):
-        q.qerl_rmsnorm_noisy(xs[i % copies], wd, z, 1e-6, out=ys[i % copies])
-    torch.cuda.synchronize()
-    print(f"profile pass done: copy {COPY_BYTES} B, {launches} noisy RMSNorms {m}x{d}")
+    wall = time.perf_counter() - t0
+    clk1 = gpu_clock()
+    step_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
+    st = stats_ms(step_ms)
+    med_s = st["median_ms"] / 1e3
+
+    # the dominant kernel alone: the gate/up contraction (55296 x 5120, 128
+    # tokens, r = 64), rotating over the 64 layers' weights
+    sw.prepare_gate_up()
+    s = cfg.layers[2]
+    kt = event_times(lambda i: sw.gate_up_contraction(i % cfg.n_layers),
+                     max(100, args.steps), stream, warmup=5)
+    ks = stats_ms(kt)
+    avg_s = ks["mean_ms"] / 1e3
+    kflops = main_kernel_flops(cfg.m, s.n, s.k, cfg.r)
+    kbytes = main_kernel_bytes(cfg.m, s.n, s.k, cfg.r)
+    digest = source_digest(*DECODE_SOURCES)
+    roofline = {"bound": "mfma", "achieved": round(kflops / avg_s / 1e12, 1),
+                "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(kflops / avg_s / 1e12 / BF16_PEAK_TFLOPS, 4),
+                "traffic": measured_traffic("decode_gate_up_32b_m128", digest),
+                "kernel": "gate/up contraction of the 32B sweep (55296x5120, M=128, r=64): "
+                          "qerl_linear_decode_prepared",
+                "avg_launch_us": round(avg_s * 1e6, 2),
+                "median_launch_us": round(ks["median_ms"] * 1e3, 2),
+                "p10_launch_us": round(ks["p10_ms"] * 1e3, 2),
+                "p90_launch_us": round(ks["p90_ms"] * 1e3, 2),
+                "flops_per_launch": kflops, "bytes_per_launch": kbytes,
+                "GB_per_s": round(kbytes / avg_s / 1e9, 1),
+                "hbm_frac": round(kbytes / avg_s / 1e9 / HBM_PEAK_GBS, 4),
+                "roofline_us": round(max(kflops / BF16_PEAK_TFLOPS / 1e6,
+                                         kbytes / HBM_PEAK_GBS / 1e3), 2)}
+    roof_step_ms = max(sw.step_flops / BF16_PEAK_TFLOPS / 1e9, sw.step_bytes / HBM_PEAK_GBS / 1e6)
+    head = {
+        "value": round(sw.step_bytes / med_s / 1e9, 1),
+        "ms_per_step": st["median_ms"],
+        "timing": dict(st, wall_s=round(wall, 4), clock_mhz_before=clk0, clock_mhz_after=clk1),
+        "step": {"bytes": sw.step_bytes, "flops": sw.step_flops,
+                 "nvfp4_weight_bytes": sw.weight_bytes, "calls": 4 * cfg.n_layers,
+                 "tflops": round(sw.step_flops / med_s / 1e12, 1),
+                 "hbm_frac": round(sw.step_bytes / med_s / 1e9 / HBM_PEAK_GBS, 4),
+                 "roofline_ms": round(roof_step_ms, 4), "binding": "mfma",
+                 "frac_of_roofline": round(roof_step_ms / st["median_ms"], 4),
+                 "setup_s": round(t_setup, 1)},
+        "roofline": roofline,
+    }
+    return head, sw
 
 
-def profile_backward(q, pc, make_layer, to_dev, dev, calls=3):
-    """Profiling pass of the backward: one plain copy of COPY_BYTES (counter
-    calibration), then `calls` qerl_linear_backward calls (dx, dA, dB) of
-    the 7B down layer at M=4096, r=32."""
+# --------------------------------------------------- 7B MLP decode (config 2)
+# Noise ring of the 7B decode step: slots, steps sampled ahead, refill period.
+# Slot safety: a refill at step i writes the slots of steps i + AHEAD - EVERY
+# + 1 .. i + AHEAD after steps <= i - EVERY finished; the steps that may
+# still read a slot are i - EVERY + 1 .. i + AHEAD - EVERY, so RING must
+# exceed AHEAD + EVERY - 1.
+NOISE_RING, NOISE_AHEAD, NOISE_EVERY = 12, 6, 4
+assert NOISE_RING > NOISE_AHEAD + NOISE_EVERY - 1
+
+
+def setup_decode7b(q, args, dev, to_dev):
     import torch
-    from workloads import normal_bf16
-    src = torch.empty(COPY_BYTES // 2, dtype=torch.int16, device=dev).fill_(1)
-    dst = torch.empty_like(src)
+    from workloads import CONFIGS, make_layer
+    cfg = CONFIGS["decode_7b_mlp"]
+    M, R = cfg.m, cfg.r
+    layers = []
+    for i, s in enumerate(cfg.layers):
+        L = make_layer(M, s.n, s.k, R, seed=1 + i, stage=cfg.stage,
+                       outlier_frac=cfg.outlier_frac, call_id=i)
+        ly = dict(name=s.name, n=s.n, k=s.k, L=L, x=to_dev(L.x), a=to_dev(L.a), b=to_dev(L.b))
+        w = to_dev(L.w)
+        ly["codes"], ly["scales"], ly["S"], ly["flag"] = q.qerl_quantize_nvfp4(w)
+        del w
+        layers.append(ly)
     torch.cuda.synchronize()
-    dst.copy_(src)
-    torch.cuda.synchronize()
-    del src, dst
-    s_dn = pc.layers[1]
-    L = make_layer(pc.m, s_dn.n, s_dn.k, pc.r, seed=12, stage=pc.stage, call_id=1)
-    x, w, a, b = to_dev(L.x), to_dev(L.w), to_dev(L.a), to_dev(L.b)
-    codes, scales, S, _ = q.qerl_quantize_nvfp4(w)
-    del w
-    psig = q.qerl_aqn_sigma(pc.sigma_start, pc.sigma_end, pc.num_stages, pc.stage)
-    z = q.qerl_aqn_sample(L.seed, 0, 1, psig, s_dn.k, device=dev)
-    dy = to_dev(normal_bf16((pc.m, s_dn.n), 1.0, 12050))
-    for _ in range(calls):
-        q.qerl_linear_backward(dy, x, codes, scales, S, a, b, pc.lora_scale, z)
-    torch.cuda.synchronize()
-    print(f"profile pass done: {calls} backward calls of the 7B down layer at M={pc.m}")
+    assert all(int(ly["flag"].item()) == 0 for ly in layers)
+    sigma = q.qerl_aqn_sigma(cfg.sigma_start, cfg.sigma_end, cfg.num_stages, cfg.stage)
+    copies = max(1, args.copies)
+    for ly in layers:
+        ly["rot"] = [(ly["codes"], ly["scales"])] + [
+            (ly["codes"].clone(), ly["scales"].clone()) for _ in range(copies - 1)]
+        ly["ws"] = q.workspace(M, ly["n"], ly["k"], R, dev)
+        ly["y"] = torch.empty((M, ly["n"]), dtype=torch.bfloat16, device=dev)
+    return cfg, layers, sigma, copies
 
 
 def make_chain(q, layers, cfg, to_dev, dev, sigma, copies):
@@ -201,6 +373,7 @@ def make_chain(q, layers, cfg, to_dev, dev, sigma, copies):
     prepare forms from the gate/up output (qerl_linear_decode_swiglu).  The
     two noise vectors are drawn here, before any timing.  Returns (step
     function, algorithmic bytes of one step)."""
+    import torch
     from workloads import norm_inputs
     M, R = cfg.m, cfg.r
     gu_l, dn_l = layers
@@ -209,17 +382,16 @@ def make_chain(q, layers, cfg, to_dev, dev, sigma, copies):
     xres, wnorm = to_dev(xres_bits), to_dev(wn_bits)
     z_gu = q.qerl_aqn_sample(41, 0, 0, sigma, d_model, device=dev)
     z_dn = q.qerl_aqn_sample(41, 0, 1, sigma, d_inter, device=dev)
-    import torch
     h = torch.empty((M, d_model), dtype=torch.bfloat16, device=dev)
+    gu = [q.bind_linear(h, c, s, gu_l["S"], gu_l["a"], gu_l["b"], cfg.lora_scale, None,
+                        gu_l["ws"], gu_l["y"]) for c, s in gu_l["rot"]]
+    dn = [q.bind_linear(gu_l["y"], c, s, dn_l["S"], dn_l["a"], dn_l["b"], cfg.lora_scale, z_dn,
+                        dn_l["ws"], dn_l["y"], entry="decode_swiglu") for c, s in dn_l["rot"]]
 
     def chain_step(i):
-        cg, sg = gu_l["rot"][i % copies]
-        cd, sd = dn_l["rot"][i % copies]
         q.qerl_rmsnorm_noisy(xres, wnorm, z_gu, 1e-6, out=h)
-        q.qerl_linear_decode(h, cg, sg, gu_l["S"], gu_l["a"], gu_l["b"], cfg.lora_scale,
-                             None, workspace=gu_l["ws"], y=gu_l["y"])
-        q.qerl_linear_decode_swiglu(gu_l["y"], cd, sd, dn_l["S"], dn_l["a"], dn_l["b"],
-                                    cfg.lora_scale, z_dn, workspace=dn_l["ws"], y=dn_l["y"])
+        gu[i % copies]()
+        dn[i % copies]()
 
     chain_bytes = (4 * M * d_model + 6 * d_model
                    + linear_bytes(M, gu_l["n"], d_model, R) - 4 * d_model
@@ -241,31 +413,324 @@ def make_mxfp4(q, gl, cfg, make_layer, to_dev, copies, z):
     return mrot, mg, mflag
 
 
-def oracle_step_rate(cfg, layers, M, R, min_seconds=10.0, max_reps=20):
-    """The oracle running the decode step on the host: per layer, sample z,
-    dequantize the NVFP4 weight and evaluate the fp64 linear layer with the
-    LoRA branch.  As on the GPU, the weights are quantized (by the oracle)
-    before timing; the step is repeated until min_seconds have passed."""
-    import threadpoolctl
-    from oracle import aqn, formats, linear, nvfp4
+def run_decode7b(q, args, dev, stream, to_dev):
+    import torch
+    from workloads import make_layer
+    cfg, layers, sigma, copies = setup_decode7b(q, args, dev, to_dev)
+    M, R = cfg.m, cfg.r
 
-    prepared = []
-    for ly in layers:
-        L = ly["L"]
-        w = formats.bf16_bits_to_f64(L.w)
-        S = nvfp4.global_scale(nvfp4.tensor_amax(w))
-        codes, scales = nvfp4.encode_with_scale(w, S)
-        del w
-        prepared.append((L, codes, scales, S))
-    sig = aqn.sigma(cfg.sigma_start, cfg.sigma_end, cfg.num_stages, cfg.stage)
+    # The AQN noise of a forward pass does not depend on its activations, so a
+    # second stream (default priority) samples the noise vectors a few steps
+    # ahead into a ring of slots, and each step waits only for its own slot.
+    # Every NOISE_EVERY steps the main stream marks its progress and the host,
+    # before refilling slots, waits for the mark of NOISE_EVERY steps earlier:
+    # no slot is rewritten while a queued step may still read it.
+    side = torch.cuda.Stream(device=dev)
+    zring = [[torch.empty(ly["k"], dtype=torch.float32, device=dev) for ly in layers]
+             for _ in range(NOISE_RING)]
+    z_ready = [torch.cuda.Event() for _ in range(NOISE_RING)]
+    marks = {}
+    calls = [[[q.bind_linear(ly["x"], c, s, ly["S"], ly["a"], ly["b"], cfg.lora_scale,
+                             zring[sl][li], ly["ws"], ly["y"]) for (c, s) in ly["rot"]]
+              for li, ly in enumerate(layers)] for sl in range(NOISE_RING)]
+
+    def sample(j):
+        sl = j % NOISE_RING
+        for li, ly in enumerate(layers):
+            q.qerl_aqn_sample(ly["L"].seed, 0, 2 * j + li, sigma, ly["k"],
+                              out=zring[sl][li], stream=side)
+        z_ready[sl].record(side)
+
+    def step(i):
+        sl = i % NOISE_RING
+        stream.wait_event(z_ready[sl])
+        for li in range(len(layers)):
+            calls[sl][li][i % copies]()
+        if i % NOISE_EVERY == NOISE_EVERY - 1:
+            mark = torch.cuda.Event()
+            mark.record(stream)
+            marks[i] = mark
+            old = marks.pop(i - NOISE_EVERY, None)
+            if old is not None:
+                old.synchronize()        # steps <= i - NOISE_EVERY are done
+            for j in range(i + NOISE_AHEAD - NOISE_EVERY + 1, i + NOISE_AHEAD + 1):
+                sample(j)
+
+    for j in range(NOISE_AHEAD):
+        sample(j)
+    steps = max(100, args.steps)
+    st = stats_ms(event_times(step, steps, stream, warmup=max(NOISE_EVERY, args.warmup)))
+    torch.cuda.synchronize()
     step_bytes = sum(linear_bytes(M, ly["n"], ly["k"], R) for ly in layers)
+    out = {"workload": "decode_7b_mlp: Qwen2.5-7B-shaped MLP, M=64 (8 prompts x 8 samples), "
+                       "gate/up 37888x3584 + down 3584x18944 NVFP4, LoRA r=32, AQN stage 1/10",
+           "weight_copies_rotated": copies,
+           "GB_per_s": round(step_bytes / (st["median_ms"] / 1e3) / 1e9, 1),
+           "hbm_frac": round(step_bytes / (st["median_ms"] / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+           "timing": st}
+
+    # the gate/up contraction kernel alone
+    ly = layers[0]
+    q.qerl_linear_prepare(ly["x"], ly["n"], ly["a"], cfg.lora_scale, zring[0][0], ly["ws"])
+    kt = event_times(lambda i: q.qerl_linear_decode_prepared(M, *ly["rot"][i % copies], ly["S"],
+                                                             ly["k"], ly["b"], ly["y"], ly["ws"]),
+                     steps, stream, warmup=5)
+    ks = stats_ms(kt)
+    kbytes = main_kernel_bytes(M, ly["n"], ly["k"], R)
+    avg_s = ks["mean_ms"] / 1e3
+    out["gate_up_kernel"] = {
+        "bound": "hbm", "achieved": round(kbytes / avg_s / 1e9, 1), "peak": HBM_PEAK_GBS,
+        "unit": "GB/s", "frac": round(kbytes / avg_s / 1e9 / HBM_PEAK_GBS, 4),
+        "traffic": measured_traffic("decode_main_gate_up_7b", source_digest(*DECODE_SOURCES)),
+        "kernel": "decode_lds<2,5> (gate/up 37888x3584, M=64, r=32)",
+        "avg_launch_us": round(avg_s * 1e6, 2),
+        "median_launch_us": round(ks["median_ms"] * 1e3, 2),
+        "p10_launch_us": round(ks["p10_ms"] * 1e3, 2),
+        "p90_launch_us": round(ks["p90_ms"] * 1e3, 2), "bytes_per_launch": kbytes}
+
+    # the same weights as a chained feed-forward block
+    chain_step, chain_bytes = make_chain(q, layers, cfg, to_dev, dev, sigma, copies)
+    cs = stats_ms(event_times(chain_step, steps, stream, warmup=args.warmup))
+    out["mlp_chain"] = {
+        "workload": "noisy RMSNorm -> gate/up -> down on SiLU(gate)*up (formed in the down "
+                    "layer's prepare), M=64",
+        "us_per_step": round(cs["median_ms"] * 1e3, 2),
+        "GB_per_s": round(chain_bytes / (cs["median_ms"] / 1e3) / 1e9, 1),
+        "frac_hbm": round(chain_bytes / (cs["median_ms"] / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+        "timing": cs}
+
+    # the gate/up weight as MXFP4 in the NVFP4 layout: general and power-of-two
+    # dequantization, three interleaved rounds, median of all launches
+    gl = layers[0]
+    mrot, mg, mflag = make_mxfp4(q, gl, cfg, make_layer, to_dev, copies, zring[0][0])
+    mx = {"workload": "gate/up 37888x3584 MXFP4 weight in the NVFP4 layout, M=64, r=32",
+          "range_flag": int(mflag.item())}
+    mx_t = {"general": [], "pow2": []}
+    for _ in range(3):
+        for name, fn in (("general", q.qerl_linear_decode_prepared),
+                         ("pow2", q.qerl_linear_decode_prepared_mxfp4)):
+            mx_t[name] += event_times(lambda i: fn(M, *mrot[i % copies], mg, gl["k"], gl["b"],
+                                                   gl["y"], gl["ws"]), 40, stream, warmup=5)
+    for name, v in mx_t.items():
+        mx[name + "_us"] = round(stats_ms(v)["median_ms"] * 1e3, 2)
+    mx["pow2_GB_per_s"] = round(kbytes / (mx["pow2_us"] * 1e-6) / 1e9, 1)
+    out["mxfp4_decode"] = mx
+    del mrot, layers, calls
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
+# ----------------------------------------------- 7B prefill + backward (config 3)
+def run_prefill7b(q, args, dev, stream, to_dev):
+    import torch
+    from workloads import CONFIGS, make_layer, normal_bf16
+    pc = CONFIGS["prefill_7b"]
+    psig = q.qerl_aqn_sigma(pc.sigma_start, pc.sigma_end, pc.num_stages, pc.stage)
+    reps = 20
+    per_layer, t_full, t_main, pflops = [], 0.0, 0.0, 0.0
+    for i, s in enumerate(pc.layers):
+        L = make_layer(pc.m, s.n, s.k, pc.r, seed=11 + i, stage=pc.stage, call_id=i)
+        x, w, a, b = to_dev(L.x), to_dev(L.w), to_dev(L.a), to_dev(L.b)
+        codes, scales, S, _ = q.qerl_quantize_nvfp4(w)
+        del w
+        z = q.qerl_aqn_sample(L.seed, 0, i, psig, s.k, device=dev)
+        ws = q.workspace(pc.m, s.n, s.k, pc.r, dev)
+        y = torch.empty((pc.m, s.n), dtype=torch.bfloat16, device=dev)
+        full = q.bind_linear(x, codes, scales, S, a, b, pc.lora_scale, z, ws, y, entry="prefill")
+        tf = stats_ms(event_times(lambda i: full(), reps, stream))
+        q.qerl_linear_prepare(x, s.n, a, pc.lora_scale, z, ws)
+        tm = stats_ms(event_times(lambda i: q.qerl_linear_prefill_prepared(
+            pc.m, codes, scales, S, s.k, b, y, ws), reps, stream))
+        fl = linear_flops(pc.m, s.n, s.k, pc.r)
+        per_layer.append({"layer": f"{s.name} {s.n}x{s.k}",
+                          "tflops": round(fl / tf["median_ms"] / 1e9, 1),
+                          "gemm_tflops": round(fl / tm["median_ms"] / 1e9, 1),
+                          "ms": tf["median_ms"], "gemm_ms": tm["median_ms"],
+                          "p10_ms": tf["p10_ms"], "p90_ms": tf["p90_ms"]})
+        t_full += tf["median_ms"]
+        t_main += tm["median_ms"]
+        pflops += fl
+        del x, a, b, codes, scales, ws, y, full
+    out = {"workload": "prefill_7b (qkv 4608x3584 + down 3584x18944, M=4096, r=32, AQN stage "
+                       "5/10)",
+           "tflops": round(pflops / t_full / 1e9, 1), "gemm_tflops": round(pflops / t_main / 1e9, 1),
+           "ms": round(t_full, 4),
+           "frac_bf16_peak": round(pflops / t_full / 1e9 / BF16_PEAK_TFLOPS, 4),
+           "gemm_frac_bf16_peak": round(pflops / t_main / 1e9 / BF16_PEAK_TFLOPS, 4),
+           "reps": reps, "layers": per_layer}
+
+    # backward through the frozen NVFP4 weight of the 7B down layer, 4096 tokens
+    s_dn = pc.layers[1]
+    L = make_layer(pc.m, s_dn.n, s_dn.k, pc.r, seed=12, stage=pc.stage, call_id=1)
+    x, w, a, b = to_dev(L.x), to_dev(L.w), to_dev(L.a), to_dev(L.b)
+    codes, scales, S, _ = q.qerl_quantize_nvfp4(w)
+    del w
+    z = q.qerl_aqn_sample(L.seed, 0, 1, psig, s_dn.k, device=dev)
+    dy = to_dev(normal_bf16((pc.m, s_dn.n), 1.0, 12050))
+    bws = torch.empty(q.lib.qerl_linear_backward_workspace_bytes(pc.m, s_dn.n, s_dn.k, pc.r),
+                      dtype=torch.uint8, device=dev)
+    tb = stats_ms(event_times(lambda i: q.qerl_linear_backward(dy, x, codes, scales, S, a, b,
+                                                               pc.lora_scale, z, workspace=bws),
+                              reps, stream))
+    mm, nn, kk, rr = pc.m, s_dn.n, s_dn.k, pc.r
+    bflops = (2.0 * mm * nn * kk          # dy W_hat
+              + 2.0 * mm * rr * kk * 3     # t = x_t A^T, gs A, dA
+              + 2.0 * mm * nn * rr * 2)    # gs = dy B, dB
+    out["backward"] = {"workload": f"backward of the 7B down layer: dy {mm}x{nn}, W {nn}x{kk} "
+                                   f"NVFP4, r={rr} (dx, dA, dB)",
+                       "ms": tb["median_ms"], "p10_ms": tb["p10_ms"], "p90_ms": tb["p90_ms"],
+                       "tflops": round(bflops / tb["median_ms"] / 1e9, 1),
+                       "frac_bf16_peak": round(bflops / tb["median_ms"] / 1e9 / BF16_PEAK_TFLOPS,
+                                               4)}
+    del x, a, b, codes, scales, dy, bws
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
+# ------------------------------------ 14B bulk quantizer + prefill (config 5)
+class Model14b:
+    """Every linear weight of a Qwen2.5-14B-shaped model (48 layers x {q, k,
+    v, o, gate, up, down}) as bf16 on the device (seeded), with the output
+    buffers of the bulk quantization and one bound quantize call each."""
+
+    def __init__(self, q, cfg, dev):
+        import torch
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(5000)
+        self.cfg = cfg
+        self.tensors = []
+        for li in range(cfg.n_layers):
+            for s in cfg.layers:
+                w = dev_normal((s.n, s.k), 0.02, gen, dev)
+                codes = torch.empty((s.n, s.k // 2), dtype=torch.uint8, device=dev)
+                scales = torch.empty((s.n, s.k // 16), dtype=torch.uint8, device=dev)
+                S = torch.empty(1, dtype=torch.float32, device=dev)
+                flag = torch.empty(1, dtype=torch.int32, device=dev)
+                self.tensors.append(dict(layer=li, name=s.name, n=s.n, k=s.k, w=w, codes=codes,
+                                         scales=scales, S=S, flag=flag))
+        self.calls = [q.bind_quantize_nvfp4(t["w"], t["codes"], t["scales"], t["S"], t["flag"])
+                      for t in self.tensors]
+        self.elements = sum(t["n"] * t["k"] for t in self.tensors)
+
+    def quantize_all(self, i=0):
+        for c in self.calls:
+            c()
+
+
+def run_14b(q, args, dev, stream):
+    import torch
+    from workloads import CONFIGS
+    cfg = CONFIGS["quantize_prefill_14b"]
+    mdl = Model14b(q, cfg, dev)
+    torch.cuda.synchronize()
+    qt = stats_ms(event_times(mdl.quantize_all, 5, stream, warmup=1))
+    flags = torch.stack([t["flag"] for t in mdl.tensors])
+    assert int(flags.max().item()) == 0
+    qbytes = 2.5625 * mdl.elements
+    out = {"workload": "quantize_prefill_14b: bulk NVFP4 quantization of every linear weight of a "
+                       "Qwen2.5-14B-shaped model (48 layers x q, k, v, o, gate, up, down; "
+                       "N(0, 0.02^2) bf16), then prefill M=16384 through layer 0's o, gate, up "
+                       "and down (r=32, AQN stage 1)",
+           "quantizer": {"tensors": len(mdl.tensors), "elements": mdl.elements,
+                         "bytes_per_elem": 2.5625, "ms": qt["median_ms"],
+                         "GB_per_s": round(qbytes / qt["median_ms"] / 1e6, 1),
+                         "hbm_frac": round(qbytes / qt["median_ms"] / 1e6 / HBM_PEAK_GBS, 4),
+                         "roofline_ms": round(qbytes / HBM_PEAK_GBS / 1e6, 4), "timing": qt}}
+    # prefill through layer 0's o, gate, up, down at 16384 tokens
+    M, R = cfg.m, cfg.r
+    sig = q.qerl_aqn_sigma(cfg.sigma_start, cfg.sigma_end, cfg.num_stages, cfg.stage)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5100)
+    xs = {}
+    per_layer, t_tot, f_tot = [], 0.0, 0.0
+    layer0 = {t["name"]: t for t in mdl.tensors if t["layer"] == 0}
+    mdl.calls = None
+    mdl.tensors = None
+    for t in layer0.values():
+        del t["w"]
+    torch.cuda.empty_cache()
+    for name in ("o", "gate", "up", "down"):
+        t = layer0[name]
+        n, k = t["n"], t["k"]
+        if k not in xs:
+            xs[k] = dev_normal((M, k), 1.0, gen, dev)
+        a = dev_normal((R, k), 0.02, gen, dev)
+        b = dev_normal((n, R), 0.01, gen, dev)
+        z = q.qerl_aqn_sample(5100, 0, len(per_layer), sig, k, device=dev)
+        ws = q.workspace(M, n, k, R, dev)
+        y = torch.empty((M, n), dtype=torch.bfloat16, device=dev)
+        call = q.bind_linear(xs[k], t["codes"], t["scales"], t["S"], a, b, cfg.lora_scale, z, ws,
+                             y, entry="prefill")
+        tt = stats_ms(event_times(lambda i: call(), 20, stream))
+        fl = linear_flops(M, n, k, R)
+        per_layer.append({"layer": f"{name} {n}x{k}", "ms": tt["median_ms"],
+                          "p10_ms": tt["p10_ms"], "p90_ms": tt["p90_ms"],
+                          "tflops": round(fl / tt["median_ms"] / 1e9, 1)})
+        t_tot += tt["median_ms"]
+        f_tot += fl
+        del a, b, z, ws, y, call
+    out["prefill"] = {"tokens": M, "ms": round(t_tot, 4), "tflops": round(f_tot / t_tot / 1e9, 1),
+                      "frac_bf16_peak": round(f_tot / t_tot / 1e9 / BF16_PEAK_TFLOPS, 4),
+                      "roofline_ms": round(f_tot / BF16_PEAK_TFLOPS / 1e9, 4),
+                      "layers": per_layer}
+    del mdl, xs, layer0
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
+# ------------------------------------------------------------- noisy RMSNorm
+def run_rmsnorm(q, dev, stream, to_dev):
+    import torch
+    from workloads import norm_inputs
+    res = []
+    for m, d, copies_n in ((4096, 3584, 10), (64, 3584, 1)):
+        xs_, ws_ = norm_inputs(m, d, seed=31)
+        wd = to_dev(ws_)
+        xcopies = [to_dev(xs_) for _ in range(copies_n)]
+        ycopies = [torch.empty_like(xcopies[0]) for _ in range(copies_n)]
+        zd = q.qerl_aqn_sample(31, 0, 0, 1e-2, d, device=dev)
+        st = stats_ms(event_times(lambda i: q.qerl_rmsnorm_noisy(
+            xcopies[i % copies_n], wd, zd, 1e-6, out=ycopies[i % copies_n]), 100, stream,
+            warmup=5))
+        t = st["median_ms"] / 1e3
+        nbytes = 4 * m * d + 2 * d + 4 * d
+        res.append({"workload": f"noisy RMSNorm {m}x{d} (Qwen2.5-7B hidden)",
+                    "us": round(t * 1e6, 2), "GB_per_s": round(nbytes / t / 1e9, 1),
+                    "frac_hbm": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4), "bytes": nbytes})
+    return res
+
+
+# --------------------------------------------------------- oracle on the host
+def oracle_sweep_rate(sw, min_seconds=12.0, max_reps=30):
+    """The oracle running a labelled slice of the headline step on the host:
+    layer 0 of the 32B sweep, the first 512 output rows of each of its four
+    projections, all 128 tokens and all K: per projection, draw the noise
+    vector, dequantize the NVFP4 weight slice and evaluate the fp64 linear
+    layer with the LoRA branch.  The weight slices are quantized by the oracle
+    before timing (the GPU step also runs on weights quantized beforehand)."""
+    import numpy as np
+    import threadpoolctl
+    import torch
+    from oracle import aqn, linear, nvfp4
+    cfg = sw.cfg
+    rows = 512
+    prepared = []
+    for p, s in enumerate(sw.shapes):
+        codes, scales, S = nvfp4.quantize(sw.host_w0[p])
+        L = sw.layers[0][p]
+        host = lambda t: t.view(torch.int16).cpu().numpy().view(np.uint16)
+        prepared.append((s, codes, scales, S, host(sw.x[s.k]), host(L["a"]),
+                         host(L["b"][:rows])))
+    sbytes = sum(linear_bytes(cfg.m, rows, s.k, cfg.r) for s in sw.shapes)
     reps, t0 = 0, time.perf_counter()
     while True:
-        for li, (L, codes, scales, S) in enumerate(prepared):
-            z = aqn.sample(L.seed, 0, 2 * reps + li, sig, L.x.shape[1])
+        for p, (s, codes, scales, S, x, a, b) in enumerate(prepared):
+            z = aqn.sample(4000, 0, 256 * reps + p, sw.sigma, s.k)
             w_hat = nvfp4.dequantize(codes, scales, S)
-            linear.linear(L.x, w_hat, z, L.a, L.b, cfg.lora_scale)
-            del w_hat
+            linear.linear(x, w_hat, z, a, b, cfg.lora_scale)
         reps += 1
         dt = time.perf_counter() - t0
         if dt >= min_seconds or reps >= max_reps:
@@ -273,13 +738,125 @@ def oracle_step_rate(cfg, layers, M, R, min_seconds=10.0, max_reps=20):
     blas = [p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()
             if p.get("user_api") == "blas"]
     threads = max(blas) if blas else 1
-    return {"value": round(reps * step_bytes / dt / 1e9, 4), "unit": "GB/s",
-            "cores": threads, "kind": "oracle",
-            "sample": f"{reps} full decode step(s), both layers and all rows (noise "
-                      f"sample, NVFP4 dequantization, fp64 linear with LoRA), {dt:.1f} s; "
-                      "weights quantized by the oracle before timing; dequantization "
-                      f"runs on one thread, the fp64 matmuls on {threads} BLAS threads "
-                      f"of {len(os.sched_getaffinity(0))} host cores"}
+    return {"value": round(reps * sbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{reps} repetition(s) in {dt:.1f} s of a slice of the 32B sweep step: "
+                      f"layer 0, the first {rows} output rows of each of qkv, o, gate/up and "
+                      "down (all 128 tokens, all K, r=64): noise vector, NVFP4 dequantization, "
+                      f"fp64 linear with LoRA; {sbytes / 1e6:.1f} MB algorithmic per repetition; "
+                      "weights quantized by the oracle before timing; noise and dequantization "
+                      f"on one thread, the fp64 matmuls on {threads} BLAS threads of "
+                      f"{len(os.sched_getaffinity(0))} host cores"}
+
+
+# ------------------------------------------------------------ profiling passes
+def profile_pass(q, args, dev, stream, to_dev):
+    import torch
+    from workloads import CONFIGS, make_layer, normal_bf16
+    kind = args.profile
+    if kind in ("decode", "sweep32", "rmsnorm", "backward", "quant14b"):
+        calibration_copy(dev)
+    if kind == "sweep32":
+        sw = Sweep32(q, CONFIGS["decode_32b_sweep"], dev)
+        for i in range(3):
+            sw.step(i)
+        sw.prepare_gate_up()
+        for i in range(PROFILE_LAUNCHES):
+            sw.gate_up_contraction(i % sw.cfg.n_layers)
+        torch.cuda.synchronize()
+        print(f"profile pass done: copy {COPY_BYTES} B, 3 sweep steps, {PROFILE_LAUNCHES} 32B "
+              "gate/up contractions at M=128")
+        return
+    if kind == "quant14b":
+        mdl = Model14b(q, CONFIGS["quantize_prefill_14b"], dev)
+        mdl.quantize_all()
+        torch.cuda.synchronize()
+        print(f"profile pass done: copy {COPY_BYTES} B, one bulk quantization of "
+              f"{len(mdl.tensors)} tensors")
+        return
+    if kind in ("prefill", "prefill14b"):
+        if kind == "prefill":
+            pc = CONFIGS["prefill_7b"]
+            shapes = pc.layers
+        else:
+            pc = CONFIGS["quantize_prefill_14b"]
+            shapes = [s for s in pc.layers if s.name in ("o", "gate", "up", "down")]
+        psig = q.qerl_aqn_sigma(pc.sigma_start, pc.sigma_end, pc.num_stages, pc.stage)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(5200)
+        for i, s in enumerate(shapes):
+            x = dev_normal((pc.m, s.k), 1.0, gen, dev)
+            w = dev_normal((s.n, s.k), 0.02, gen, dev)
+            a = dev_normal((pc.r, s.k), 0.02, gen, dev)
+            b = dev_normal((s.n, pc.r), 0.01, gen, dev)
+            codes, scales, S, _ = q.qerl_quantize_nvfp4(w)
+            del w
+            z = q.qerl_aqn_sample(5200, 0, i, psig, s.k, device=dev)
+            ws = q.workspace(pc.m, s.n, s.k, pc.r, dev)
+            y = torch.empty((pc.m, s.n), dtype=torch.bfloat16, device=dev)
+            q.qerl_linear_prepare(x, s.n, a, pc.lora_scale, z, ws)
+            for _ in range(3):
+                q.qerl_linear_prefill_prepared(pc.m, codes, scales, S, s.k, b, y, ws)
+            torch.cuda.synchronize()
+            del x, a, b, codes, scales, ws, y
+        print(f"profile pass done: {kind}, one prepare and 3 GEMMs per layer")
+        return
+    if kind == "rmsnorm":
+        from workloads import norm_inputs
+        m, d, copies, launches = 4096, 3584, 10, 20
+        x, w = norm_inputs(m, d, seed=31)
+        wd = to_dev(w)
+        xs = [to_dev(x) for _ in range(copies)]
+        ys = [torch.empty_like(xs[0]) for _ in range(copies)]
+        z = q.qerl_aqn_sample(31, 0, 0, 1e-2, d, device=dev)
+        for i in range(launches):
+            q.qerl_rmsnorm_noisy(xs[i % copies], wd, z, 1e-6, out=ys[i % copies])
+        torch.cuda.synchronize()
+        print(f"profile pass done: copy {COPY_BYTES} B, {launches} noisy RMSNorms {m}x{d}")
+        return
+    if kind == "backward":
+        pc = CONFIGS["prefill_7b"]
+        s_dn = pc.layers[1]
+        L = make_layer(pc.m, s_dn.n, s_dn.k, pc.r, seed=12, stage=pc.stage, call_id=1)
+        x, w, a, b = to_dev(L.x), to_dev(L.w), to_dev(L.a), to_dev(L.b)
+        codes, scales, S, _ = q.qerl_quantize_nvfp4(w)
+        del w
+        psig = q.qerl_aqn_sigma(pc.sigma_start, pc.sigma_end, pc.num_stages, pc.stage)
+        z = q.qerl_aqn_sample(L.seed, 0, 1, psig, s_dn.k, device=dev)
+        dy = to_dev(normal_bf16((pc.m, s_dn.n), 1.0, 12050))
+        for _ in range(3):
+            q.qerl_linear_backward(dy, x, codes, scales, S, a, b, pc.lora_scale, z)
+        torch.cuda.synchronize()
+        print(f"profile pass done: 3 backward calls of the 7B down layer at M={pc.m}")
+        return
+    # decode / chain / mxfp4: the 7B MLP weights
+    cfg, layers, sigma, copies = setup_decode7b(q, args, dev, to_dev)
+    M = cfg.m
+    if kind == "chain":
+        chain_step, _ = make_chain(q, layers, cfg, to_dev, dev, sigma, copies)
+        for i in range(PROFILE_LAUNCHES):
+            chain_step(i)
+        torch.cuda.synchronize()
+        print(f"profile pass done: {PROFILE_LAUNCHES} chained decode feed-forward steps")
+        return
+    gl = layers[0]
+    z = q.qerl_aqn_sample(gl["L"].seed, 0, 0, sigma, gl["k"], device=dev)
+    if kind == "mxfp4":
+        mrot, mg, _ = make_mxfp4(q, gl, cfg, make_layer, to_dev, copies, z)
+        for fn in (q.qerl_linear_decode_prepared, q.qerl_linear_decode_prepared_mxfp4):
+            for i in range(PROFILE_LAUNCHES):
+                fn(M, *mrot[i % copies], mg, gl["k"], gl["b"], gl["y"], gl["ws"])
+        torch.cuda.synchronize()
+        print(f"profile pass done: {PROFILE_LAUNCHES} MXFP4 gate/up contractions with each "
+              "dequantization")
+        return
+    q.qerl_linear_prepare(gl["x"], gl["n"], gl["a"], cfg.lora_scale, z, gl["ws"])
+    for i in range(PROFILE_LAUNCHES):
+        c, s = gl["rot"][i % copies]
+        q.qerl_linear_decode_prepared(M, c, s, gl["S"], gl["k"], gl["b"], gl["y"], gl["ws"])
+    torch.cuda.synchronize()
+    print(f"profile pass done: copy {COPY_BYTES} B, {PROFILE_LAUNCHES} gate/up contractions "
+          f"({main_kernel_bytes(M, gl['n'], gl['k'], cfg.r):.0f} algorithmic B each)")
 
 
 def main():
@@ -294,357 +871,51 @@ def main():
     import torch
 
     import nvfp4_weight_quantized_qerl_amd as q
-    from workloads import CONFIGS, make_layer
 
     dev = "cuda:0"
     torch.cuda.set_device(0)
     to_dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
     stream = torch.cuda.current_stream()
 
-    if args.profile == "prefill":
-        profile_prefill(q, CONFIGS["prefill_7b"], make_layer, to_dev, dev)
-        return
-    if args.profile == "rmsnorm":
-        profile_rmsnorm(q, to_dev, dev)
-        return
-    if args.profile == "backward":
-        profile_backward(q, CONFIGS["prefill_7b"], make_layer, to_dev, dev)
-        return
-
-    cfg = CONFIGS["decode_7b_mlp"]
-    M, R = cfg.m, cfg.r
-    layers = []
-    for i, s in enumerate(cfg.layers):
-        L = make_layer(M, s.n, s.k, R, seed=1 + i, stage=cfg.stage,
-                       outlier_frac=cfg.outlier_frac, call_id=i)
-        layers.append(dict(name=s.name, n=s.n, k=s.k, L=L, x=to_dev(L.x), w=to_dev(L.w),
-                           a=to_dev(L.a), b=to_dev(L.b)))
-
-    # ---- quantize once (timed on its own: bulk quantizer GB/s)
-    torch.cuda.synchronize()
-    qtimes = []
-    for rep in range(3):
-        t0 = time.perf_counter()
-        for ly in layers:
-            ly["codes"], ly["scales"], ly["S"], ly["flag"] = q.qerl_quantize_nvfp4(ly["w"])
-        torch.cuda.synchronize()
-        qtimes.append(time.perf_counter() - t0)
-    q_elems = sum(ly["n"] * ly["k"] for ly in layers)
-    q_bytes = 2.5625 * q_elems
-    assert all(int(ly["flag"].item()) == 0 for ly in layers)
-
-    sigma = q.qerl_aqn_sigma(cfg.sigma_start, cfg.sigma_end, cfg.num_stages, cfg.stage)
-    copies = max(1, args.copies)
-    for ly in layers:
-        ly["rot"] = [(ly["codes"], ly["scales"])] + [
-            (ly["codes"].clone(), ly["scales"].clone()) for _ in range(copies - 1)]
-        ly["z"] = torch.empty(ly["k"], dtype=torch.float32, device=dev)
-        ly["ws"] = q.workspace(M, ly["n"], ly["k"], R, dev)
-        ly["y"] = torch.empty((M, ly["n"]), dtype=torch.bfloat16, device=dev)
-        del ly["w"]
-    torch.cuda.empty_cache()
-
-    if args.profile == "chain":
-        chain_step, _ = make_chain(q, layers, cfg, to_dev, dev, sigma, copies)
-        for i in range(PROFILE_LAUNCHES):
-            chain_step(i)
-        torch.cuda.synchronize()
-        print(f"profile pass done: {PROFILE_LAUNCHES} chained decode feed-forward steps")
-        return
-    if args.profile == "mxfp4":
-        gl = layers[0]
-        z = q.qerl_aqn_sample(gl["L"].seed, 0, 0, sigma, gl["k"], device=dev)
-        mrot, mg, _ = make_mxfp4(q, gl, cfg, make_layer, to_dev, copies, z)
-        for fn in (q.qerl_linear_decode_prepared, q.qerl_linear_decode_prepared_mxfp4):
-            for i in range(PROFILE_LAUNCHES):
-                fn(M, *mrot[i % copies], mg, gl["k"], gl["b"], gl["y"], gl["ws"])
-        torch.cuda.synchronize()
-        print(f"profile pass done: {PROFILE_LAUNCHES} MXFP4 gate/up contractions with each "
-              "dequantization")
-        return
     if args.profile:
-        # Plain copy of known size: FETCH_SIZE / WRITE_SIZE of this dispatch
-        # calibrate the counters of the contraction kernel below.
-        src = torch.empty(COPY_BYTES // 2, dtype=torch.int16, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-        ly = layers[0]
-        q.qerl_aqn_sample(ly["L"].seed, 0, 0, sigma, ly["k"], out=ly["z"])
-        q.qerl_linear_prepare(ly["x"], ly["n"], ly["a"], cfg.lora_scale, ly["z"], ly["ws"])
-        for i in range(PROFILE_LAUNCHES):
-            c, s = ly["rot"][i % copies]
-            q.qerl_linear_decode_prepared(M, c, s, ly["S"], ly["k"], ly["b"], ly["y"], ly["ws"])
-        torch.cuda.synchronize()
-        print(f"profile pass done: copy {COPY_BYTES} B, {PROFILE_LAUNCHES} gate/up contractions "
-              f"({main_kernel_bytes(M, ly['n'], ly['k'], R):.0f} algorithmic B each)")
+        profile_pass(q, args, dev, stream, to_dev)
         return
 
-    # The AQN noise of a forward pass does not depend on its activations, so a
-    # second stream (default priority) samples the noise vectors a few steps
-    # ahead into a ring of slots, and each step waits only for its own slot.
-    # Every NOISE_EVERY steps the main stream marks its progress and the host,
-    # before refilling slots, waits for the mark of NOISE_EVERY steps earlier:
-    # no slot is rewritten while a queued step may still read it.  (A wait of
-    # the side stream on an event of the main stream, each step, serialised
-    # the queues on this runtime.)
-    side = torch.cuda.Stream(device=dev)
-    zring = [[torch.empty(ly["k"], dtype=torch.float32, device=dev) for ly in layers]
-             for _ in range(NOISE_RING)]
-    z_ready = [torch.cuda.Event() for _ in range(NOISE_RING)]
-    marks = {}
-
-    def sample(j):
-        sl = j % NOISE_RING
-        for li, ly in enumerate(layers):
-            q.qerl_aqn_sample(ly["L"].seed, 0, 2 * j + li, sigma, ly["k"],
-                              out=zring[sl][li], stream=side)
-        z_ready[sl].record(side)
-
-    def step(i):
-        sl = i % NOISE_RING
-        stream.wait_event(z_ready[sl])
-        for li, ly in enumerate(layers):
-            codes, scales = ly["rot"][i % copies]
-            q.qerl_linear_decode(ly["x"], codes, scales, ly["S"], ly["a"], ly["b"],
-                                 cfg.lora_scale, zring[sl][li], workspace=ly["ws"], y=ly["y"])
-        if i % NOISE_EVERY == NOISE_EVERY - 1:
-            mark = torch.cuda.Event()
-            mark.record(stream)
-            marks[i] = mark
-            old = marks.pop(i - NOISE_EVERY, None)
-            if old is not None:
-                old.synchronize()        # steps <= i - NOISE_EVERY are done
-            for j in range(i + NOISE_AHEAD - NOISE_EVERY + 1, i + NOISE_AHEAD + 1):
-                sample(j)
-
-    for j in range(NOISE_AHEAD):
-        sample(j)
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(args.warmup + i)
-    torch.cuda.synchronize()
-    dt = time.perf_counter() - t0
-    ms_per_step = 1e3 * dt / args.steps
-    step_bytes = sum(linear_bytes(M, ly["n"], ly["k"], R) for ly in layers)
-    value = step_bytes / (dt / args.steps) / 1e9
-
-    # ---- the same 7B weights as one chained decode feed-forward block: noisy
-    # RMSNorm (Eq. 10, noise of the gate/up group) -> fused gate/up layer (no
-    # noise of its own) -> SiLU(gate) * up -> down layer (its own noise).  The
-    # two noise vectors are drawn before timing (the step above draws them on
-    # a second stream, off its critical path).
-    chain = None
-    if not args.no_chain:
-        chain_step, chain_bytes = make_chain(q, layers, cfg, to_dev, dev, sigma, copies)
-        for i in range(args.warmup):
-            chain_step(i)
-        c0 = torch.cuda.Event(enable_timing=True)
-        c1 = torch.cuda.Event(enable_timing=True)
-        c0.record(stream)
-        for i in range(args.steps):
-            chain_step(i)
-        c1.record(stream)
-        c1.synchronize()
-        t_chain = c0.elapsed_time(c1) / 1e3 / args.steps
-        chain = {"workload": "decode_7b_mlp chained: noisy RMSNorm -> gate/up -> down on "
-                             "SiLU(gate)*up (formed in the down layer's prepare), M=64",
-                 "us_per_step": round(t_chain * 1e6, 2),
-                 "GB_per_s": round(chain_bytes / t_chain / 1e9, 1),
-                 "frac_hbm": round(chain_bytes / t_chain / 1e9 / HBM_PEAK_GBS, 4)}
-
-    # ---- the gate/up weight as MXFP4 (E8M0 per 32) in the NVFP4 layout: the
-    # contraction with the general dequantization and with the power-of-two
-    # one, same rotation and workspace as the NVFP4 roofline pass below
-    mx = None
-    if not args.no_chain:
-        gl = layers[0]
-        mrot, mg, mflag = make_mxfp4(q, gl, cfg, make_layer, to_dev, copies, zring[0][0])
-        mx = {"workload": "gate/up 37888x3584 MXFP4 weight in the NVFP4 layout, M=64, r=32",
-              "range_flag": int(mflag.item())}
-        mx_bytes = main_kernel_bytes(M, gl["n"], gl["k"], R)
-        # three interleaved rounds, median per variant (box noise is ~±5%)
-        mx_t = {"general_us": [], "pow2_us": []}
-        for _ in range(3):
-            for name, fn in (("general_us", q.qerl_linear_decode_prepared),
-                             ("pow2_us", q.qerl_linear_decode_prepared_mxfp4)):
-                for i in range(5):
-                    fn(M, *mrot[i % copies], mg, gl["k"], gl["b"], gl["y"], gl["ws"])
-                m0 = torch.cuda.Event(enable_timing=True)
-                m1 = torch.cuda.Event(enable_timing=True)
-                m0.record(stream)
-                for i in range(max(20, args.steps)):
-                    fn(M, *mrot[i % copies], mg, gl["k"], gl["b"], gl["y"], gl["ws"])
-                m1.record(stream)
-                m1.synchronize()
-                mx_t[name].append(m0.elapsed_time(m1) * 1e3 / max(20, args.steps))
-        for name, v in mx_t.items():
-            mx[name] = round(sorted(v)[1], 2)
-        mx["pow2_GB_per_s"] = round(mx_bytes / (mx["pow2_us"] * 1e-6) / 1e9, 1)
-        del mrot
-
-    # ---- dominant kernel alone: gate/up contraction, HIP events on its stream
-    ly = layers[0]
-    q.qerl_linear_prepare(ly["x"], ly["n"], ly["a"], cfg.lora_scale, zring[0][0], ly["ws"])
-    reps = max(20, args.steps)
-    for i in range(5):
-        c, s = ly["rot"][i % copies]
-        q.qerl_linear_decode_prepared(M, c, s, ly["S"], ly["k"], ly["b"], ly["y"], ly["ws"])
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    for i in range(reps):
-        c, s = ly["rot"][i % copies]
-        q.qerl_linear_decode_prepared(M, c, s, ly["S"], ly["k"], ly["b"], ly["y"], ly["ws"])
-    ev1.record(stream)
-    ev1.synchronize()
-    kern_s = ev0.elapsed_time(ev1) / 1e3 / reps
-    kbytes = main_kernel_bytes(M, ly["n"], ly["k"], R)
-    achieved = kbytes / kern_s / 1e9
-    digest = source_digest(*DECODE_SOURCES)
-    traffic = measured_traffic("decode_main_gate_up_7b", digest)
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": traffic, "kernel": "decode_main (gate/up 37888x3584, M=64, r=32)",
-                "avg_launch_us": round(kern_s * 1e6, 2), "bytes_per_launch": kbytes}
-
-    # ---- prefill (Qwen2.5-7B qkv and down, 4096 tokens): TFLOP/s, for the
-    # whole call (prepare + GEMM) and for the GEMM kernel alone
-    prefill = None
-    backward = None
-    if not args.no_prefill:
-        pc = CONFIGS["prefill_7b"]
-        psig = q.qerl_aqn_sigma(pc.sigma_start, pc.sigma_end, pc.num_stages, pc.stage)
-        per_layer, t_full, t_main, pflops = [], 0.0, 0.0, 0.0
-        for i, s in enumerate(pc.layers):
-            L = make_layer(pc.m, s.n, s.k, pc.r, seed=11 + i, stage=pc.stage, call_id=i)
-            x, w, a, b = to_dev(L.x), to_dev(L.w), to_dev(L.a), to_dev(L.b)
-            codes, scales, S, _ = q.qerl_quantize_nvfp4(w)
-            del w
-            z = q.qerl_aqn_sample(L.seed, 0, i, psig, s.k, device=dev)
-            ws = q.workspace(pc.m, s.n, s.k, pc.r, dev)
-            y = torch.empty((pc.m, s.n), dtype=torch.bfloat16, device=dev)
-
-            def timed(fn, reps=5):
-                for _ in range(2):
-                    fn()
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                for _ in range(reps):
-                    fn()
-                e1.record(stream)
-                e1.synchronize()
-                return e0.elapsed_time(e1) / 1e3 / reps
-
-            tf = timed(lambda: q.qerl_linear_prefill(x, codes, scales, S, a, b, pc.lora_scale,
-                                                      z, workspace=ws, y=y))
-            q.qerl_linear_prepare(x, s.n, a, pc.lora_scale, z, ws)
-            tm = timed(lambda: q.qerl_linear_prefill_prepared(pc.m, codes, scales, S, s.k, b,
-                                                               y, ws))
-            fl = linear_flops(pc.m, s.n, s.k, pc.r)
-            per_layer.append({"layer": f"{s.name} {s.n}x{s.k}",
-                              "tflops": round(fl / tf / 1e12, 1),
-                              "gemm_tflops": round(fl / tm / 1e12, 1),
-                              "ms": round(1e3 * tf, 3), "gemm_ms": round(1e3 * tm, 3)})
-            t_full += tf
-            t_main += tm
-            pflops += fl
-            del x, a, b, codes, scales, ws, y
-        # backward through the frozen NVFP4 weight of the 7B down layer at the
-        # same 4096 tokens: dx, dA and dB
-        s_dn = pc.layers[1]
-        L = make_layer(pc.m, s_dn.n, s_dn.k, pc.r, seed=12, stage=pc.stage, call_id=1)
-        x, w, a, b = to_dev(L.x), to_dev(L.w), to_dev(L.a), to_dev(L.b)
-        codes, scales, S, _ = q.qerl_quantize_nvfp4(w)
-        del w
-        z = q.qerl_aqn_sample(L.seed, 0, 1, psig, s_dn.k, device=dev)
-        from workloads import normal_bf16
-        dy = to_dev(normal_bf16((pc.m, s_dn.n), 1.0, 12050))
-        bws = torch.empty(q.lib.qerl_linear_backward_workspace_bytes(pc.m, s_dn.n, s_dn.k, pc.r),
-                          dtype=torch.uint8, device=dev)
-        tb = timed(lambda: q.qerl_linear_backward(dy, x, codes, scales, S, a, b, pc.lora_scale,
-                                                  z, workspace=bws), reps=3)
-        mm, nn, kk, rr = pc.m, s_dn.n, s_dn.k, pc.r
-        bflops = (2.0 * mm * nn * kk          # dy W_hat
-                  + 2.0 * mm * rr * kk * 3     # t = x_t A^T, gs A, dA
-                  + 2.0 * mm * nn * rr * 2)    # gs = dy B, dB
-        backward = {"workload": f"backward of the 7B down layer: dy {mm}x{nn}, W {nn}x{kk} "
-                                f"NVFP4, r={rr} (dx, dA, dB)",
-                    "ms": round(1e3 * tb, 3), "tflops": round(bflops / tb / 1e12, 1),
-                    "frac_bf16_peak": round(bflops / tb / 1e12 / BF16_PEAK_TFLOPS, 4)}
-        del x, a, b, codes, scales, dy, bws
-        prefill = {"workload": "prefill_7b (qkv 4608x3584 + down 3584x18944, M=4096, r=32)",
-                   "tflops": round(pflops / t_full / 1e12, 1),
-                   "gemm_tflops": round(pflops / t_main / 1e12, 1),
-                   "ms": round(1e3 * t_full, 3),
-                   "frac_bf16_peak": round(pflops / t_full / 1e12 / BF16_PEAK_TFLOPS, 4),
-                   "gemm_frac_bf16_peak": round(pflops / t_main / 1e12 / BF16_PEAK_TFLOPS, 4),
-                   "layers": per_layer}
-
-    # ---- noisy RMSNorm producer (Eq. 10) on the 7B hidden size: the 4096-token
-    # prefill rows (HBM-bound; copies rotated past the Infinity Cache) and the
-    # 64 decode rows (latency-bound)
-    rmsnorm = None
-    if not args.no_prefill:
-        from workloads import norm_inputs
-        rmsnorm = []
-        for m, d, copies_n in ((4096, 3584, 10), (64, 3584, 1)):
-            xs_, ws_ = norm_inputs(m, d, seed=31)
-            wd = to_dev(ws_)
-            xcopies = [to_dev(xs_) for _ in range(copies_n)]
-            ycopies = [torch.empty_like(xcopies[0]) for _ in range(copies_n)]
-            zd = q.qerl_aqn_sample(31, 0, 0, sigma, d, device=dev)
-            run = lambda i: q.qerl_rmsnorm_noisy(xcopies[i % copies_n], wd, zd, 1e-6,
-                                                 out=ycopies[i % copies_n])
-            for i in range(5):
-                run(i)
-            reps = 50
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for i in range(reps):
-                run(i)
-            e1.record(stream)
-            e1.synchronize()
-            t = e0.elapsed_time(e1) / 1e3 / reps
-            nbytes = 4 * m * d + 2 * d + 4 * d
-            rmsnorm.append({"workload": f"noisy RMSNorm {m}x{d} (Qwen2.5-7B hidden)",
-                            "us": round(t * 1e6, 2), "GB_per_s": round(nbytes / t / 1e9, 1),
-                            "frac_hbm": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4),
-                            "bytes": nbytes})
-            del xcopies, ycopies
-
-    # ---- oracle on the host cores: the same step, weights quantized beforehand
+    parts = set(args.only or PARTS)
+    out = {"metric": "NVFP4+LoRA linear: decode weight-stream GB/s and prefill TFLOP/s, "
+                     "% roofline",
+           "value": None, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": None, "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16 (NVFP4 weights)",
+           "data": "synthetic",
+           "config": {"workload": "decode_32b_sweep: Qwen2.5-32B-shaped decode step, 64 layers x "
+                                  "{qkv 7168x5120, o 5120x5120, gate/up 55296x5120, down "
+                                  "5120x27648} NVFP4 (17.55 GB streamed per step), M=128 (8 "
+                                  "prompts x 16 samples), LoRA r=64 on every projection, AQN "
+                                  "stage 1/10 with one noise vector per projection and layer",
+                      "global_batch": 128, "parallelism": "none (1 GPU)"}}
     cpu = None
-    if not args.no_cpu:
-        cpu = oracle_step_rate(cfg, layers, M, R)
-
-    out = {
-        "metric": "NVFP4+LoRA linear: decode weight-stream GB/s and prefill TFLOP/s, % roofline",
-        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16 (NVFP4 weights)", "data": "synthetic",
-        "config": {"workload": "decode_7b_mlp: Qwen2.5-7B-shaped MLP, M=64 (8 prompts x 8 "
-                               "samples), gate/up 37888x3584 + down 3584x18944 NVFP4, LoRA "
-                               "r=32, AQN stage 1/10", "global_batch": M,
-                   "weight_copies_rotated": copies, "parallelism": "none (1 GPU)"},
-        "roofline": roofline,
-        "step_frac_hbm": round(value / HBM_PEAK_GBS, 4),
-        "prefill": prefill,
-        "rmsnorm": rmsnorm,
-        "mlp_chain": chain,
-        "backward": backward,
-        "mxfp4_decode": mx,
-        "quantizer": {"GB_per_s": round(q_bytes / min(qtimes) / 1e9, 1),
-                      "elements": q_elems, "bytes_per_elem": 2.5625},
-        "cpu_baseline": cpu,
-    }
+    if "sweep" in parts:
+        head, sw = run_sweep(q, args, dev, stream)
+        out["value"] = head["value"]
+        out["ms_per_step"] = head["ms_per_step"]
+        out["roofline"] = head["roofline"]
+        out["timing"] = head["timing"]
+        out["step"] = head["step"]
+        if not args.no_cpu:
+            cpu = oracle_sweep_rate(sw)
+        del sw
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    if "decode7b" in parts:
+        out["decode_7b_mlp"] = run_decode7b(q, args, dev, stream, to_dev)
+    if "prefill7b" in parts:
+        out["prefill_7b"] = run_prefill7b(q, args, dev, stream, to_dev)
+    if "q14b" in parts:
+        out["quantize_prefill_14b"] = run_14b(q, args, dev, stream)
+    if "rmsnorm" in parts:
+        out["rmsnorm"] = run_rmsnorm(q, dev, stream, to_dev)
+    out["cpu_baseline"] = cpu
     print(json.dumps(out))
 
 

@@ -192,6 +192,21 @@ QERL_API qerl_status qerl_aqn_sample(uint64_t seed, uint64_t stream_id,
                             float* z_out, void* stream);
 
 /*
+ * qerl_aqn_sample_batch -- `count` noise vectors in one launch, for the
+ * layers of a forward pass that each draw their own [QeRL summary, §3.4,
+ * Eq. 7; "Per-block noise sharing" (Fig. 6): one vector per noise group of
+ * every layer].  Row i of z_out [count, d] is bit-identical to
+ * qerl_aqn_sample(seed, stream_id, call_id0 + i * call_stride, sigma, d).
+ *   count  1 .. 65535
+ *   z_out  device out, [count, d] float, 4-byte aligned
+ * Other arguments and errors as qerl_aqn_sample.
+ */
+QERL_API qerl_status qerl_aqn_sample_batch(uint64_t seed, uint64_t stream_id,
+                                           uint64_t call_id0, uint64_t call_stride,
+                                           int64_t count, double sigma, int64_t d,
+                                           float* z_out, void* stream);
+
+/*
  * qerl_rmsnorm_noisy -- the noisy RMSNorm that produces a linear layer's
  * input [QeRL summary, §3.4 "Noise Merging", Eq. 10]:
  *     y[i, j] = bf16( (w_j + z_j) * x[i, j] / sqrt(mean_j' x[i, j']^2 + delta) )

@@ -2,9 +2,14 @@
 
 Python binding of libqerl.so (C ABI: include/qerl.h).  Each function has
 the name of the C call it wraps and does argument marshalling only: it
-checks devices and dtypes, allocates outputs with torch, passes raw device
-pointers and torch's current HIP stream, and raises QerlError on a
-non-zero status.  Every step of the computation runs in the HIP kernels.
+checks devices, dtypes and shapes (the C ABI receives raw pointers and
+cannot), allocates outputs with torch, passes raw device pointers and
+torch's current HIP stream, and raises QerlError on a non-zero status.
+Every step of the computation runs in the HIP kernels.
+
+`bind_linear` marshals the arguments of one linear call once and returns a
+callable that re-issues it, for callers that repeat the same call many times
+(every layer of every decode step).
 """
 import ctypes
 
@@ -48,6 +53,41 @@ def _bits16(t, name):
     return t.contiguous()
 
 
+def _need(t, name, dtype, shape, device):
+    """Check a tensor argument that goes to the library as a raw pointer."""
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    dts = dtype if isinstance(dtype, tuple) else (dtype,)
+    if t.dtype not in dts:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {' or '.join(map(str, dts))}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def _check_linear_args(m, n, k, r, dev, codes, scales, gscale, lora_a=None, lora_b=None, z=None,
+                       y=None):
+    _need(codes, "codes", torch.uint8, (n, k // 2), dev)
+    _need(scales, "scales", torch.uint8, (n, k // 16), dev)
+    if not isinstance(gscale, torch.Tensor) or gscale.dtype != torch.float32 or \
+            gscale.numel() < 1 or gscale.device != dev:
+        raise TypeError("gscale must be a float32 device tensor with at least one element")
+    if lora_a is not None:
+        _need(lora_a, "lora_a", _BF16, (r, k), dev)
+    if lora_b is not None:
+        _need(lora_b, "lora_b", _BF16, (n, r), dev)
+    _need(z, "z", torch.float32, (k,), dev)
+    _need(y, "y", _BF16, (m, n), dev)
+
+
 def qerl_abi_version():
     return lib.qerl_abi_version()
 
@@ -65,6 +105,22 @@ def qerl_quantize_nvfp4(w):
     _check(lib.qerl_quantize_nvfp4(_ptr(w), n, k, _ptr(codes), _ptr(scales), _ptr(gscale),
                                    _ptr(flag), _stream(dev)), "qerl_quantize_nvfp4")
     return codes, scales, gscale, flag
+
+
+def bind_quantize_nvfp4(w, codes, scales, gscale, flag=None):
+    """A BoundCall of qerl_quantize_nvfp4 into preallocated outputs (codes
+    uint8 [n, k/2], scales uint8 [n, k/16], gscale float32 [1], flag int32 [1]
+    or None); its result is (codes, scales, gscale, flag)."""
+    w = _bits16(w, "w")
+    n, k = w.shape
+    dev = w.device
+    _need(codes, "codes", torch.uint8, (n, k // 2), dev)
+    _need(scales, "scales", torch.uint8, (n, k // 16), dev)
+    _need(gscale, "gscale", torch.float32, (1,), dev)
+    _need(flag, "flag", torch.int32, (1,), dev)
+    args = (_ptr(w), n, k, _ptr(codes), _ptr(scales), _ptr(gscale), _ptr(flag), _stream(dev))
+    return BoundCall("qerl_quantize_nvfp4", args, (w, codes, scales, gscale, flag),
+                     (codes, scales, gscale, flag))
 
 
 def qerl_aqn_sigma(sigma_start, sigma_end, num_stages, stage):
@@ -91,6 +147,16 @@ def qerl_aqn_sample(seed, stream_id, call_id, sigma, d, device="cuda", out=None,
     hs = _stream(z.device) if stream is None else ctypes.c_void_p(stream.cuda_stream)
     _check(lib.qerl_aqn_sample(seed, stream_id, call_id, sigma, d, _ptr(z), hs),
            "qerl_aqn_sample")
+    return z
+
+
+def qerl_aqn_sample_batch(seed, stream_id, call_id0, call_stride, count, sigma, d,
+                          device="cuda", out=None):
+    """z [count, d]: row i is qerl_aqn_sample(seed, stream_id,
+    call_id0 + i * call_stride, sigma, d)."""
+    z = out if out is not None else torch.empty((count, d), dtype=torch.float32, device=device)
+    _check(lib.qerl_aqn_sample_batch(seed, stream_id, call_id0, call_stride, count, sigma, d,
+                                     _ptr(z), _stream(z.device)), "qerl_aqn_sample_batch")
     return z
 
 
@@ -130,9 +196,12 @@ def workspace(m, n, k, r, device="cuda"):
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
-def _linear(fn_name, x, codes, scales, gscale, lora_a, lora_b, lora_scale, z, ws, y,
-            gate_up=False):
+def _linear_args(fn_name, x, codes, scales, gscale, lora_a, lora_b, lora_scale, z, ws, y,
+                 gate_up=False):
+    """Checked C arguments of a whole linear call (and its output y)."""
     x = _bits16(x, "x")
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [m, k]")
     m, k = x.shape
     if gate_up:
         if k % 2:
@@ -142,15 +211,55 @@ def _linear(fn_name, x, codes, scales, gscale, lora_a, lora_b, lora_scale, z, ws
     r = 0 if lora_a is None else int(lora_a.shape[0])
     la = None if lora_a is None else _bits16(lora_a, "lora_a")
     lb = None if lora_b is None else _bits16(lora_b, "lora_b")
-    if ws is None:
-        ws = workspace(m, n, k, r, x.device)
+    if (la is None) != (lb is None):
+        raise ValueError("lora_a and lora_b go together")
     if y is None:
         y = torch.empty((m, n), dtype=torch.bfloat16, device=x.device)
-    fn = getattr(lib, fn_name)
-    _check(fn(_ptr(x), m, _ptr(codes), _ptr(scales), _ptr(gscale), n, k, _ptr(la), _ptr(lb), r,
-              float(lora_scale), _ptr(z), _ptr(y), _ptr(ws), ws.numel(), _stream(x.device)),
-           fn_name)
+    _check_linear_args(m, n, k, r, x.device, codes, scales, gscale, la, lb, z, y)
+    if ws is None:
+        ws = workspace(m, n, k, r, x.device)
+    _need(ws, "workspace", torch.uint8, (ws.numel(),), x.device)
+    args = (_ptr(x), m, _ptr(codes), _ptr(scales), _ptr(gscale), n, k, _ptr(la), _ptr(lb), r,
+            float(lora_scale), _ptr(z), _ptr(y), _ptr(ws), ws.numel(), _stream(x.device))
+    # the tensors stay referenced as long as the arguments are
+    return args, y, (x, codes, scales, gscale, la, lb, z, ws)
+
+
+def _linear(fn_name, x, codes, scales, gscale, lora_a, lora_b, lora_scale, z, ws, y,
+            gate_up=False):
+    args, y, _ = _linear_args(fn_name, x, codes, scales, gscale, lora_a, lora_b, lora_scale, z,
+                              ws, y, gate_up)
+    _check(getattr(lib, fn_name)(*args), fn_name)
     return y
+
+
+class BoundCall:
+    """One library call whose arguments were checked and marshalled once;
+    each call of the object enqueues it again (on the stream that was
+    current when it was bound).  It keeps its tensors alive."""
+
+    def __init__(self, fn_name, args, keep, out):
+        self.fn_name = fn_name
+        self.fn = getattr(lib, fn_name)
+        self.args = args
+        self.keep = keep
+        self.out = out
+
+    def __call__(self):
+        status = self.fn(*self.args)
+        if status != QERL_OK:
+            raise QerlError(status, self.fn_name)
+        return self.out
+
+
+def bind_linear(x, codes, scales, gscale, lora_a=None, lora_b=None, lora_scale=0.0, z=None,
+                workspace=None, y=None, entry="decode"):
+    """A BoundCall of qerl_linear_<entry> (entry: decode, prefill, decode_swiglu
+    or decode_mxfp4) with these arguments; its result is y."""
+    fn_name = "qerl_linear_" + entry
+    args, y, keep = _linear_args(fn_name, x, codes, scales, gscale, lora_a, lora_b, lora_scale,
+                                 z, workspace, y, gate_up=(entry == "decode_swiglu"))
+    return BoundCall(fn_name, args, keep, y)
 
 
 def qerl_linear_decode(x, codes, scales, gscale, lora_a=None, lora_b=None, lora_scale=0.0,
@@ -180,6 +289,9 @@ def qerl_linear_prepare(x, n, lora_a, lora_scale, z, workspace):
     m, k = x.shape
     r = 0 if lora_a is None else int(lora_a.shape[0])
     la = None if lora_a is None else _bits16(lora_a, "lora_a")
+    _need(la, "lora_a", _BF16, (r, k), x.device)
+    _need(z, "z", torch.float32, (k,), x.device)
+    _need(workspace, "workspace", torch.uint8, (workspace.numel(),), x.device)
     _check(lib.qerl_linear_prepare(_ptr(x), m, n, k, _ptr(la), r, float(lora_scale), _ptr(z),
                                    _ptr(workspace), workspace.numel(), _stream(x.device)),
            "qerl_linear_prepare")
@@ -189,6 +301,8 @@ def _prepared(fn_name, m, codes, scales, gscale, k, lora_b, y, workspace):
     n = codes.shape[0]
     r = 0 if lora_b is None else int(lora_b.shape[1])
     lb = None if lora_b is None else _bits16(lora_b, "lora_b")
+    _check_linear_args(m, n, k, r, codes.device, codes, scales, gscale, None, lb, None, y)
+    _need(workspace, "workspace", torch.uint8, (workspace.numel(),), codes.device)
     fn = getattr(lib, fn_name)
     _check(fn(m, _ptr(codes), _ptr(scales), _ptr(gscale), n, k, _ptr(lb), r, _ptr(y),
               _ptr(workspace), workspace.numel(), _stream(y.device)), fn_name)
@@ -219,6 +333,9 @@ def qerl_linear_backward(dy, x, codes, scales, gscale, lora_a=None, lora_b=None,
     r = 0 if lora_a is None else int(lora_a.shape[0])
     la = None if lora_a is None else _bits16(lora_a, "lora_a")
     lb = None if lora_b is None else _bits16(lora_b, "lora_b")
+    if x.shape[0] != m:
+        raise ValueError("dy and x must have the same number of rows")
+    _check_linear_args(m, n, k, r, dy.device, codes, scales, gscale, la, lb, z)
     nbytes = lib.qerl_linear_backward_workspace_bytes(m, n, k, r)
     if nbytes == 0:
         raise ValueError("invalid backward sizes")

@@ -55,7 +55,7 @@ const char* qerl_status_string(int status) {
   }
 }
 
-int qerl_abi_version(void) { return 9; }
+int qerl_abi_version(void) { return 10; }
 
 qerl_status qerl_quantize_nvfp4(const void* w_bf16, int64_t n, int64_t k, void* codes,
                                 void* scales, float* gscale, int32_t* nonfinite_flag,
@@ -152,8 +152,19 @@ qerl_status qerl_aqn_sample(uint64_t seed, uint64_t stream_id, uint64_t call_id,
   if (d < 1) return QERL_ERR_SHAPE;
   if (!(sigma >= 0.0) || !std::isfinite(sigma)) return QERL_ERR_RANGE;
   if (!aligned(z_out, 4)) return QERL_ERR_ALIGN;
-  return from_hip(qerl::launch_aqn_sample(seed, stream_id, call_id, sigma, d, z_out,
+  return from_hip(qerl::launch_aqn_sample(seed, stream_id, call_id, 0, 0, 1, sigma, d, z_out,
                                           static_cast<hipStream_t>(stream)));
+}
+
+qerl_status qerl_aqn_sample_batch(uint64_t seed, uint64_t stream_id, uint64_t call_id0,
+                                  uint64_t call_stride, int64_t count, double sigma, int64_t d,
+                                  float* z_out, void* stream) {
+  if (!z_out) return QERL_ERR_NULL;
+  if (d < 1 || count < 1 || count > 65535) return QERL_ERR_SHAPE;
+  if (!(sigma >= 0.0) || !std::isfinite(sigma)) return QERL_ERR_RANGE;
+  if (!aligned(z_out, 4)) return QERL_ERR_ALIGN;
+  return from_hip(qerl::launch_aqn_sample(seed, stream_id, call_id0, call_stride, 0, count,
+                                          sigma, d, z_out, static_cast<hipStream_t>(stream)));
 }
 
 qerl_status qerl_rmsnorm_noisy(const void* x, int64_t m, int64_t d, const void* w,

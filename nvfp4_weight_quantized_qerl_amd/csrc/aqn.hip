@@ -8,6 +8,12 @@
 // (Box and Muller, 1958), all in fp64; z_j = RN_fp32(sigma * n_j).
 // One thread per counter value; no state, so any slice of z can be
 // recomputed independently.
+//
+// Several vectors in one launch: vector v (blockIdx.y) takes call id
+// call0 + v * call_step and counter word 2 = v * row_step, so the same
+// kernel draws a batch of per-call vectors (row_step 0: each is the vector
+// qerl_aqn_sample gives for its call id) or one vector per token row of a
+// call (call_step 0, row_step 1: row 0 is the shared vector).
 #include "qerl_device.h"
 #include "qerl_internal.h"
 
@@ -42,11 +48,13 @@ __device__ __forceinline__ void box_muller(uint64_t ra, uint64_t rb,
 }
 
 __global__ __launch_bounds__(256) void aqn_sample_kernel(
-    uint64_t seed, uint64_t stream_id, uint64_t call_id, double sigma,
-    int64_t d, float* __restrict__ z) {
+    uint64_t seed, uint64_t stream_id, uint64_t call0, uint64_t call_step,
+    uint64_t row_step, double sigma, int64_t d, float* __restrict__ z) {
   const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (4 * q >= d) return;
-  uint64_t c[4] = {(uint64_t)q, call_id, 0ull, 0ull};
+  const uint64_t v = blockIdx.y;
+  z += (int64_t)v * d;
+  uint64_t c[4] = {(uint64_t)q, call0 + v * call_step, v * row_step, 0ull};
   philox4x64_10(c, seed, stream_id);
   double n[4];
   box_muller(c[0], c[1], &n[0], &n[1]);
@@ -60,13 +68,13 @@ __global__ __launch_bounds__(256) void aqn_sample_kernel(
 
 }  // namespace
 
-hipError_t launch_aqn_sample(uint64_t seed, uint64_t stream_id,
-                             uint64_t call_id, double sigma, int64_t d,
-                             float* z, hipStream_t stream) {
+hipError_t launch_aqn_sample(uint64_t seed, uint64_t stream_id, uint64_t call0,
+                             uint64_t call_step, uint64_t row_step, int64_t count,
+                             double sigma, int64_t d, float* z, hipStream_t stream) {
   const int64_t quads = (d + 3) / 4;
   const int64_t grid = (quads + 255) / 256;
-  hipLaunchKernelGGL(aqn_sample_kernel, dim3((unsigned)grid), dim3(256), 0,
-                     stream, seed, stream_id, call_id, sigma, d, z);
+  hipLaunchKernelGGL(aqn_sample_kernel, dim3((unsigned)grid, (unsigned)count), dim3(256), 0,
+                     stream, seed, stream_id, call0, call_step, row_step, sigma, d, z);
   return hipGetLastError();
 }
 

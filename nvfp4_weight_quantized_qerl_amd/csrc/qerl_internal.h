@@ -25,9 +25,11 @@ hipError_t launch_mxfp4_to_nvfp4(const uint8_t* codes, const uint8_t* s8, int64_
                                  uint8_t* s4, float* gscale, int32_t* flag, hipStream_t stream);
 
 // -------------------------------------------------------------------- noise
-hipError_t launch_aqn_sample(uint64_t seed, uint64_t stream_id,
-                             uint64_t call_id, double sigma, int64_t d,
-                             float* z, hipStream_t stream);
+// `count` vectors of length d, vector v with call id call0 + v * call_step
+// and Philox counter word 2 = v * row_step, stored one after the other.
+hipError_t launch_aqn_sample(uint64_t seed, uint64_t stream_id, uint64_t call0,
+                             uint64_t call_step, uint64_t row_step, int64_t count,
+                             double sigma, int64_t d, float* z, hipStream_t stream);
 
 // ------------------------------------------------------------------ rmsnorm
 // y = bf16((w + z) * x / sqrt(mean(x^2) + delta)) per row of x [m, d].

@@ -168,8 +168,3 @@ def dequantize(packed, scales, S):
                     axis=1)
     return float(np.float32(S)) * (s_b * vals)
 
-
-def dequantize_rows(packed, scales, S, rows):
-    """Eq. 6 for a subset of output rows only (sampled parity checks)."""
-    rows = np.asarray(rows)
-    return dequantize(np.asarray(packed)[rows], np.asarray(scales)[rows], S)

@@ -41,7 +41,7 @@ def test_status_strings():
     for s in range(7):
         assert lib.qerl_status_string(s).decode().startswith("QERL_")
     assert b"unknown" in lib.qerl_status_string(99)
-    assert lib.qerl_abi_version() == 9
+    assert lib.qerl_abi_version() == 10
 
 
 FAKE = ctypes.c_void_p(0x10000)        # aligned, never dereferenced on error
@@ -100,6 +100,13 @@ def test_sample_validation():
     assert f(0, 0, 0, -0.01, 16, FAKE, None) == 4
     assert f(0, 0, 0, float("nan"), 16, FAKE, None) == 4
     assert f(0, 0, 0, 0.01, 16, ctypes.c_void_p(0x10002), None) == 3
+    g = lib.qerl_aqn_sample_batch
+    assert g(0, 0, 0, 1, 4, 0.01, 16, None, None) == 1
+    assert g(0, 0, 0, 1, 0, 0.01, 16, FAKE, None) == 2
+    assert g(0, 0, 0, 1, 65536, 0.01, 16, FAKE, None) == 2
+    assert g(0, 0, 0, 1, 4, 0.01, 0, FAKE, None) == 2
+    assert g(0, 0, 0, 1, 4, float("inf"), 16, FAKE, None) == 4
+    assert g(0, 0, 0, 1, 4, 0.01, 16, ctypes.c_void_p(0x10002), None) == 3
 
 
 def test_rmsnorm_validation():

@@ -58,3 +58,17 @@ def test_noise_statistics_large():
     # tail mass beyond 3 sigma: 0.0027 two-sided
     tail = np.mean(np.abs(z) > 3)
     assert abs(tail - 0.0026998) < 5 * math.sqrt(0.0027 / d)
+
+
+@pytest.mark.parametrize("count,stride,d", [(3, 4, 5120), (64, 4, 27648), (5, 1, 7), (2, 0, 100)])
+def test_batch_rows_equal_single_calls(count, stride, d):
+    # qerl_aqn_sample_batch: row i is the vector of call id c0 + i * stride,
+    # bit for bit, and within one fp32 ulp of the oracle's
+    sig, c0 = 0.01, 1000 + stride
+    zb = q.qerl_aqn_sample_batch(11, 2, c0, stride, count, sig, d, device="cuda:0")
+    torch.cuda.synchronize()
+    zb = host(zb)
+    assert zb.shape == (count, d)
+    for i in sorted({0, count // 2, count - 1}):
+        assert np.array_equal(zb[i], gpu_z(11, 2, c0 + i * stride, sig, d))
+        assert ulp_diff(zb[i], aqn.sample(11, 2, c0 + i * stride, sig, d)).max() <= 1

@@ -24,9 +24,10 @@ TOL = 2e-2
 
 
 class GpuLayer:
-    """Device copies of a layer's inputs, quantized on the GPU."""
+    """Device copies of a layer's inputs, quantized on the GPU.  The noise
+    has the layer's stage sigma unless `sigma` is given."""
 
-    def __init__(self, L, num_stages=10):
+    def __init__(self, L, num_stages=10, sigma=None):
         self.L = L
         self.x = dev16(L.x)
         wdev = dev16(L.w)
@@ -35,9 +36,10 @@ class GpuLayer:
         self.a = None if L.a is None else dev16(L.a)
         self.b = None if L.b is None else dev16(L.b)
         self.z = None
-        if L.stage > 0:
-            sig = q.qerl_aqn_sigma(1e-2, 5e-4, num_stages, L.stage)
-            self.z = q.qerl_aqn_sample(L.seed, L.stream_id, L.call_id, sig, L.x.shape[1],
+        if sigma is None and L.stage > 0:
+            sigma = q.qerl_aqn_sigma(1e-2, 5e-4, num_stages, L.stage)
+        if sigma:
+            self.z = q.qerl_aqn_sample(L.seed, L.stream_id, L.call_id, sigma, L.x.shape[1],
                                        device="cuda:0")
 
     def run(self, entry="decode", **kw):
@@ -48,12 +50,18 @@ class GpuLayer:
         return formats.bf16_bits_to_f64(host(y))
 
 
-def check(L, cols=None, entries=("decode", "prefill")):
-    g = GpuLayer(L)
-    z, _ = oracle_noise(L)
+def check(L, cols=None, entries=("decode", "prefill"), sigma=None):
+    g = GpuLayer(L, sigma=sigma)
+    if sigma is None:
+        z, _ = oracle_noise(L)
+    else:
+        z = aqn.sample(L.seed, L.stream_id, L.call_id, sigma, L.x.shape[1])
     n = L.w.shape[0]
     cols = np.arange(n) if cols is None else cols
     ref = oracle_columns(L, cols, z)
+    if sigma is not None and sigma >= 0.1:
+        # The bar must see the noise: the same layer without it is far off.
+        assert linear.max_rel_error(oracle_columns(L, cols, None), ref) > 10 * TOL
     errs = {}
     for e in entries:
         y = g.run(e)
@@ -61,6 +69,8 @@ def check(L, cols=None, entries=("decode", "prefill")):
         err = linear.max_rel_error(y[:, cols], ref)
         errs[e] = err
         assert err <= TOL, (e, err)
+    print(f"linear m={L.x.shape[0]} n={n} k={L.x.shape[1]} " +
+          " ".join(f"{e}={v:.3g}" for e, v in errs.items()), flush=True)
     return errs
 
 
@@ -168,3 +178,46 @@ def test_decode_32b_layer_shapes(idx):
     s = cfg.layers[idx]
     L = make_layer(cfg.m, s.n, s.k, cfg.r, seed=31 + idx, stage=cfg.stage, call_id=idx)
     check(L, cols=_sample_cols(s.n, 30 + idx, 96), entries=("decode",))
+
+
+# Noise large enough to dominate the output (sigma = 0.25: the noise term is
+# about a quarter of y), so that a dropped, sign-flipped or shifted noise
+# channel fails the 2e-2 bar by far on every kernel path.
+@pytest.mark.parametrize("m,n,k,r,entry", [
+    (64, 1024, 3584, 32, "decode"),     # LDS-staged, unsplit
+    (64, 96, 8192, 32, "decode"),       # LDS-staged, split K + finish
+    (17, 200, 1040, 24, "decode"),      # general kernel (k % 256 != 0), split K
+    (128, 640, 5120, 64, "decode"),     # 128 tokens
+    (96, 200, 4096, 40, "decode"),      # 96 tokens, ragged rank
+    (300, 520, 1024, 32, "prefill"),    # prefill GEMM, ragged M tile
+])
+def test_noise_dominant(m, n, k, r, entry):
+    L = make_layer(m, n, k, r, seed=5 * m + k, call_id=7)
+    check(L, entries=(entry,), sigma=0.25)
+
+
+def test_noise_dominant_prefill_7b_down_full_size():
+    cfg = CONFIGS["prefill_7b"]
+    s = cfg.layers[1]
+    L = make_layer(cfg.m, s.n, s.k, cfg.r, seed=12, call_id=1)
+    check(L, cols=_sample_cols(s.n, 44, 48), entries=("prefill",), sigma=0.25)
+
+
+@pytest.mark.parametrize("idx", [1, 2])
+def test_decode_32b_layer_shapes_o_and_gate_up(idx):
+    # the o projection (5120 x 5120) and the fused gate/up (55296 x 5120) of
+    # the 32B sweep at its 128 tokens and rank 64
+    cfg = CONFIGS["decode_32b_sweep"]
+    s = cfg.layers[idx]
+    L = make_layer(cfg.m, s.n, s.k, cfg.r, seed=31 + idx, stage=cfg.stage, call_id=idx)
+    check(L, cols=_sample_cols(s.n, 30 + idx, 96), entries=("decode",))
+
+
+@pytest.mark.parametrize("idx", [3, 4, 6])
+def test_prefill_14b_m16384_sampled(idx):
+    # one layer of the 14B model at 16384 prefill tokens: o, gate and down
+    # (up has gate's shape), rank 32, stage 1
+    cfg = CONFIGS["quantize_prefill_14b"]
+    s = cfg.layers[idx]
+    L = make_layer(cfg.m, s.n, s.k, cfg.r, seed=51 + idx, stage=cfg.stage, call_id=idx)
+    check(L, cols=_sample_cols(s.n, 50 + idx, 32), entries=("prefill",))
