@@ -131,6 +131,24 @@ def event_times(fn, iters, stream, warmup=3):
     return [ev[i].elapsed_time(ev[i + 1]) for i in range(iters)]
 
 
+def batch_times(fn, stream, batches=10, per_batch=20, warmup=5):
+    """Average time (ms) per call of fn(i) in each of `batches` batches of
+    `per_batch` back-to-back calls, from HIP events around each batch on
+    `stream` (an event between every two calls would add its own time to
+    short kernels)."""
+    import torch
+    for i in range(warmup):
+        fn(i)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(batches + 1)]
+    ev[0].record(stream)
+    for b in range(batches):
+        for j in range(per_batch):
+            fn(b * per_batch + j)
+        ev[b + 1].record(stream)
+    ev[-1].synchronize()
+    return [ev[b].elapsed_time(ev[b + 1]) / per_batch for b in range(batches)]
+
+
 def gpu_clock():
     """Current shader clock (MHz) as rocm-smi reports it, or None."""
     try:
@@ -198,7 +216,8 @@ def dev_normal(shape, std, gen, dev):
 # ------------------------------------------------- headline: the 32B sweep
 class Sweep32:
     """The Qwen2.5-32B decode sweep (64 layers x 4 projections, M=128, r=64),
-    generated and quantized on the device (seeded), with every call bound."""
+    generated and quantized on the device (seeded), held in the tiled layout
+    of the 128-token kernel, with every call bound."""
 
     def __init__(self, q, cfg, dev, keep_host_layer0=False):
         import torch
@@ -214,7 +233,7 @@ class Sweep32:
                 self.x[s.k] = dev_normal((M, s.k), 1.0, gen, dev)
         self.z = [torch.empty((cfg.n_layers, s.k), dtype=torch.float32, device=dev)
                   for s in self.shapes]
-        self.ws = [q.workspace(M, s.n, s.k, R, dev) for s in self.shapes]
+        self.ws = [q.tiled_workspace(M, s.n, s.k, R, dev) for s in self.shapes]
         self.y = [torch.empty((M, s.n), dtype=torch.bfloat16, device=dev) for s in self.shapes]
         self.layers = []                             # [layer][proj] dict
         self.host_w0 = []
@@ -228,16 +247,28 @@ class Sweep32:
                 if li == 0 and keep_host_layer0:
                     self.host_w0.append(w[:512].view(torch.int16).cpu().numpy().view("uint16"))
                 del w
+                # held in the tiled layout of the 128-token kernel (re-laid once)
+                tiles = q.qerl_nvfp4_tile128(codes, scales)
+                if li == 0 and p == 2:
+                    self.std_gate_up = (codes, scales)   # one standard copy, for comparison
+                del codes, scales
                 a = dev_normal((R, s.k), 0.02, gen, dev)
                 b = dev_normal((s.n, R), 0.01, gen, dev)
-                row.append(dict(codes=codes, scales=scales, S=S, a=a, b=b))
+                row.append(dict(tiles=tiles, S=S, a=a, b=b))
             self.layers.append(row)
         torch.cuda.synchronize()
         assert all(int(f.item()) == 0 for f in flags)
-        self.calls = [[q.bind_linear(self.x[s.k], L["codes"], L["scales"], L["S"], L["a"], L["b"],
-                                     cfg.lora_scale, self.z[p][li], self.ws[p], self.y[p])
+        self.calls = [[q.bind_linear_tiled(self.x[s.k], L["tiles"], L["S"], s.n, L["a"], L["b"],
+                                           cfg.lora_scale, self.z[p][li], self.ws[p], self.y[p])
                        for p, (s, L) in enumerate(zip(self.shapes, row))]
                       for li, row in enumerate(self.layers)]
+        s = self.shapes[2]
+        self.gate_up_prepared = [q.bind_linear_tiled_prepared(M, row[2]["tiles"], row[2]["S"], s.n,
+                                                              s.k, row[2]["b"], self.y[2],
+                                                              self.ws[2]) for row in self.layers]
+        self.gate_up_std = q.bind_linear_prepared(M, *self.std_gate_up, self.layers[0][2]["S"],
+                                                  s.k, self.layers[0][2]["b"], self.y[2],
+                                                  q.workspace(M, s.n, s.k, R, dev))
         self.step_bytes = cfg.n_layers * sum(linear_bytes(M, s.n, s.k, R) for s in self.shapes)
         self.step_flops = cfg.n_layers * sum(linear_flops(M, s.n, s.k, R) for s in self.shapes)
         self.weight_bytes = cfg.n_layers * sum(0.5625 * s.n * s.k for s in self.shapes)
@@ -252,15 +283,14 @@ class Sweep32:
 
     def gate_up_contraction(self, li):
         """The gate/up contraction of layer li from the prepared workspace."""
-        s, L = self.shapes[2], self.layers[li][2]
-        self.q.qerl_linear_decode_prepared(self.cfg.m, L["codes"], L["scales"], L["S"], s.k,
-                                           L["b"], self.y[2], self.ws[2])
+        self.gate_up_prepared[li]()
 
     def prepare_gate_up(self):
         s, L = self.shapes[2], self.layers[0][2]
         self.q.qerl_aqn_sample(4000, 0, 2, self.sigma, s.k, out=self.z[2][0])
-        self.q.qerl_linear_prepare(self.x[s.k], s.n, L["a"], self.cfg.lora_scale, self.z[2][0],
-                                   self.ws[2])
+        for ws in (self.ws[2], self.gate_up_std.keep[-1]):
+            self.q.qerl_linear_prepare(self.x[s.k], s.n, L["a"], self.cfg.lora_scale,
+                                       self.z[2][0], ws)
 
 
 def run_sweep(q, args, dev, stream):
@@ -291,23 +321,29 @@ def run_sweep(q, args, dev, stream):
     # tokens, r = 64), rotating over the 64 layers' weights
     sw.prepare_gate_up()
     s = cfg.layers[2]
-    kt = event_times(lambda i: sw.gate_up_contraction(i % cfg.n_layers),
-                     max(100, args.steps), stream, warmup=5)
+    kt = batch_times(lambda i: sw.gate_up_contraction(i % cfg.n_layers), stream,
+                     batches=max(10, args.steps // 10), per_batch=16)
     ks = stats_ms(kt)
     avg_s = ks["mean_ms"] / 1e3
     kflops = main_kernel_flops(cfg.m, s.n, s.k, cfg.r)
     kbytes = main_kernel_bytes(cfg.m, s.n, s.k, cfg.r)
+    # the same contraction on the standard (row-major) layout of one layer
+    std = stats_ms(batch_times(lambda i: sw.gate_up_std(), stream, batches=5, per_batch=10))
     digest = source_digest(*DECODE_SOURCES)
     roofline = {"bound": "mfma", "achieved": round(kflops / avg_s / 1e12, 1),
                 "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(kflops / avg_s / 1e12 / BF16_PEAK_TFLOPS, 4),
                 "traffic": measured_traffic("decode_gate_up_32b_m128", digest),
-                "kernel": "gate/up contraction of the 32B sweep (55296x5120, M=128, r=64): "
-                          "qerl_linear_decode_prepared",
+                "kernel": "decode_m128 (tiled weight): gate/up contraction of the 32B sweep "
+                          "(55296x5120, M=128, r=64), qerl_linear_decode_tiled_prepared",
+                "standard_layout_median_us": round(std["median_ms"] * 1e3, 2),
                 "avg_launch_us": round(avg_s * 1e6, 2),
                 "median_launch_us": round(ks["median_ms"] * 1e3, 2),
                 "p10_launch_us": round(ks["p10_ms"] * 1e3, 2),
                 "p90_launch_us": round(ks["p90_ms"] * 1e3, 2),
+                "timing": "average per launch over batches of 16 back-to-back launches "
+                          "(rotating the 64 layers' weights), HIP events around each batch; "
+                          "median / p10 / p90 over the batches",
                 "flops_per_launch": kflops, "bytes_per_launch": kbytes,
                 "GB_per_s": round(kbytes / avg_s / 1e9, 1),
                 "hbm_frac": round(kbytes / avg_s / 1e9 / HBM_PEAK_GBS, 4),
@@ -472,9 +508,9 @@ def run_decode7b(q, args, dev, stream, to_dev):
     # the gate/up contraction kernel alone
     ly = layers[0]
     q.qerl_linear_prepare(ly["x"], ly["n"], ly["a"], cfg.lora_scale, zring[0][0], ly["ws"])
-    kt = event_times(lambda i: q.qerl_linear_decode_prepared(M, *ly["rot"][i % copies], ly["S"],
-                                                             ly["k"], ly["b"], ly["y"], ly["ws"]),
-                     steps, stream, warmup=5)
+    kcalls = [q.bind_linear_prepared(M, c, s_, ly["S"], ly["k"], ly["b"], ly["y"], ly["ws"])
+              for c, s_ in ly["rot"]]
+    kt = batch_times(lambda i: kcalls[i % copies](), stream, batches=10, per_batch=12)
     ks = stats_ms(kt)
     kbytes = main_kernel_bytes(M, ly["n"], ly["k"], R)
     avg_s = ks["mean_ms"] / 1e3
@@ -506,16 +542,18 @@ def run_decode7b(q, args, dev, stream, to_dev):
     mx = {"workload": "gate/up 37888x3584 MXFP4 weight in the NVFP4 layout, M=64, r=32",
           "range_flag": int(mflag.item())}
     mx_t = {"general": [], "pow2": []}
+    mcalls = {e: [q.bind_linear_prepared(M, c, s_, mg, gl["k"], gl["b"], gl["y"], gl["ws"],
+                                         entry=e) for c, s_ in mrot]
+              for e in ("decode", "decode_mxfp4")}
     for _ in range(3):
-        for name, fn in (("general", q.qerl_linear_decode_prepared),
-                         ("pow2", q.qerl_linear_decode_prepared_mxfp4)):
-            mx_t[name] += event_times(lambda i: fn(M, *mrot[i % copies], mg, gl["k"], gl["b"],
-                                                   gl["y"], gl["ws"]), 40, stream, warmup=5)
+        for name, e in (("general", "decode"), ("pow2", "decode_mxfp4")):
+            mx_t[name] += batch_times(lambda i: mcalls[e][i % copies](), stream, batches=4,
+                                      per_batch=12)
     for name, v in mx_t.items():
         mx[name + "_us"] = round(stats_ms(v)["median_ms"] * 1e3, 2)
     mx["pow2_GB_per_s"] = round(kbytes / (mx["pow2_us"] * 1e-6) / 1e9, 1)
     out["mxfp4_decode"] = mx
-    del mrot, layers, calls
+    del mrot, mcalls, kcalls, layers, calls
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     return out
@@ -892,7 +930,8 @@ def main():
                                   "{qkv 7168x5120, o 5120x5120, gate/up 55296x5120, down "
                                   "5120x27648} NVFP4 (17.55 GB streamed per step), M=128 (8 "
                                   "prompts x 16 samples), LoRA r=64 on every projection, AQN "
-                                  "stage 1/10 with one noise vector per projection and layer",
+                                  "stage 1/10 with one noise vector per projection and layer; "
+                                  "weights held in the tiled NVFP4 layout",
                       "global_batch": 128, "parallelism": "none (1 GPU)"}}
     cpu = None
     if "sweep" in parts:

@@ -335,6 +335,10 @@ QERL_API qerl_status qerl_linear_prefill(const void* x, int64_t m, const void* c
  * t = bf16(s x_t A^T) [§3.4, Eq. 2].  Arguments as above; n is needed to
  * size the workspace.
  *
+ * Its workspace may be one sized for any linear entry point with the same
+ * (m, n, k, r) (qerl_linear_workspace_bytes or
+ * qerl_linear_tiled_workspace_bytes).
+ *
  * qerl_linear_decode_prepared / qerl_linear_prefill_prepared run the main
  * contraction y = bf16(S acc + t B^T) from a workspace that
  * qerl_linear_prepare filled with the same (m, n, k, r); x, z and lora_a
@@ -378,6 +382,58 @@ QERL_API qerl_status qerl_linear_decode_prepared_mxfp4(
     int64_t m, const void* codes, const void* scales, const float* gscale, int64_t n, int64_t k,
     const void* lora_b, int32_t r, void* y, void* workspace, size_t workspace_bytes,
     void* stream);
+
+/*
+ * Tiled weight layout for the 128-token decode kernel.  A rollout engine
+ * quantizes the model once and holds it [QeRL summary, §3.3 "Roadmap";
+ * §3.2], so the stored NVFP4 weight may be re-laid once at load for the
+ * kernel that reads it every token.  The tiled weight holds the same codes
+ * and scales (same S) grouped in tiles of 32 rows x 128 channels
+ * (2304 bytes: 2048 of codes, then 256 of block scales), tile (st, b) of
+ * rows 32 st .. 32 st + 31 and channels 128 b .. 128 b + 127 at byte
+ * (st * (k / 128) + b) * 2304.  Inside a tile, the 16 bytes at
+ * ((2 kh + h) * 32 + c) * 16 are the codes of row 32 st + c, channels
+ * 128 b + 64 kh + 32 h + 0..31 (two per byte, the even channel in the low
+ * nibble), and the 2 bytes at 2048 + ((2 kh + h) * 32 + c) * 2 their two
+ * block scales.  Rows past n are zero.  With this order one wave of the
+ * kernel loads 1 KB of contiguous codes and 128 B of contiguous scales per
+ * 32 rows and 128 channels, instead of 32 separate pieces of each.
+ *
+ * qerl_nvfp4_tile128_bytes -- size of the tiled weight: ceil(n/32) * (k/128)
+ *   * 2304 bytes; 0 if n < 1 or k is not a positive multiple of 128.
+ * qerl_nvfp4_tile128 -- re-lays (codes [n, k/2], scales [n, k/16]) as above.
+ *   codes, tiled   device, 16-byte aligned; k % 128 == 0; tiled holds
+ *                  qerl_nvfp4_tile128_bytes(n, k) bytes and must not overlap
+ *                  codes or scales
+ * qerl_linear_tiled_workspace_bytes -- workspace of the tiled entry points
+ *   (0 if the sizes are invalid).
+ * qerl_linear_decode_tiled / qerl_linear_decode_tiled_prepared -- the same
+ *   operations and arguments as qerl_linear_decode / _prepared with the
+ *   tiled weight in place of (codes, scales); k % 128 == 0.  Every chunk of
+ *   up to 128 tokens runs the single-pass 128-token kernel, which gives
+ *   results bit-identical to qerl_linear_decode for chunks of 65 to 128
+ *   tokens.  The prepared half reads a workspace filled by
+ *   qerl_linear_prepare with the same (m, n, k, r).
+ */
+QERL_API size_t qerl_nvfp4_tile128_bytes(int64_t n, int64_t k);
+
+QERL_API qerl_status qerl_nvfp4_tile128(const void* codes, const void* scales, int64_t n,
+                                        int64_t k, void* tiled, void* stream);
+
+QERL_API size_t qerl_linear_tiled_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t r);
+
+QERL_API qerl_status qerl_linear_decode_tiled(const void* x, int64_t m, const void* tiled,
+                                              const float* gscale, int64_t n, int64_t k,
+                                              const void* lora_a, const void* lora_b, int32_t r,
+                                              float lora_scale, const float* z, void* y,
+                                              void* workspace, size_t workspace_bytes,
+                                              void* stream);
+
+QERL_API qerl_status qerl_linear_decode_tiled_prepared(int64_t m, const void* tiled,
+                                                       const float* gscale, int64_t n, int64_t k,
+                                                       const void* lora_b, int32_t r, void* y,
+                                                       void* workspace, size_t workspace_bytes,
+                                                       void* stream);
 
 /*
  * qerl_linear_backward -- gradients of the layer through the frozen NVFP4

@@ -75,7 +75,7 @@ _BF16 = (torch.bfloat16, torch.int16, torch.uint16)
 
 def _check_linear_args(m, n, k, r, dev, codes, scales, gscale, lora_a=None, lora_b=None, z=None,
                        y=None):
-    _need(codes, "codes", torch.uint8, (n, k // 2), dev)
+    _need(codes, "codes", torch.uint8, (n, k // 2), dev)      # None: checked by the caller
     _need(scales, "scales", torch.uint8, (n, k // 16), dev)
     if not isinstance(gscale, torch.Tensor) or gscale.dtype != torch.float32 or \
             gscale.numel() < 1 or gscale.device != dev:
@@ -309,6 +309,21 @@ def _prepared(fn_name, m, codes, scales, gscale, k, lora_b, y, workspace):
     return y
 
 
+def bind_linear_prepared(m, codes, scales, gscale, k, lora_b, y, workspace, entry="decode"):
+    """A BoundCall of qerl_linear_<entry>_prepared (entry: decode, prefill or
+    decode_mxfp4 for qerl_linear_decode_prepared_mxfp4)."""
+    fn_name = ("qerl_linear_decode_prepared_mxfp4" if entry == "decode_mxfp4"
+               else f"qerl_linear_{entry}_prepared")
+    n = codes.shape[0]
+    r = 0 if lora_b is None else int(lora_b.shape[1])
+    lb = None if lora_b is None else _bits16(lora_b, "lora_b")
+    _check_linear_args(m, n, k, r, codes.device, codes, scales, gscale, None, lb, None, y)
+    _need(workspace, "workspace", torch.uint8, (workspace.numel(),), codes.device)
+    args = (m, _ptr(codes), _ptr(scales), _ptr(gscale), n, k, _ptr(lb), r, _ptr(y),
+            _ptr(workspace), workspace.numel(), _stream(y.device))
+    return BoundCall(fn_name, args, (codes, scales, gscale, lb, y, workspace), y)
+
+
 def qerl_linear_decode_prepared(m, codes, scales, gscale, k, lora_b, y, workspace):
     """Contraction half of qerl_linear_decode from a workspace that
     qerl_linear_prepare filled for the same (m, n, k, r)."""
@@ -391,3 +406,96 @@ def qerl_linear_decode_prepared_mxfp4(m, codes, scales, gscale, k, lora_b, y, wo
     """qerl_linear_decode_prepared for power-of-two block scales."""
     return _prepared("qerl_linear_decode_prepared_mxfp4", m, codes, scales, gscale, k, lora_b, y,
                      workspace)
+
+
+# ------------------------------------------------------- tiled weight layout
+def qerl_nvfp4_tile128_bytes(n, k):
+    return int(lib.qerl_nvfp4_tile128_bytes(n, k))
+
+
+def qerl_nvfp4_tile128(codes, scales):
+    """The NVFP4 weight (codes [n, k/2], scales [n, k/16]) re-laid in the
+    tiled layout of the 128-token decode kernel (uint8 [ceil(n/32), k/128,
+    2304]); n and k are needed again by the tiled linear calls."""
+    n, k = codes.shape[0], codes.shape[1] * 2
+    _need(scales, "scales", torch.uint8, (n, k // 16), codes.device)
+    if not codes.is_contiguous() or codes.dtype != torch.uint8:
+        raise TypeError("codes must be a contiguous uint8 tensor")
+    nbytes = qerl_nvfp4_tile128_bytes(n, k)
+    if nbytes == 0:
+        raise ValueError("the tiled layout needs k to be a multiple of 128")
+    out = torch.empty(((n + 31) // 32, k // 128, 2304), dtype=torch.uint8, device=codes.device)
+    _check(lib.qerl_nvfp4_tile128(_ptr(codes), _ptr(scales), n, k, _ptr(out),
+                                  _stream(codes.device)), "qerl_nvfp4_tile128")
+    return out
+
+
+def qerl_linear_tiled_workspace_bytes(m, n, k, r):
+    return int(lib.qerl_linear_tiled_workspace_bytes(m, n, k, r))
+
+
+def tiled_workspace(m, n, k, r, device="cuda"):
+    nbytes = qerl_linear_tiled_workspace_bytes(m, n, k, r)
+    if nbytes == 0:
+        raise ValueError("invalid tiled linear sizes")
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def _tiled_args(x, tiled, gscale, n, lora_a, lora_b, lora_scale, z, ws, y):
+    x = _bits16(x, "x")
+    m, k = x.shape
+    r = 0 if lora_a is None else int(lora_a.shape[0])
+    la = None if lora_a is None else _bits16(lora_a, "lora_a")
+    lb = None if lora_b is None else _bits16(lora_b, "lora_b")
+    if (la is None) != (lb is None):
+        raise ValueError("lora_a and lora_b go together")
+    _need(tiled, "tiled", torch.uint8, ((n + 31) // 32, k // 128, 2304), x.device)
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.bfloat16, device=x.device)
+    _check_linear_args(m, n, k, r, x.device, None, None, gscale, la, lb, z, y)
+    if ws is None:
+        ws = tiled_workspace(m, n, k, r, x.device)
+    _need(ws, "workspace", torch.uint8, (ws.numel(),), x.device)
+    args = (_ptr(x), m, _ptr(tiled), _ptr(gscale), n, k, _ptr(la), _ptr(lb), r,
+            float(lora_scale), _ptr(z), _ptr(y), _ptr(ws), ws.numel(), _stream(x.device))
+    return args, y, (x, tiled, gscale, la, lb, z, ws)
+
+
+def qerl_linear_decode_tiled(x, tiled, gscale, n, lora_a=None, lora_b=None, lora_scale=0.0,
+                             z=None, workspace=None, y=None):
+    """qerl_linear_decode with the weight in the tiled layout."""
+    args, y, _ = _tiled_args(x, tiled, gscale, n, lora_a, lora_b, lora_scale, z, workspace, y)
+    _check(lib.qerl_linear_decode_tiled(*args), "qerl_linear_decode_tiled")
+    return y
+
+
+def bind_linear_tiled(x, tiled, gscale, n, lora_a=None, lora_b=None, lora_scale=0.0, z=None,
+                      workspace=None, y=None):
+    """A BoundCall of qerl_linear_decode_tiled; its result is y."""
+    args, y, keep = _tiled_args(x, tiled, gscale, n, lora_a, lora_b, lora_scale, z, workspace, y)
+    return BoundCall("qerl_linear_decode_tiled", args, keep, y)
+
+
+def qerl_linear_decode_tiled_prepared(m, tiled, gscale, n, k, lora_b, y, workspace):
+    """Contraction half of qerl_linear_decode_tiled from a prepared workspace."""
+    r = 0 if lora_b is None else int(lora_b.shape[1])
+    lb = None if lora_b is None else _bits16(lora_b, "lora_b")
+    _need(tiled, "tiled", torch.uint8, ((n + 31) // 32, k // 128, 2304), tiled.device)
+    _check_linear_args(m, n, k, r, tiled.device, None, None, gscale, None, lb, None, y)
+    _check(lib.qerl_linear_decode_tiled_prepared(m, _ptr(tiled), _ptr(gscale), n, k, _ptr(lb), r,
+                                                 _ptr(y), _ptr(workspace), workspace.numel(),
+                                                 _stream(tiled.device)),
+           "qerl_linear_decode_tiled_prepared")
+    return y
+
+
+def bind_linear_tiled_prepared(m, tiled, gscale, n, k, lora_b, y, workspace):
+    """A BoundCall of qerl_linear_decode_tiled_prepared."""
+    r = 0 if lora_b is None else int(lora_b.shape[1])
+    lb = None if lora_b is None else _bits16(lora_b, "lora_b")
+    _need(tiled, "tiled", torch.uint8, ((n + 31) // 32, k // 128, 2304), tiled.device)
+    _check_linear_args(m, n, k, r, tiled.device, None, None, gscale, None, lb, None, y)
+    args = (m, _ptr(tiled), _ptr(gscale), n, k, _ptr(lb), r, _ptr(y), _ptr(workspace),
+            workspace.numel(), _stream(tiled.device))
+    return BoundCall("qerl_linear_decode_tiled_prepared", args, (tiled, gscale, lb, y, workspace),
+                     y)

@@ -45,6 +45,14 @@ SIGNATURES = {
                                                 c_vp]),
     "qerl_linear_decode_prepared_mxfp4": (ctypes.c_int, [c_i64, c_vp, c_vp, c_vp, c_i64, c_i64,
                                                          c_vp, c_i32, c_vp, c_vp, c_sz, c_vp]),
+    "qerl_nvfp4_tile128_bytes": (c_sz, [c_i64, c_i64]),
+    "qerl_nvfp4_tile128": (ctypes.c_int, [c_vp, c_vp, c_i64, c_i64, c_vp, c_vp]),
+    "qerl_linear_tiled_workspace_bytes": (c_sz, [c_i64, c_i64, c_i64, c_i32]),
+    "qerl_linear_decode_tiled": (ctypes.c_int, [c_vp, c_i64, c_vp, c_vp, c_i64, c_i64, c_vp,
+                                                c_vp, c_i32, c_f32, c_vp, c_vp, c_vp, c_sz,
+                                                c_vp]),
+    "qerl_linear_decode_tiled_prepared": (ctypes.c_int, [c_i64, c_vp, c_vp, c_i64, c_i64, c_vp,
+                                                         c_i32, c_vp, c_vp, c_sz, c_vp]),
     "qerl_linear_backward_workspace_bytes": (c_sz, [c_i64, c_i64, c_i64, c_i32]),
     "qerl_linear_backward": (ctypes.c_int, [c_vp, c_i64, c_vp, c_vp, c_vp, c_i64, c_i64, c_vp,
                                             c_vp, c_vp, c_i32, c_f32, c_vp, c_vp, c_vp, c_vp,

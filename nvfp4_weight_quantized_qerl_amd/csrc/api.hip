@@ -19,14 +19,15 @@ qerl_status check_linear(const void* x, int64_t m, const void* codes,
                          const void* scales, const float* gscale, int64_t n,
                          int64_t k, int32_t r, float lora_scale, const float* z,
                          const void* y, void* ws, size_t ws_bytes,
-                         qerl::LinearPlan* plan) {
+                         qerl::LinearPlan* plan, bool tiled = false) {
   if (!codes || !scales || !gscale || !y || !ws) return QERL_ERR_NULL;
   if (m < 1 || n < 1 || k < 16 || k % 16) return QERL_ERR_SHAPE;
   if (r < 0 || r > 128 || !std::isfinite(lora_scale)) return QERL_ERR_RANGE;
   if ((x && !aligned(x, 16)) || !aligned(codes, 16) || !aligned(gscale, 4) ||
       !aligned(y, 2) || (z && !aligned(z, 16)) || !aligned(ws, 256))
     return QERL_ERR_ALIGN;
-  if (!qerl::make_linear_plan(m, n, k, r, plan)) return QERL_ERR_SHAPE;
+  if (tiled && k % 128) return QERL_ERR_SHAPE;
+  if (!qerl::make_linear_plan(m, n, k, r, plan, tiled)) return QERL_ERR_SHAPE;
   if (ws_bytes < plan->total) return QERL_ERR_WORKSPACE;
   return QERL_OK;
 }
@@ -230,14 +231,14 @@ static qerl_status linear_full(bool prefill, const void* x, int64_t m, const voi
                                int64_t k, const void* lora_a, const void* lora_b,
                                int32_t r, float lora_scale, const float* z, void* y,
                                void* workspace, size_t workspace_bytes, void* stream,
-                               bool pow2 = false, bool swiglu = false) {
+                               bool pow2 = false, bool swiglu = false, bool tiled = false) {
   if (!x) return QERL_ERR_NULL;
   if (r > 0 && (!lora_a) != (!lora_b)) return QERL_ERR_NULL;
   const int32_t r_eff = (r > 0 && lora_a && lora_b) ? r : 0;
   if (r < 0 || r > 128) return QERL_ERR_RANGE;
   qerl::LinearPlan plan;
   qerl_status s = check_linear(x, m, codes, scales, gscale, n, k, r_eff, lora_scale, z, y,
-                               workspace, workspace_bytes, &plan);
+                               workspace, workspace_bytes, &plan, tiled);
   if (s != QERL_OK) return s;
   s = check_prepare(x, r_eff ? lora_a : nullptr, r_eff);
   if (s != QERL_OK) return s;
@@ -297,7 +298,9 @@ qerl_status qerl_linear_prepare(const void* x, int64_t m, int64_t n, int64_t k,
     return QERL_ERR_ALIGN;
   qerl::LinearPlan plan;
   if (!qerl::make_linear_plan(m, n, k, r, &plan)) return QERL_ERR_SHAPE;
-  if (workspace_bytes < plan.total) return QERL_ERR_WORKSPACE;
+  // It writes x_t, the LoRA-down partials and t, which come first in the
+  // workspace of every linear entry point (standard or tiled).
+  if (workspace_bytes < plan.off_ypart) return QERL_ERR_WORKSPACE;
   return from_hip(qerl::launch_linear_prepare(
       plan, static_cast<const uint16_t*>(x), z, static_cast<const uint16_t*>(lora_a),
       lora_scale, static_cast<char*>(workspace), static_cast<hipStream_t>(stream)));
@@ -307,11 +310,11 @@ static qerl_status linear_prepared(bool prefill, int64_t m, const void* codes,
                                    const void* scales, const float* gscale, int64_t n,
                                    int64_t k, const void* lora_b, int32_t r, void* y,
                                    void* workspace, size_t workspace_bytes, void* stream,
-                                   bool pow2 = false) {
+                                   bool pow2 = false, bool tiled = false) {
   if (r > 0 && !lora_b) return QERL_ERR_NULL;
   qerl::LinearPlan plan;
   qerl_status s = check_linear(nullptr, m, codes, scales, gscale, n, k, r, 1.0f, nullptr, y,
-                               workspace, workspace_bytes, &plan);
+                               workspace, workspace_bytes, &plan, tiled);
   if (s != QERL_OK) return s;
   plan.pow2_scales = pow2;
   const uint8_t* c = static_cast<const uint8_t*>(codes);
@@ -358,6 +361,45 @@ qerl_status qerl_linear_decode_prepared_mxfp4(int64_t m, const void* codes, cons
                                               void* stream) {
   return linear_prepared(false, m, codes, scales, gscale, n, k, lora_b, r, y, workspace,
                          workspace_bytes, stream, true);
+}
+
+size_t qerl_nvfp4_tile128_bytes(int64_t n, int64_t k) {
+  if (n < 1 || k < 128 || k % 128) return 0;
+  return qerl::tile128_bytes(n, k);
+}
+
+qerl_status qerl_nvfp4_tile128(const void* codes, const void* scales, int64_t n, int64_t k,
+                               void* tiled, void* stream) {
+  if (!codes || !scales || !tiled) return QERL_ERR_NULL;
+  if (n < 1 || k < 128 || k % 128) return QERL_ERR_SHAPE;
+  if (((n + 31) / 32) * (k / 128) * 2304 >= ((int64_t)1 << 31)) return QERL_ERR_SHAPE;
+  if (!aligned(codes, 16) || !aligned(tiled, 16)) return QERL_ERR_ALIGN;
+  return from_hip(qerl::tile128(static_cast<const uint8_t*>(codes),
+                                static_cast<const uint8_t*>(scales), n, k,
+                                static_cast<uint8_t*>(tiled), static_cast<hipStream_t>(stream)));
+}
+
+size_t qerl_linear_tiled_workspace_bytes(int64_t m, int64_t n, int64_t k, int32_t r) {
+  qerl::LinearPlan p;
+  if (k % 128 || !qerl::make_linear_plan(m, n, k, r, &p, true)) return 0;
+  return p.total;
+}
+
+qerl_status qerl_linear_decode_tiled(const void* x, int64_t m, const void* tiled,
+                                     const float* gscale, int64_t n, int64_t k,
+                                     const void* lora_a, const void* lora_b, int32_t r,
+                                     float lora_scale, const float* z, void* y,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  return linear_full(false, x, m, tiled, tiled, gscale, n, k, lora_a, lora_b, r, lora_scale, z,
+                     y, workspace, workspace_bytes, stream, false, false, true);
+}
+
+qerl_status qerl_linear_decode_tiled_prepared(int64_t m, const void* tiled, const float* gscale,
+                                              int64_t n, int64_t k, const void* lora_b,
+                                              int32_t r, void* y, void* workspace,
+                                              size_t workspace_bytes, void* stream) {
+  return linear_prepared(false, m, tiled, tiled, gscale, n, k, lora_b, r, y, workspace,
+                         workspace_bytes, stream, false, true);
 }
 
 }  // extern "C"

@@ -1,12 +1,14 @@
-// Decode contraction: launches over the m rows in chunks of at most
-// 32 * dec_mt rows.  Per chunk, one contraction kernel -- the LDS-staged
-// one (decode_lds.h) where its shape conditions hold, else the general one
-// (decode_kernel.h) -- and, when K is split across workgroups, the
-// finishing kernel below.
+// Decode contraction: launches over the m rows in chunks.  Per chunk, one
+// contraction kernel -- the single-pass 128-token one (decode_m128.h) for
+// chunks of three or four 32-row tiles when k % 128 == 0, else the
+// LDS-staged one (decode_lds.h) where its shape conditions hold, else the
+// general one (decode_kernel.h) -- and, when K is split across
+// workgroups, the finishing kernel below.
 #include <algorithm>
 
 #include "decode_kernel.h"
 #include "decode_lds.h"
+#include "decode_m128.h"
 #include "qerl_internal.h"
 
 namespace qerl {
@@ -23,13 +25,13 @@ decode::DecodeKernel pick_decode(int mt, int nt) {
 }
 
 struct FinishArgs {
-  const float* __restrict__ ypart;      // [split, rows, n] fp32 partial sums of acc
+  const float* __restrict__ ypart;      // [split, prows, n] fp32 partial sums of acc
   const float* __restrict__ gscale;
   const uint16_t* __restrict__ t;       // [rows, rpad16] bf16 s x_t A^T of this chunk
   const uint16_t* __restrict__ lora_b;  // [n, r] bf16
   uint16_t* __restrict__ y;             // [m_valid, n] rows of this chunk
   int64_t n;
-  int split, rows, m_valid, r, rpad16, lora_vec;
+  int split, rows, prows, m_valid, r, rpad16, lora_vec;   // rows <= prows finished
 };
 
 constexpr int kFinishBatch = 16;   // splits whose partial sums a thread loads together
@@ -88,7 +90,7 @@ __global__ __launch_bounds__(256) void splitk_finish(FinishArgs a) {
   const int ncol = (int)max<int64_t>(0, min<int64_t>(4, a.n - col));
   const bool vec = ncol == 4 && a.n % 4 == 0;
   const float* src = a.ypart + (int64_t)(32 * u + rr) * a.n + col;
-  const int64_t sstride = (int64_t)a.rows * a.n;
+  const int64_t sstride = (int64_t)a.prows * a.n;
   float4 acc4 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   for (int s0 = 0; s0 < a.split; s0 += kFinishBatch) {
     float4 part[kFinishBatch];
@@ -141,10 +143,12 @@ __global__ __launch_bounds__(256) void splitk_finish(FinishArgs a) {
   }
 }
 
+// rows: token rows to finish (a multiple of 32, at most prows, the rows of
+// one split's partial tile block).
 hipError_t launch_finish(const LinearPlan& p, int split, int rows, int m_valid,
                          const float* ypart, const float* gscale, const uint16_t* t,
                          const uint16_t* lora_b, int r, int lora_vec, uint16_t* y,
-                         hipStream_t stream) {
+                         hipStream_t stream, int prows = 0) {
   FinishArgs f;
   f.ypart = ypart;
   f.gscale = gscale;
@@ -154,6 +158,7 @@ hipError_t launch_finish(const LinearPlan& p, int split, int rows, int m_valid,
   f.n = p.n;
   f.split = split;
   f.rows = rows;
+  f.prows = prows ? prows : rows;
   f.m_valid = m_valid;
   f.r = r;
   f.rpad16 = p.rpad16;
@@ -199,6 +204,39 @@ hipError_t run_decode_lds(const LinearPlan& p, int mt, const uint8_t* codes,
                        stream);
 }
 
+// Single-pass contraction (decode_m128.h) of one chunk of up to 128 rows:
+// xrows rows of x_t (and t) exist, m_valid of them are output rows.
+hipError_t run_decode_m128(const LinearPlan& p, const uint8_t* codes, const uint8_t* scales,
+                           const float* gscale, const uint16_t* t, const uint16_t* lora_b, int r,
+                           int lora_vec, const uint16_t* xt, uint16_t* y, int xrows, int m_valid,
+                           char* ws, hipStream_t stream) {
+  d128::Args a;
+  a.xt = xt;
+  a.codes = codes;
+  a.scales = scales;
+  a.gscale = gscale;
+  a.t = t;
+  a.lora_b = lora_b;
+  a.y = y;
+  a.ypart = reinterpret_cast<float*>(ws + p.off_ypart);
+  a.n = p.n;
+  a.k = p.k;
+  a.nblocks = p.k / d128::kBlock;
+  a.xrows = xrows;
+  a.m_valid = m_valid;
+  a.split = p.m128_split;
+  a.r = r;
+  a.rpad16 = p.rpad16;
+  a.lora_vec = lora_vec;
+  hipLaunchKernelGGL(d128::pick(p.pow2_scales, p.tiled),
+                     dim3((unsigned)p.m128_groups, (unsigned)a.split),
+                     dim3(512), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.split == 1) return e;
+  return launch_finish(p, a.split, (int)((xrows + 31) / 32 * 32), m_valid, a.ypart, gscale, t,
+                       lora_b, r, lora_vec, y, stream, d128::kTokens);
+}
+
 }  // namespace
 
 hipError_t run_decode_chunks(const LinearPlan& p, const uint8_t* codes,
@@ -226,6 +264,16 @@ hipError_t run_decode_chunks(const LinearPlan& p, const uint8_t* codes,
   int64_t m0 = 0;
   while (m0 < p.m) {
     const int64_t tiles_left = (p.mpad - m0) / 32;
+    if (p.m128 && (tiles_left >= 3 || p.tiled)) {
+      const int xrows = (int)std::min<int64_t>(d128::kTokens, p.mpad - m0);
+      const int m_valid = (int)std::min<int64_t>(d128::kTokens, p.m - m0);
+      hipError_t e = run_decode_m128(p, codes, scales, gscale, t + m0 * p.rpad16, lora_b, a.r,
+                                     a.lora_vec, xt + m0 * p.k, y + m0 * p.n, xrows, m_valid, ws,
+                                     stream);
+      if (e != hipSuccess) return e;
+      m0 += d128::kTokens;
+      continue;
+    }
     int mt = p.dec_mt;
     if (tiles_left < mt) mt = tiles_left >= 2 ? 2 : 1;
     a.xt = xt + m0 * p.k;
@@ -251,6 +299,13 @@ hipError_t run_decode_chunks(const LinearPlan& p, const uint8_t* codes,
   }
   return hipSuccess;
 }
+
+hipError_t tile128(const uint8_t* codes, const uint8_t* scales, int64_t n, int64_t k,
+                   uint8_t* out, hipStream_t stream) {
+  return d128::launch_tile128(codes, scales, n, k, out, stream);
+}
+
+size_t tile128_bytes(int64_t n, int64_t k) { return d128::tile128_bytes(n, k); }
 
 hipError_t launch_linear_decode_main(const LinearPlan& p, const uint8_t* codes,
                                      const uint8_t* scales, const float* gscale,

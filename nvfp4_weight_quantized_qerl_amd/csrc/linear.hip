@@ -16,9 +16,7 @@
 //           and written one row per instruction, and tpart = x_t A^T over
 //           the chunk (bf16 MFMA, fp32, operands through LDS);
 //   treduce: t = bf16(sum over chunks of tpart), summed in a fixed order
-//           so the result is deterministic.  When every decode chunk of the
-//           shape splits K, the split-K finishing kernel sums tpart for its
-//           own rows instead, and treduce is not launched.
+//           so the result is deterministic.
 // Without a LoRA branch a single elementwise kernel (xt_kernel) writes x_t.
 #include <algorithm>
 
@@ -96,10 +94,25 @@ void plan_decode(LinearPlan* p, int mt) {
   p->dec_kblk_per_split = per;
 }
 
+// Single-pass 128-token contraction: 256 weight rows per workgroup; K is
+// split across workgroups when the row groups alone leave CUs idle (at
+// least two 128-wide blocks per split).
+void plan_m128(LinearPlan* p) {
+  const int cu = device_cu_count();
+  const int64_t groups = cdiv(p->n, 256);
+  const int64_t nblocks = p->k / 128;
+  int64_t split = 1;
+  if (groups * 4 < cu * 3) split = std::max<int64_t>(1, std::min<int64_t>(cu / groups, nblocks / 2));
+  p->m128 = true;
+  p->m128_groups = (int)groups;
+  p->m128_split = (int)split;
+}
+
 }  // namespace
 
-bool make_linear_plan(int64_t m, int64_t n, int64_t k, int r, LinearPlan* p) {
+bool make_linear_plan(int64_t m, int64_t n, int64_t k, int r, LinearPlan* p, bool tiled) {
   if (m < 1 || n < 1 || k < 16 || k % 16 || r < 0 || r > 128) return false;
+  if (tiled && (k % 128 || ((n + 31) / 32) * (k / 128) * 2304 >= ((int64_t)1 << 31))) return false;
   *p = LinearPlan{};
   p->m = m;
   p->n = n;
@@ -116,9 +129,16 @@ bool make_linear_plan(int64_t m, int64_t n, int64_t k, int r, LinearPlan* p) {
   // With k % 256 == 0 the LDS-staged kernel (up to two tiles) is used even
   // for more rows, one 64-row chunk after the other: it streams the weights
   // fast enough that two passes beat one pass of the general kernel.
-  const int mt_cap = k % 256 == 0 ? 2 : 4;
+  // With k % 128 == 0 and at least three token tiles the single-pass
+  // 128-token kernel takes chunks of 128 rows, and the kernels planned here
+  // only a remainder of one or two tiles.
+  // (Its buffer descriptors take 32-bit byte counts: codes under 2 GB.)
+  const bool m128 = tiled || (k % 128 == 0 && mtiles >= 3 && n * (k / 2) < ((int64_t)1 << 31));
+  const int mt_cap = (m128 || k % 256 == 0) ? 2 : 4;
   const int mt = std::min(mt_cap, mtiles >= 4 ? 4 : (mtiles >= 2 ? 2 : 1));
   plan_decode(p, mt);
+  if (m128) plan_m128(p);
+  p->tiled = tiled;
   p->pf_tile_m = 128;
   p->pf_tile_n = 128;
   size_t off = 0;
@@ -130,9 +150,10 @@ bool make_linear_plan(int64_t m, int64_t n, int64_t k, int r, LinearPlan* p) {
   p->off_xt = take((size_t)p->mpad * k * 2);
   p->off_tpart = take(r ? (size_t)p->kchunks * p->mpad * p->rpad32 * 4 : 0);
   p->off_t = take(r ? (size_t)p->mpad * p->rpad16 * 2 : 0);
-  p->off_ypart = take(p->dec_split > 1
-                          ? (size_t)p->dec_split * 32 * p->dec_mt * n * 4
-                          : 0);
+  size_t ypart = p->dec_split > 1 ? (size_t)p->dec_split * 32 * p->dec_mt * n * 4 : 0;
+  if (p->m128 && p->m128_split > 1)
+    ypart = std::max(ypart, (size_t)p->m128_split * 128 * n * 4);
+  p->off_ypart = take(ypart);
   p->total = off;
   return true;
 }

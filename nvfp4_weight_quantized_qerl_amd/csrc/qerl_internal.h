@@ -57,6 +57,13 @@ struct LinearPlan {
   int dec_groups;      // row groups = ceil(n / dec_rows)
   int dec_split;       // K splits across workgroups
   int64_t dec_kblk_per_split;  // 64-wide K blocks per split
+  // single-pass 128-token contraction (k % 128 == 0): chunks of up to 128
+  // rows with at least three 32-row tiles; the kernels above take the rest
+  bool m128;
+  bool tiled;          // the weight is in the tiled layout: every chunk runs the
+                       // 128-token kernel
+  int m128_groups;     // 256-row groups = ceil(n / 256)
+  int m128_split;      // K splits across workgroups
   // every block scale is a power of two (MXFP4 in the NVFP4 layout): the
   // LDS-staged decode kernel may use its single-instruction dequantization
   bool pow2_scales;
@@ -66,7 +73,8 @@ struct LinearPlan {
   size_t off_xt, off_tpart, off_t, off_ypart, total;
 };
 
-bool make_linear_plan(int64_t m, int64_t n, int64_t k, int r, LinearPlan* p);
+// tiled: the plan of the tiled-layout entry points (k % 128 == 0).
+bool make_linear_plan(int64_t m, int64_t n, int64_t k, int r, LinearPlan* p, bool tiled = false);
 
 // With swiglu_input, x is the fused gate/up output [m, 2k] and the layer
 // input is bf16(SiLU(gate) * up), formed as the rows are loaded.  Without
@@ -106,6 +114,12 @@ hipError_t run_decode_chunks(const LinearPlan& p, const uint8_t* codes,
                              const uint8_t* scales, const float* gscale,
                              const uint16_t* lora_b, uint16_t* y, char* ws,
                              hipStream_t stream);
+
+// Tiled layout of the 128-token decode kernel (decode_m128.h): size and
+// re-layout of a standard NVFP4 weight (k % 128 == 0).
+size_t tile128_bytes(int64_t n, int64_t k);
+hipError_t tile128(const uint8_t* codes, const uint8_t* scales, int64_t n, int64_t k,
+                   uint8_t* out, hipStream_t stream);
 
 hipError_t launch_linear_prefill_main(const LinearPlan& p, const uint8_t* codes,
                                       const uint8_t* scales, const float* gscale,

@@ -211,3 +211,24 @@ def test_linear_validation():
     assert dp(4, FAKE, FAKE, FAKE, 64, 40, FAKE, 8, FAKE, FAKE, W, None) == 2
     assert dp(4, FAKE, FAKE, FAKE, 64, 64, FAKE, 200, FAKE, FAKE, W, None) == 4
     assert dp(4, FAKE, FAKE, FAKE, 64, 64, FAKE, 8, FAKE, FAKE, 16, None) == 5
+
+
+def test_tiled_layout_validation():
+    assert lib.qerl_nvfp4_tile128_bytes(64, 128) == 2 * 1 * 2304
+    assert lib.qerl_nvfp4_tile128_bytes(33, 256) == 2 * 2 * 2304
+    assert lib.qerl_nvfp4_tile128_bytes(64, 192) == 0
+    assert lib.qerl_nvfp4_tile128_bytes(0, 128) == 0
+    f = lib.qerl_nvfp4_tile128
+    assert f(None, FAKE, 64, 128, FAKE, None) == 1
+    assert f(FAKE, FAKE, 64, 96, FAKE, None) == 2
+    assert f(MIS, FAKE, 64, 128, FAKE, None) == 3
+    assert lib.qerl_linear_tiled_workspace_bytes(128, 256, 192, 8) == 0
+    assert lib.qerl_linear_tiled_workspace_bytes(128, 256, 256, 8) > 0
+    d = lib.qerl_linear_decode_tiled
+    ws = lib.qerl_linear_tiled_workspace_bytes(4, 64, 256, 8)
+    # k % 128 != 0 is a shape error; a short workspace is reported
+    assert d(FAKE, 4, FAKE, FAKE, 64, 272, FAKE, FAKE, 8, 2.0, None, FAKE, FAKE, 1 << 30, None) == 2
+    assert d(FAKE, 4, FAKE, FAKE, 64, 256, FAKE, FAKE, 8, 2.0, None, FAKE, FAKE, ws - 1, None) == 5
+    p = lib.qerl_linear_decode_tiled_prepared
+    assert p(4, FAKE, FAKE, 64, 256, FAKE, 8, FAKE, FAKE, ws - 1, None) == 5
+    assert p(4, None, FAKE, 64, 256, FAKE, 8, FAKE, FAKE, ws, None) == 1

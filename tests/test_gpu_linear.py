@@ -221,3 +221,31 @@ def test_prefill_14b_m16384_sampled(idx):
     s = cfg.layers[idx]
     L = make_layer(cfg.m, s.n, s.k, cfg.r, seed=51 + idx, stage=cfg.stage, call_id=idx)
     check(L, cols=_sample_cols(s.n, 50 + idx, 32), entries=("prefill",))
+
+
+# The single-pass 128-token contraction (k % 128 == 0, three or four 32-row
+# token tiles per chunk): 256 weight rows per workgroup, K split across
+# workgroups for narrow layers, four weight register sets (block counts per
+# split that leave a tail of one, two or three blocks).
+@pytest.mark.parametrize("m,n,k,r,stage", [
+    (128, 512, 640, 32, 1),      # 5 blocks over 2 splits: tails of 2 and 3
+    (128, 300, 896, 24, 2),      # 7 blocks, ragged last row group, r % 16 != 0
+    (128, 2048, 1152, 64, 3),    # 9 blocks, 8 row groups
+    (70, 777, 1024, 8, 1),       # 70 tokens: three tiles, ragged output rows
+    (96, 64, 384, 72, 4),        # one subtile of rows, 3 blocks, rank 72 (B read in the loop)
+    (128, 20000, 256, 0, 1),     # no LoRA, unsplit (79 row groups), 2 blocks
+    (128, 7168, 5120, 64, 0),    # the 32B qkv shape, no noise
+    (160, 640, 1280, 32, 2),     # a 128-token chunk and a 32-token remainder
+    (224, 384, 768, 16, 1),      # a 128-token chunk and a 96-token chunk
+])
+def test_decode_128_tokens(m, n, k, r, stage):
+    L = make_layer(m, n, k, r, seed=3 * m + n + k, stage=stage, outlier_frac=1e-3, call_id=2)
+    check(L, entries=("decode",))
+
+
+@pytest.mark.parametrize("m,n,k,r", [(128, 512, 640, 32), (128, 4096, 2560, 64), (96, 300, 1024, 8)])
+def test_decode_128_tokens_deterministic(m, n, k, r):
+    L = make_layer(m, n, k, r, seed=77, stage=1)
+    g = GpuLayer(L)
+    y1, y2 = g.run(), g.run()
+    assert np.array_equal(y1, y2)

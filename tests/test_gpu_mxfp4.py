@@ -65,6 +65,7 @@ def test_range_flag():
 
 
 @pytest.mark.parametrize("m,n,k,r,entry", [(64, 512, 1024, 16, "decode"),
+                                           (128, 512, 1024, 16, "decode"),
                                            (300, 384, 2048, 32, "prefill")])
 def test_mxfp4_layer(m, n, k, r, entry):
     L = make_layer(m, n, k, r, seed=43, outlier_frac=0.001, stage=2)
@@ -84,7 +85,8 @@ def test_mxfp4_layer(m, n, k, r, entry):
     assert err <= 2e-2
 
 
-@pytest.mark.parametrize("m,n,k,r", [(64, 37888 // 8, 3584, 32), (50, 1024, 18944, 32), (3, 160, 512, 8)])
+@pytest.mark.parametrize("m,n,k,r", [(64, 37888 // 8, 3584, 32), (50, 1024, 18944, 32), (3, 160, 512, 8),
+                                     (128, 1000, 5120, 64), (100, 96, 2560, 32)])
 def test_power_of_two_decode_is_bit_identical(m, n, k, r):
     # the scaled-conversion dequantization gives the same bf16 weights, so the
     # whole result must match the general decode call bit for bit
