@@ -436,6 +436,31 @@ QERL_API qerl_status qerl_linear_decode_tiled_prepared(int64_t m, const void* ti
                                                        void* stream);
 
 /*
+ * qerl_linear_decode_noalloc -- for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation): qerl_linear_decode with the same arguments
+ * minus the workspace, which is replaced by a device array inside the
+ * library of qerl_linear_noalloc_scratch_bytes() bytes (64 MiB) per GPU,
+ * held until the process ends.  It allocates and frees nothing.
+ *   - Sizes whose workspace (qerl_linear_workspace_bytes) exceeds the
+ *     array return QERL_ERR_WORKSPACE before anything is enqueued.
+ *   - `stream` must belong to the current device (else QERL_ERR_RANGE);
+ *     the array of the current device is used.
+ *   - Every call on one GPU uses that GPU's single array: calls that
+ *     overlap on one GPU (other streams, other host threads) race and must
+ *     be serialised by the caller.  The array keeps the last call's
+ *     contents; no call relies on them.
+ * Results are bit-identical to qerl_linear_decode.
+ */
+QERL_API size_t qerl_linear_noalloc_scratch_bytes(void);
+
+QERL_API qerl_status qerl_linear_decode_noalloc(const void* x, int64_t m, const void* codes,
+                                                const void* scales, const float* gscale,
+                                                int64_t n, int64_t k, const void* lora_a,
+                                                const void* lora_b, int32_t r, float lora_scale,
+                                                const float* z, void* y, void* stream);
+
+/*
  * qerl_linear_backward -- gradients of the layer through the frozen NVFP4
  * weight.  The rollout's log-probabilities are taken on the same quantized
  * model and only the LoRA factors (and RMSNorm scales) are trained

@@ -269,6 +269,26 @@ def qerl_linear_decode(x, codes, scales, gscale, lora_a=None, lora_b=None, lora_
                    lora_scale, z, workspace, y)
 
 
+def qerl_linear_decode_noalloc(x, codes, scales, gscale, lora_a=None, lora_b=None,
+                               lora_scale=0.0, z=None, y=None):
+    """qerl_linear_decode with the library's own per-GPU scratch (no
+    workspace; calls overlapping on one GPU race)."""
+    x = _bits16(x, "x")
+    m, k = x.shape
+    n = codes.shape[0]
+    r = 0 if lora_a is None else int(lora_a.shape[0])
+    la = None if lora_a is None else _bits16(lora_a, "lora_a")
+    lb = None if lora_b is None else _bits16(lora_b, "lora_b")
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.bfloat16, device=x.device)
+    _check_linear_args(m, n, k, r, x.device, codes, scales, gscale, la, lb, z, y)
+    _check(lib.qerl_linear_decode_noalloc(_ptr(x), m, _ptr(codes), _ptr(scales), _ptr(gscale), n,
+                                          k, _ptr(la), _ptr(lb), r, float(lora_scale), _ptr(z),
+                                          _ptr(y), _stream(x.device)),
+           "qerl_linear_decode_noalloc")
+    return y
+
+
 def qerl_linear_decode_swiglu(gate_up, codes, scales, gscale, lora_a=None, lora_b=None,
                               lora_scale=0.0, z=None, workspace=None, y=None):
     """qerl_linear_decode of x = bf16(SiLU(gate) * up) from the fused gate/up

@@ -53,6 +53,9 @@ SIGNATURES = {
                                                 c_vp]),
     "qerl_linear_decode_tiled_prepared": (ctypes.c_int, [c_i64, c_vp, c_vp, c_i64, c_i64, c_vp,
                                                          c_i32, c_vp, c_vp, c_sz, c_vp]),
+    "qerl_linear_noalloc_scratch_bytes": (c_sz, []),
+    "qerl_linear_decode_noalloc": (ctypes.c_int, [c_vp, c_i64, c_vp, c_vp, c_vp, c_i64, c_i64,
+                                                  c_vp, c_vp, c_i32, c_f32, c_vp, c_vp, c_vp]),
     "qerl_linear_backward_workspace_bytes": (c_sz, [c_i64, c_i64, c_i64, c_i32]),
     "qerl_linear_backward": (ctypes.c_int, [c_vp, c_i64, c_vp, c_vp, c_vp, c_i64, c_i64, c_vp,
                                             c_vp, c_vp, c_i32, c_f32, c_vp, c_vp, c_vp, c_vp,

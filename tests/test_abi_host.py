@@ -33,7 +33,8 @@ def test_every_declared_symbol_is_exported():
     assert sorted(_lib.SIGNATURES) == names
     for name in names:
         if name not in ("qerl_status_string", "qerl_abi_version",
-                        "qerl_linear_workspace_bytes", "qerl_linear_backward_workspace_bytes"):
+                        "qerl_linear_workspace_bytes", "qerl_linear_backward_workspace_bytes",
+                        "qerl_linear_noalloc_scratch_bytes"):
             assert hasattr(q, name), name
 
 
