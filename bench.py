@@ -26,6 +26,9 @@ sub-measurement:
                         ahead on a second stream), its gate/up contraction
                         kernel, the chained feed-forward block and the MXFP4
                         weight;
+  `decode_layer_7b`     a whole 7B decode layer at 64 tokens as a chain of calls
+                        (noisy RMSNorm, q/k/v, attention stub, o, gate/up,
+                        SiLU * up, down), with per-call and per-row noise;
   `prefill_7b`          4096-token prefill of the 7B qkv and down layers, and
                         the backward of the 7B down layer;
   `quantize_prefill_14b` bulk quantization of every linear weight of a
@@ -53,7 +56,7 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 COPY_BYTES = 512 << 20         # calibration copy of the profiling passes
 PROFILE_LAUNCHES = 50          # contractions of a profiling pass
 
-PARTS = ("sweep", "decode7b", "prefill7b", "q14b", "rmsnorm")
+PARTS = ("sweep", "decode7b", "layer7b", "prefill7b", "q14b", "rmsnorm")
 
 
 def parse():
@@ -559,6 +562,109 @@ def run_decode7b(q, args, dev, stream, to_dev):
     return out
 
 
+# ------------------------------------------- 7B chained decode layer (f4 row)
+def run_layer7b(q, args, dev, stream, copies=4):
+    """One whole Qwen2.5-7B decode layer at 64 tokens as a chain of library
+    calls: noisy RMSNorm -> q/k/v [4608, 3584] -> attention over a
+    one-position context (28 q / 4 kv heads of 128) -> o [3584, 3584] ->
+    noisy RMSNorm -> gate/up [37888, 3584] -> SiLU(gate) * up -> down [3584,
+    18944]; LoRA r=32 everywhere, AQN stage 1.  Two noise variants: one
+    vector per call (q/k/v and gate/up groups in the RMSNorm scale, o and
+    down in their input), and one row per token on every linear call.
+    Weights (seeded, on the device) are rotated over `copies` layers (524 MB)
+    so that the Infinity Cache cannot hold them."""
+    import torch
+    M, R, H, I, HQ, HKV, DH = 64, 32, 3584, 18944, 28, 4, 128
+    shapes = [((HQ + 2 * HKV) * DH, H), (H, HQ * DH), (2 * I, H), (H, I)]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7000)
+    layers = []
+    for c in range(copies):
+        row = []
+        for n, k in shapes:
+            w = dev_normal((n, k), 0.02, gen, dev)
+            codes, scales, S, _ = q.qerl_quantize_nvfp4(w)
+            del w
+            row.append(dict(codes=codes, scales=scales, S=S, n=n, k=k,
+                            a=dev_normal((R, k), 0.02, gen, dev),
+                            b=dev_normal((n, R), 0.01, gen, dev)))
+        layers.append(row)
+    x = dev_normal((M, H), 1.0, gen, dev)
+    w1 = (1.0 + 0.05 * torch.randn(H, generator=gen, device=dev)).to(torch.bfloat16)
+    w2 = (1.0 + 0.05 * torch.randn(H, generator=gen, device=dev)).to(torch.bfloat16)
+    sig = 1e-2
+    zv = [q.qerl_aqn_sample(7000, 0, i, sig, k, device=dev) for i, (_, k) in enumerate(shapes)]
+    zr = [q.qerl_aqn_sample_rows(7000, 0, i, sig, M, k, device=dev)
+          for i, (_, k) in enumerate(shapes)]
+    h = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+    att = torch.empty((M, HQ * DH), dtype=torch.bfloat16, device=dev)
+    act = torch.empty((M, I), dtype=torch.bfloat16, device=dev)
+    ys = [torch.empty((M, n), dtype=torch.bfloat16, device=dev) for n, _ in shapes]
+    wss = [q.workspace(M, n, k, R, dev) for n, k in shapes]
+    ins = [h, att, h, act]
+
+    def bound(per_row):
+        calls = []
+        for row in layers:
+            c = []
+            for i, L in enumerate(row):
+                inp = ins[i]
+                entry = "decode_rownoise" if per_row else "decode"
+                z = zr[i] if per_row else (zv[i] if i in (1, 3) else None)
+                if i == 3 and not per_row:
+                    inp, entry = ys[2], "decode_swiglu"
+                c.append(q.bind_linear(inp, L["codes"], L["scales"], L["S"], L["a"], L["b"], 2.0,
+                                       z, wss[i], ys[i], entry=entry))
+            calls.append(c)
+        return calls
+
+    shared, rows = bound(False), bound(True)
+
+    def step_shared(i):
+        c = shared[i % copies]
+        q.qerl_rmsnorm_noisy(x, w1, zv[0], 1e-6, out=h)
+        c[0]()
+        q.qerl_attention_stub(ys[0], HQ, HKV, DH, out=att)
+        c[1]()
+        q.qerl_rmsnorm_noisy(ys[1], w2, zv[2], 1e-6, out=h)
+        c[2]()
+        c[3]()
+
+    def step_rows(i):
+        c = rows[i % copies]
+        q.qerl_rmsnorm_noisy(x, w1, None, 1e-6, out=h)
+        c[0]()
+        q.qerl_attention_stub(ys[0], HQ, HKV, DH, out=att)
+        c[1]()
+        q.qerl_rmsnorm_noisy(ys[1], w2, None, 1e-6, out=h)
+        c[2]()
+        q.qerl_swiglu(ys[2], out=act)
+        c[3]()
+
+    # algorithmic bytes of a layer: the linear calls without their noise
+    # input, the RMSNorms (x in, y out, w), the stub (v heads in, heads out)
+    lin = sum(linear_bytes(M, n, k, R) - 4 * k for n, k in shapes)
+    base = lin + 2 * (4 * M * H + 2 * H) + 2 * M * (HKV + HQ) * DH
+    # per call: z of the two RMSNorms, o and down; down reads gate and up
+    shared_bytes = base + 4 * (H + H + H + I) + 2 * M * I
+    # per row: z rows of the four linear calls; the SwiGLU kernel in between
+    rows_bytes = base + 4 * M * (3 * H + I) + 6 * M * I
+    out = {"workload": "Qwen2.5-7B decode layer at M=64: noisy RMSNorm, q/k/v, attention stub "
+                       "(one-position context), o, noisy RMSNorm, gate/up, SiLU*up, down; "
+                       f"LoRA r=32, AQN stage 1; weights rotated over {copies} layers"}
+    for name, fn, nbytes in (("per_call_noise", step_shared, shared_bytes),
+                             ("per_row_noise", step_rows, rows_bytes)):
+        st = stats_ms(event_times(fn, max(100, args.steps), stream, warmup=args.warmup))
+        out[name] = {"us_per_layer": round(st["median_ms"] * 1e3, 2),
+                     "GB_per_s": round(nbytes / (st["median_ms"] / 1e3) / 1e9, 1),
+                     "frac_hbm": round(nbytes / (st["median_ms"] / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "timing": st}
+    del layers, shared, rows
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
 # ----------------------------------------------- 7B prefill + backward (config 3)
 def run_prefill7b(q, args, dev, stream, to_dev):
     import torch
@@ -948,6 +1054,8 @@ def main():
         torch.cuda.empty_cache()
     if "decode7b" in parts:
         out["decode_7b_mlp"] = run_decode7b(q, args, dev, stream, to_dev)
+    if "layer7b" in parts:
+        out["decode_layer_7b"] = run_layer7b(q, args, dev, stream)
     if "prefill7b" in parts:
         out["prefill_7b"] = run_prefill7b(q, args, dev, stream, to_dev)
     if "q14b" in parts:

@@ -207,6 +207,21 @@ QERL_API qerl_status qerl_aqn_sample_batch(uint64_t seed, uint64_t stream_id,
                                            float* z_out, void* stream);
 
 /*
+ * qerl_aqn_sample_rows -- one noise vector per token row of a call, the
+ * variant in which each rollout of a batch sees its own draw of the noise
+ * [QeRL summary, §3.4 "Noise injection frequency": a different sample per
+ * rollout].  Row i of z_out [m, d] takes Philox counter (j/4, call_id, i, 0)
+ * for element j, so row 0 is bit-identical to qerl_aqn_sample(seed,
+ * stream_id, call_id, sigma, d).
+ *   m      1 .. 65535 rows
+ *   z_out  device out, [m, d] float, 4-byte aligned
+ * Other arguments and errors as qerl_aqn_sample.
+ */
+QERL_API qerl_status qerl_aqn_sample_rows(uint64_t seed, uint64_t stream_id, uint64_t call_id,
+                                          double sigma, int64_t m, int64_t d, float* z_out,
+                                          void* stream);
+
+/*
  * qerl_rmsnorm_noisy -- the noisy RMSNorm that produces a linear layer's
  * input [QeRL summary, §3.4 "Noise Merging", Eq. 10]:
  *     y[i, j] = bf16( (w_j + z_j) * x[i, j] / sqrt(mean_j' x[i, j']^2 + delta) )
@@ -311,6 +326,49 @@ QERL_API qerl_status qerl_linear_decode_swiglu(const void* gate_up, int64_t m, c
                                       float lora_scale, const float* z, void* y,
                                       void* workspace, size_t workspace_bytes,
                                       void* stream);
+
+/*
+ * qerl_linear_decode_rownoise / qerl_linear_prefill_rownoise -- the same
+ * operations and arguments as qerl_linear_decode / qerl_linear_prefill with
+ * one noise row per token: x_t[i, j] = x[i, j] (1 + z_rows[i, j]) (the
+ * per-rollout noise of qerl_aqn_sample_rows).
+ *   z_rows   device, [m, k] float, rows 16-byte aligned (k % 16 == 0);
+ *            required (non-NULL)
+ */
+QERL_API qerl_status qerl_linear_decode_rownoise(const void* x, int64_t m, const void* codes,
+                                                 const void* scales, const float* gscale,
+                                                 int64_t n, int64_t k, const void* lora_a,
+                                                 const void* lora_b, int32_t r,
+                                                 float lora_scale, const float* z_rows, void* y,
+                                                 void* workspace, size_t workspace_bytes,
+                                                 void* stream);
+
+QERL_API qerl_status qerl_linear_prefill_rownoise(const void* x, int64_t m, const void* codes,
+                                                  const void* scales, const float* gscale,
+                                                  int64_t n, int64_t k, const void* lora_a,
+                                                  const void* lora_b, int32_t r,
+                                                  float lora_scale, const float* z_rows, void* y,
+                                                  void* workspace, size_t workspace_bytes,
+                                                  void* stream);
+
+/*
+ * qerl_attention_stub -- the attention step between the fused q/k/v layer
+ * and the output projection of a decode layer (W_q, W_k, W_v, W_o [QeRL
+ * summary, §3.4 "Layer coverage"]), reduced to a context of one position:
+ * each token attends only to its own key and value, the softmax of a single
+ * score is exactly 1, and query head h outputs the value of its key/value
+ * head h / (n_q_heads / n_kv_heads) (grouped-query attention):
+ *     out[i, h d + e] = qkv[i, (n_q_heads + n_kv_heads + h / g) d + e],
+ *     g = n_q_heads / n_kv_heads, d = head_dim
+ * The values are copied bit for bit.
+ *   qkv    device, [m, (n_q_heads + 2 n_kv_heads) head_dim] bf16 (q heads,
+ *          then k heads, then v heads), 16-byte aligned
+ *   n_q_heads % n_kv_heads == 0; head_dim >= 8, head_dim % 8 == 0
+ *   out    device out, [m, n_q_heads head_dim] bf16, 16-byte aligned
+ */
+QERL_API qerl_status qerl_attention_stub(const void* qkv, int64_t m, int32_t n_q_heads,
+                                         int32_t n_kv_heads, int32_t head_dim, void* out,
+                                         void* stream);
 
 /*
  * qerl_linear_prefill -- the same operation and arguments as

@@ -160,6 +160,29 @@ def qerl_aqn_sample_batch(seed, stream_id, call_id0, call_stride, count, sigma, 
     return z
 
 
+def qerl_aqn_sample_rows(seed, stream_id, call_id, sigma, m, d, device="cuda", out=None):
+    """z [m, d], one noise row per token; row 0 is qerl_aqn_sample's vector."""
+    z = out if out is not None else torch.empty((m, d), dtype=torch.float32, device=device)
+    _check(lib.qerl_aqn_sample_rows(seed, stream_id, call_id, sigma, m, d, _ptr(z),
+                                    _stream(z.device)), "qerl_aqn_sample_rows")
+    return z
+
+
+def qerl_attention_stub(qkv, n_q_heads, n_kv_heads, head_dim, out=None):
+    """Attention over a context of one position: each query head outputs the
+    value of its key/value head, out [m, n_q_heads * head_dim]."""
+    qkv = _bits16(qkv, "qkv")
+    m, width = qkv.shape
+    if width != (n_q_heads + 2 * n_kv_heads) * head_dim:
+        raise ValueError("qkv width must be (n_q_heads + 2 n_kv_heads) head_dim")
+    if out is None:
+        out = torch.empty((m, n_q_heads * head_dim), dtype=torch.bfloat16, device=qkv.device)
+    _need(out, "out", _BF16, (m, n_q_heads * head_dim), qkv.device)
+    _check(lib.qerl_attention_stub(_ptr(qkv), m, n_q_heads, n_kv_heads, head_dim, _ptr(out),
+                                   _stream(qkv.device)), "qerl_attention_stub")
+    return out
+
+
 def qerl_rmsnorm_noisy(x, w, z=None, delta=1e-6, out=None):
     """y = bf16((w + z) * x / sqrt(mean(x^2) + delta)) per row of x [m, d]."""
     x = _bits16(x, "x")
@@ -197,7 +220,7 @@ def workspace(m, n, k, r, device="cuda"):
 
 
 def _linear_args(fn_name, x, codes, scales, gscale, lora_a, lora_b, lora_scale, z, ws, y,
-                 gate_up=False):
+                 gate_up=False, z_rows=False):
     """Checked C arguments of a whole linear call (and its output y)."""
     x = _bits16(x, "x")
     if x.dim() != 2:
@@ -215,7 +238,11 @@ def _linear_args(fn_name, x, codes, scales, gscale, lora_a, lora_b, lora_scale, 
         raise ValueError("lora_a and lora_b go together")
     if y is None:
         y = torch.empty((m, n), dtype=torch.bfloat16, device=x.device)
-    _check_linear_args(m, n, k, r, x.device, codes, scales, gscale, la, lb, z, y)
+    if z_rows:
+        _need(z, "z", torch.float32, (m, k), x.device)
+        _check_linear_args(m, n, k, r, x.device, codes, scales, gscale, la, lb, None, y)
+    else:
+        _check_linear_args(m, n, k, r, x.device, codes, scales, gscale, la, lb, z, y)
     if ws is None:
         ws = workspace(m, n, k, r, x.device)
     _need(ws, "workspace", torch.uint8, (ws.numel(),), x.device)
@@ -226,9 +253,9 @@ def _linear_args(fn_name, x, codes, scales, gscale, lora_a, lora_b, lora_scale, 
 
 
 def _linear(fn_name, x, codes, scales, gscale, lora_a, lora_b, lora_scale, z, ws, y,
-            gate_up=False):
+            gate_up=False, z_rows=False):
     args, y, _ = _linear_args(fn_name, x, codes, scales, gscale, lora_a, lora_b, lora_scale, z,
-                              ws, y, gate_up)
+                              ws, y, gate_up, z_rows)
     _check(getattr(lib, fn_name)(*args), fn_name)
     return y
 
@@ -254,11 +281,13 @@ class BoundCall:
 
 def bind_linear(x, codes, scales, gscale, lora_a=None, lora_b=None, lora_scale=0.0, z=None,
                 workspace=None, y=None, entry="decode"):
-    """A BoundCall of qerl_linear_<entry> (entry: decode, prefill, decode_swiglu
-    or decode_mxfp4) with these arguments; its result is y."""
+    """A BoundCall of qerl_linear_<entry> (entry: decode, prefill, decode_swiglu,
+    decode_mxfp4, decode_rownoise or prefill_rownoise) with these arguments;
+    its result is y."""
     fn_name = "qerl_linear_" + entry
     args, y, keep = _linear_args(fn_name, x, codes, scales, gscale, lora_a, lora_b, lora_scale,
-                                 z, workspace, y, gate_up=(entry == "decode_swiglu"))
+                                 z, workspace, y, gate_up=(entry == "decode_swiglu"),
+                                 z_rows=entry.endswith("rownoise"))
     return BoundCall(fn_name, args, keep, y)
 
 
@@ -295,6 +324,20 @@ def qerl_linear_decode_swiglu(gate_up, codes, scales, gscale, lora_a=None, lora_
     output [m, 2k] (gate first), without writing x."""
     return _linear("qerl_linear_decode_swiglu", gate_up, codes, scales, gscale, lora_a, lora_b,
                    lora_scale, z, workspace, y, gate_up=True)
+
+
+def qerl_linear_decode_rownoise(x, codes, scales, gscale, lora_a=None, lora_b=None,
+                                lora_scale=0.0, z_rows=None, workspace=None, y=None):
+    """qerl_linear_decode with one noise row per token (z_rows [m, k])."""
+    return _linear("qerl_linear_decode_rownoise", x, codes, scales, gscale, lora_a, lora_b,
+                   lora_scale, z_rows, workspace, y, z_rows=True)
+
+
+def qerl_linear_prefill_rownoise(x, codes, scales, gscale, lora_a=None, lora_b=None,
+                                 lora_scale=0.0, z_rows=None, workspace=None, y=None):
+    """qerl_linear_prefill with one noise row per token (z_rows [m, k])."""
+    return _linear("qerl_linear_prefill_rownoise", x, codes, scales, gscale, lora_a, lora_b,
+                   lora_scale, z_rows, workspace, y, z_rows=True)
 
 
 def qerl_linear_prefill(x, codes, scales, gscale, lora_a=None, lora_b=None, lora_scale=0.0,

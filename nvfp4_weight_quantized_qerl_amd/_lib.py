@@ -24,6 +24,15 @@ SIGNATURES = {
     "qerl_aqn_sample": (ctypes.c_int, [c_u64, c_u64, c_u64, c_f64, c_i64, c_vp, c_vp]),
     "qerl_aqn_sample_batch": (ctypes.c_int, [c_u64, c_u64, c_u64, c_u64, c_i64, c_f64, c_i64,
                                              c_vp, c_vp]),
+    "qerl_aqn_sample_rows": (ctypes.c_int, [c_u64, c_u64, c_u64, c_f64, c_i64, c_i64, c_vp,
+                                            c_vp]),
+    "qerl_linear_decode_rownoise": (ctypes.c_int, [c_vp, c_i64, c_vp, c_vp, c_vp, c_i64, c_i64,
+                                                   c_vp, c_vp, c_i32, c_f32, c_vp, c_vp, c_vp,
+                                                   c_sz, c_vp]),
+    "qerl_linear_prefill_rownoise": (ctypes.c_int, [c_vp, c_i64, c_vp, c_vp, c_vp, c_i64, c_i64,
+                                                    c_vp, c_vp, c_i32, c_f32, c_vp, c_vp, c_vp,
+                                                    c_sz, c_vp]),
+    "qerl_attention_stub": (ctypes.c_int, [c_vp, c_i64, c_i32, c_i32, c_i32, c_vp, c_vp]),
     "qerl_rmsnorm_noisy": (ctypes.c_int, [c_vp, c_i64, c_i64, c_vp, c_vp, c_f32, c_vp, c_vp]),
     "qerl_swiglu": (ctypes.c_int, [c_vp, c_i64, c_i64, c_vp, c_vp]),
     "qerl_linear_workspace_bytes": (c_sz, [c_i64, c_i64, c_i64, c_i32]),

@@ -231,7 +231,8 @@ static qerl_status linear_full(bool prefill, const void* x, int64_t m, const voi
                                int64_t k, const void* lora_a, const void* lora_b,
                                int32_t r, float lora_scale, const float* z, void* y,
                                void* workspace, size_t workspace_bytes, void* stream,
-                               bool pow2 = false, bool swiglu = false, bool tiled = false) {
+                               bool pow2 = false, bool swiglu = false, bool tiled = false,
+                               bool z_rows = false) {
   if (!x) return QERL_ERR_NULL;
   if (r > 0 && (!lora_a) != (!lora_b)) return QERL_ERR_NULL;
   const int32_t r_eff = (r > 0 && lora_a && lora_b) ? r : 0;
@@ -247,7 +248,7 @@ static qerl_status linear_full(bool prefill, const void* x, int64_t m, const voi
   char* ws = static_cast<char*>(workspace);
   hipError_t e = qerl::launch_linear_prepare(plan, static_cast<const uint16_t*>(x), z,
                                              static_cast<const uint16_t*>(lora_a),
-                                             lora_scale, ws, st, swiglu);
+                                             lora_scale, ws, st, swiglu, true, z_rows);
   if (e != hipSuccess) return QERL_ERR_HIP;
   const uint8_t* c = static_cast<const uint8_t*>(codes);
   const uint8_t* sc = static_cast<const uint8_t*>(scales);
@@ -361,6 +362,51 @@ qerl_status qerl_linear_decode_prepared_mxfp4(int64_t m, const void* codes, cons
                                               void* stream) {
   return linear_prepared(false, m, codes, scales, gscale, n, k, lora_b, r, y, workspace,
                          workspace_bytes, stream, true);
+}
+
+qerl_status qerl_aqn_sample_rows(uint64_t seed, uint64_t stream_id, uint64_t call_id,
+                                 double sigma, int64_t m, int64_t d, float* z_out,
+                                 void* stream) {
+  if (!z_out) return QERL_ERR_NULL;
+  if (d < 1 || m < 1 || m > 65535) return QERL_ERR_SHAPE;
+  if (!(sigma >= 0.0) || !std::isfinite(sigma)) return QERL_ERR_RANGE;
+  if (!aligned(z_out, 4)) return QERL_ERR_ALIGN;
+  return from_hip(qerl::launch_aqn_sample(seed, stream_id, call_id, 0, 1, m, sigma, d, z_out,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+qerl_status qerl_linear_decode_rownoise(const void* x, int64_t m, const void* codes,
+                                        const void* scales, const float* gscale, int64_t n,
+                                        int64_t k, const void* lora_a, const void* lora_b,
+                                        int32_t r, float lora_scale, const float* z_rows,
+                                        void* y, void* workspace, size_t workspace_bytes,
+                                        void* stream) {
+  if (!z_rows) return QERL_ERR_NULL;
+  return linear_full(false, x, m, codes, scales, gscale, n, k, lora_a, lora_b, r, lora_scale,
+                     z_rows, y, workspace, workspace_bytes, stream, false, false, false, true);
+}
+
+qerl_status qerl_linear_prefill_rownoise(const void* x, int64_t m, const void* codes,
+                                         const void* scales, const float* gscale, int64_t n,
+                                         int64_t k, const void* lora_a, const void* lora_b,
+                                         int32_t r, float lora_scale, const float* z_rows,
+                                         void* y, void* workspace, size_t workspace_bytes,
+                                         void* stream) {
+  if (!z_rows) return QERL_ERR_NULL;
+  return linear_full(true, x, m, codes, scales, gscale, n, k, lora_a, lora_b, r, lora_scale,
+                     z_rows, y, workspace, workspace_bytes, stream, false, false, false, true);
+}
+
+qerl_status qerl_attention_stub(const void* qkv, int64_t m, int32_t n_q_heads,
+                                int32_t n_kv_heads, int32_t head_dim, void* out, void* stream) {
+  if (!qkv || !out) return QERL_ERR_NULL;
+  if (m < 1 || n_q_heads < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads || head_dim < 8 ||
+      head_dim % 8)
+    return QERL_ERR_SHAPE;
+  if (!aligned(qkv, 16) || !aligned(out, 16)) return QERL_ERR_ALIGN;
+  return from_hip(qerl::launch_attention_stub(static_cast<const uint16_t*>(qkv), m, n_q_heads,
+                                              n_kv_heads, head_dim, static_cast<uint16_t*>(out),
+                                              static_cast<hipStream_t>(stream)));
 }
 
 size_t qerl_nvfp4_tile128_bytes(int64_t n, int64_t k) {

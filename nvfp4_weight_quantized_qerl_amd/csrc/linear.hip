@@ -164,7 +164,8 @@ struct PrepArgs {
   const uint16_t* __restrict__ x;  // [m, ldx]; with swiglu, gate in 0 .. k-1 and up in k .. 2k-1
   int64_t ldx;
   int swiglu;                      // the layer input is bf16(SiLU(gate) * up)
-  const float* __restrict__ z;
+  const float* __restrict__ z;     // [k] shared by the rows, or [m, k] one row per token
+  int64_t z_ld;                    // 0: shared; k: one noise row per token
   const uint16_t* __restrict__ a;
   uint16_t* __restrict__ xt;     // null: x_t is not written (only the LoRA-down partials)
   float* __restrict__ tpart;
@@ -213,7 +214,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs p) {
   const int64_t kl = kc + 8 * lane;       // this lane's channels
   const bool kin = kl < p.k;              // k % 8 == 0: all eight in range or none
   float4 z0 = make_float4(0.0f, 0.0f, 0.0f, 0.0f), z1 = z0;
-  if (kin && p.z) {
+  if (kin && p.z && p.z_ld == 0) {
     z0 = *reinterpret_cast<const float4*>(p.z + kl);
     z1 = *reinterpret_cast<const float4*>(p.z + kl + 4);
   }
@@ -238,7 +239,15 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs p) {
   for (int i = 0; i < 8; ++i) {
     const int rr = 8 * wave + i;
     const int64_t mrow = row0 + rr;
-    if (mrow < p.m && p.z) xv[i] = noisy8(xv[i], z0, z1);
+    if (mrow < p.m && p.z) {
+      if (p.z_ld && kin) {
+        const float* zr = p.z + mrow * p.z_ld + kl;     // this token's own noise row
+        xv[i] = noisy8(xv[i], *reinterpret_cast<const float4*>(zr),
+                       *reinterpret_cast<const float4*>(zr + 4));
+      } else {
+        xv[i] = noisy8(xv[i], z0, z1);
+      }
+    }
     if (kin && p.xt) *reinterpret_cast<uint4*>(p.xt + mrow * p.k + kl) = xv[i];
     xs[rr * 64 + (lane ^ (rr & 15))] = xv[i];
   }
@@ -285,9 +294,11 @@ __global__ __launch_bounds__(256) void xt_kernel(PrepArgs p) {
   if (mrow < p.m) {
     xv = *reinterpret_cast<const uint4*>(p.x + mrow * p.ldx + k0);
     if (p.swiglu) xv = swiglu8(xv, *reinterpret_cast<const uint4*>(p.x + mrow * p.ldx + p.k + k0));
-    if (p.z)
-      xv = noisy8(xv, *reinterpret_cast<const float4*>(p.z + k0),
-                  *reinterpret_cast<const float4*>(p.z + k0 + 4));
+    if (p.z) {
+      const float* zr = p.z + mrow * p.z_ld + k0;
+      xv = noisy8(xv, *reinterpret_cast<const float4*>(zr),
+                  *reinterpret_cast<const float4*>(zr + 4));
+    }
   }
   *reinterpret_cast<uint4*>(p.xt + mrow * p.k + k0) = xv;
 }
@@ -333,6 +344,7 @@ hipError_t launch_lora_down(const uint16_t* x, int64_t m, int64_t mpad, int64_t 
   a.ldx = k;
   a.swiglu = 0;
   a.z = nullptr;
+  a.z_ld = 0;
   a.a = a_rk;
   a.xt = nullptr;
   a.tpart = tpart;
@@ -372,12 +384,14 @@ hipError_t launch_treduce(const LinearPlan& p, char* ws, hipStream_t stream) {
 hipError_t launch_linear_prepare(const LinearPlan& p, const uint16_t* x,
                                  const float* z, const uint16_t* lora_a,
                                  float lora_scale, char* ws,
-                                 hipStream_t stream, bool swiglu_input, bool write_xt) {
+                                 hipStream_t stream, bool swiglu_input, bool write_xt,
+                                 bool z_rows) {
   PrepArgs a;
   a.x = x;
   a.ldx = swiglu_input ? 2 * p.k : p.k;
   a.swiglu = swiglu_input ? 1 : 0;
   a.z = z;
+  a.z_ld = (z && z_rows) ? p.k : 0;
   a.a = lora_a;
   a.xt = write_xt ? reinterpret_cast<uint16_t*>(ws + p.off_xt) : nullptr;
   a.tpart = reinterpret_cast<float*>(ws + p.off_tpart);

@@ -80,11 +80,17 @@ bool make_linear_plan(int64_t m, int64_t n, int64_t k, int r, LinearPlan* p, boo
 // input is bf16(SiLU(gate) * up), formed as the rows are loaded.  Without
 // write_xt only t is produced (x_t is not stored; nothing is launched
 // without a LoRA branch).
+// z_rows: z is [m, k], one noise row per token (else [k], shared).
 hipError_t launch_linear_prepare(const LinearPlan& p, const uint16_t* x,
                                  const float* z, const uint16_t* lora_a,
                                  float lora_scale, char* ws,
                                  hipStream_t stream, bool swiglu_input = false,
-                                 bool write_xt = true);
+                                 bool write_xt = true, bool z_rows = false);
+
+// Single-position attention stub: out[i, h dh + e] = v[i, (h / (hq / hkv)) dh + e]
+// of qkv [m, (hq + 2 hkv) dh] (q, then k, then v heads).
+hipError_t launch_attention_stub(const uint16_t* qkv, int64_t m, int hq, int hkv, int dh,
+                                 uint16_t* out, hipStream_t stream);
 
 // t = bf16(scale x a_rk^T) for x [m, k] (rows m..mpad-1 read as zero) and
 // a_rk [r, k]: the LoRA-down kernels on any operands (partials [ceil(k/512),

@@ -18,7 +18,9 @@ the normal numbers are produced.  The oracle and the HIP library both use
   * Philox4x64-10, the counter-based generator of Salmon, Moraes, Dror and
     Shaw, "Parallel random numbers: as easy as 1, 2, 3" (SC'11), with
       key     = (seed, stream_id)
-      counter = (j // 4, call_id, 0, 0)   for noise element j;
+      counter = (j // 4, call_id, row, 0) for noise element j, row = 0 for
+                the vector shared by a call's token rows, row = i for token
+                row i when every rollout draws its own;
   * the Box-Muller transform (Box and Muller, 1958) on the four 64-bit
     output words (r0, r1, r2, r3) of that counter:
       u1 = ((r >> 11) + 1) * 2**-53  in (0, 1]   from r0 (resp. r2)
@@ -127,11 +129,13 @@ def box_muller_pair(r_a, r_b):
     return rad * math.cos(ang), rad * math.sin(ang)
 
 
-def standard_normals(seed, stream_id, call_id, d):
-    """n_0..n_{d-1} for (seed, stream_id, call_id), fp64."""
+def standard_normals(seed, stream_id, call_id, d, row=0):
+    """n_0..n_{d-1} for (seed, stream_id, call_id), fp64; `row` is counter
+    word 2 (0 for the noise vector shared by the rows of a call, i for
+    token row i of the per-rollout variant)."""
     out = np.empty(int(d), dtype=np.float64)
     for q in range((int(d) + 3) // 4):
-        r0, r1, r2, r3 = philox4x64((q, call_id, 0, 0), (seed, stream_id))
+        r0, r1, r2, r3 = philox4x64((q, call_id, row, 0), (seed, stream_id))
         vals = box_muller_pair(r0, r1) + box_muller_pair(r2, r3)
         for i in range(4):
             j = 4 * q + i
@@ -140,7 +144,15 @@ def standard_normals(seed, stream_id, call_id, d):
     return out
 
 
-def sample(seed, stream_id, call_id, sig, d):
+def sample(seed, stream_id, call_id, sig, d, row=0):
     """AQN noise vector z (fp32 [d]) [QeRL summary, §3.4, Eq. 7]."""
-    n = standard_normals(seed, stream_id, call_id, d)
+    n = standard_normals(seed, stream_id, call_id, d, row)
     return (float(sig) * n).astype(np.float32)
+
+
+def sample_rows(seed, stream_id, call_id, sig, m, d):
+    """One noise vector per token row (fp32 [m, d]): the variant in which
+    every rollout of a batch sees its own draw [QeRL summary, §3.4 "Noise
+    injection frequency"].  Row i uses counter word 2 = i, so row 0 is the
+    shared vector of `sample`."""
+    return np.stack([sample(seed, stream_id, call_id, sig, d, row=i) for i in range(int(m))])
