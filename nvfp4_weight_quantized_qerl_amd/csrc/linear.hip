@@ -174,7 +174,8 @@ struct PrepArgs {
   float lora_scale;
 };
 
-// One workgroup: 32 rows x one 512-wide K chunk.
+// One workgroup: 32 rows x one 512-wide K chunk x RT 32-wide rank tiles
+// (the launches use RT = 1 and one rank tile per grid z).
 //   x_t: wave w reads and writes rows 8 w .. 8 w + 7, one row of the chunk
 //        (1 KB) per instruction, lane l holding channels 8 l .. 8 l + 7; the
 //        rows also go to an LDS tile, 16-byte chunk q of row rr stored at
@@ -195,8 +196,10 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs p) {
   const int64_t kc = (int64_t)blockIdx.y * kPrepChunk;
   const int64_t row0 = (int64_t)blockIdx.x * 32;
 
-  // A operands of this wave's 128 channels (lane: row j = 32 t + c of A).
+  // A operands of this wave's 128 channels (lane: row j = 32 t + c of A,
+  // from the rank tiles of this workgroup: blockIdx.z picks RT tiles of 32).
   const int64_t kb = kc + 128 * wave;
+  const int rank0 = 32 * RT * (int)blockIdx.z;
   uint4 av[RT > 0 ? RT : 1][STEPS];
 #pragma unroll
   for (int s = 0; s < STEPS; ++s) {
@@ -204,7 +207,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs p) {
     const bool in = kb + 16 * s < p.k;   // k % 16 == 0: the whole step is in range
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
-      const int j = 32 * t + c;
+      const int j = rank0 + 32 * t + c;
       av[t][s] = (in && j < p.r) ? *reinterpret_cast<const uint4*>(p.a + (int64_t)j * p.k + k0)
                                  : make_uint4(0u, 0u, 0u, 0u);
     }
@@ -248,7 +251,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs p) {
         xv[i] = noisy8(xv[i], z0, z1);
       }
     }
-    if (kin && p.xt) *reinterpret_cast<uint4*>(p.xt + mrow * p.k + kl) = xv[i];
+    if (kin && p.xt && blockIdx.z == 0) *reinterpret_cast<uint4*>(p.xt + mrow * p.k + kl) = xv[i];
     xs[rr * 64 + (lane ^ (rr & 15))] = xv[i];
   }
   if (RT == 0) return;
@@ -277,7 +280,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs p) {
     for (int w = 0; w < 3; ++w)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[t][v] += red[((w * RT + t) * 16 + v) * 64 + lane];
-    float* dst = p.tpart + ((int64_t)blockIdx.y * p.mpad + row0) * p.rpad32 + 32 * t + c;
+    float* dst = p.tpart + ((int64_t)blockIdx.y * p.mpad + row0) * p.rpad32 + rank0 + 32 * t + c;
 #pragma unroll
     for (int v = 0; v < 16; ++v) dst[(int64_t)acc_row(v, lane) * p.rpad32] = p.lora_scale * acc[t][v];
   }
@@ -355,14 +358,11 @@ hipError_t launch_lora_down(const uint16_t* x, int64_t m, int64_t mpad, int64_t 
   a.rpad32 = (int)rup(r, 32);
   a.lora_scale = scale;
   const int kchunks = (int)cdiv(k, kPrepChunk);
-  const dim3 grid((unsigned)(mpad / 32), (unsigned)kchunks);
-  switch (a.rpad32 / 32) {
-    case 1: hipLaunchKernelGGL(prep_kernel<1>, grid, dim3(256), 0, stream, a); break;
-    case 2: hipLaunchKernelGGL(prep_kernel<2>, grid, dim3(256), 0, stream, a); break;
-    case 3: hipLaunchKernelGGL(prep_kernel<3>, grid, dim3(256), 0, stream, a); break;
-    case 4: hipLaunchKernelGGL(prep_kernel<4>, grid, dim3(256), 0, stream, a); break;
-    default: return hipErrorInvalidValue;
-  }
+  // One 32-wide rank tile per workgroup (grid z): a workgroup loads a
+  // quarter of A at rank 128 and finishes sooner; x is read once per tile.
+  const dim3 grid((unsigned)(mpad / 32), (unsigned)kchunks, (unsigned)(a.rpad32 / 32));
+  if (a.rpad32 < 32 || a.rpad32 > 128) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(prep_kernel<1>, grid, dim3(256), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int rpad16 = (int)rup(r, 16);
@@ -407,14 +407,11 @@ hipError_t launch_linear_prepare(const LinearPlan& p, const uint16_t* x,
     hipLaunchKernelGGL(xt_kernel, dim3((unsigned)cdiv(threads, 256)), dim3(256), 0, stream, a);
     return hipGetLastError();
   }
-  const dim3 grid((unsigned)(p.mpad / 32), (unsigned)p.kchunks);
-  switch (p.rpad32 / 32) {
-    case 1: hipLaunchKernelGGL(prep_kernel<1>, grid, dim3(256), 0, stream, a); break;
-    case 2: hipLaunchKernelGGL(prep_kernel<2>, grid, dim3(256), 0, stream, a); break;
-    case 3: hipLaunchKernelGGL(prep_kernel<3>, grid, dim3(256), 0, stream, a); break;
-    case 4: hipLaunchKernelGGL(prep_kernel<4>, grid, dim3(256), 0, stream, a); break;
-    default: return hipErrorInvalidValue;
-  }
+  // One 32-wide rank tile per workgroup (grid z); the tile-0 workgroups
+  // also write x_t.
+  const dim3 grid((unsigned)(p.mpad / 32), (unsigned)p.kchunks, (unsigned)(p.rpad32 / 32));
+  if (p.rpad32 < 32 || p.rpad32 > 128) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(prep_kernel<1>, grid, dim3(256), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_treduce(p, ws, stream);
