@@ -347,6 +347,20 @@ def qerl_linear_prefill(x, codes, scales, gscale, lora_a=None, lora_b=None, lora
                    lora_scale, z, workspace, y)
 
 
+def bind_linear_prepare(x, n, lora_a, lora_scale, z, workspace):
+    """A BoundCall of qerl_linear_prepare (the first half of a linear call)."""
+    x = _bits16(x, "x")
+    m, k = x.shape
+    r = 0 if lora_a is None else int(lora_a.shape[0])
+    la = None if lora_a is None else _bits16(lora_a, "lora_a")
+    _need(la, "lora_a", _BF16, (r, k), x.device)
+    _need(z, "z", torch.float32, (k,), x.device)
+    _need(workspace, "workspace", torch.uint8, (workspace.numel(),), x.device)
+    args = (_ptr(x), m, n, k, _ptr(la), r, float(lora_scale), _ptr(z), _ptr(workspace),
+            workspace.numel(), _stream(x.device))
+    return BoundCall("qerl_linear_prepare", args, (x, la, z, workspace), workspace)
+
+
 def qerl_linear_prepare(x, n, lora_a, lora_scale, z, workspace):
     x = _bits16(x, "x")
     m, k = x.shape
