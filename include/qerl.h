@@ -91,7 +91,7 @@ QERL_API int qerl_abi_version(void);
  *   nonfinite_flag device out, nullable; set to 1 if w holds an inf or a
  *                  NaN, else 0.  When it is 1, codes/scales/gscale are
  *                  unspecified.
- * Four kernels are enqueued (reset, amax, scale, encode).
+ * Three kernels are enqueued (reset, amax, encode).
  */
 QERL_API qerl_status qerl_quantize_nvfp4(const void* w_bf16, int64_t n, int64_t k,
                                 void* codes, void* scales, float* gscale,

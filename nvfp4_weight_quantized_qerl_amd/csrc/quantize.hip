@@ -9,16 +9,20 @@
 //   code = sign | RNE_E2M1(|w| / (s_b S)), saturating at 6, ties to even
 // with the quotients taken exactly, so the encoding is unique.
 //
-// Four stream-ordered kernels:
-//   reset    gscale slot <- 0 (it doubles as the amax accumulator)
+// Three stream-ordered kernels:
+//   reset    gscale slot <- 0x80000000 (the slot doubles as the amax
+//            accumulator; the top bit marks "still an amax")
 //   amax     max over |w| as integers (bf16 bits & 0x7fff; for
-//            non-negative floats integer order is value order) combined
-//            with a global atomic max of the fp32 bit pattern
-//   scale    one thread: non-finite flag, S = RN_fp32(amax / 2688)
-//   encode   one thread per 16-element block (blocks are contiguous in
-//            memory because k % 16 == 0), grid-stride; each workgroup
-//            first tabulates the element keys of all 126 nonzero block-scale
-//            codes (they depend only on the code and S)
+//            non-negative floats integer order is value order), one global
+//            atomic max per workgroup of 0x80000000 | (fp32 bits of the max)
+//   encode   every workgroup forms the non-finite flag and S = RN_fp32(amax
+//            / 2688) from the slot (or takes S from it if another workgroup
+//            has already stored S there: S never has the top bit set), and
+//            workgroup 0 stores S and the flag; then one thread per
+//            16-element block (blocks are contiguous in memory because
+//            k % 16 == 0), two blocks per iteration, grid-stride; each
+//            workgroup first tabulates the element keys of all 126 nonzero
+//            block-scale codes (they depend only on the code and S)
 //
 // Exactness of `encode` (no rounding can change a decision):
 //  * q = amax_b / (6 S) in fp64.  amax_b has 8 significant bits and 6 S at
@@ -42,11 +46,17 @@
 namespace qerl {
 namespace {
 
-__global__ void qz_reset(uint32_t* slot) { *slot = 0u; }
+constexpr uint32_t kAmaxMark = 0x80000000u;
 
-__global__ __launch_bounds__(256) void qz_amax(const uint4* __restrict__ w,
-                                               int64_t nvec,
-                                               uint32_t* __restrict__ slot) {
+__global__ void qz_reset(uint32_t* slot) { *slot = kAmaxMark; }
+
+// At most one workgroup per CU: the per-workgroup atomics on the one slot
+// are serialised where the slot lives, so there are few of them.
+constexpr int kAmaxThreads = 512;
+
+__global__ __launch_bounds__(kAmaxThreads) void qz_amax(const uint4* __restrict__ w,
+                                                        int64_t nvec,
+                                                        uint32_t* __restrict__ slot) {
   uint32_t m = 0;
   auto fold = [&](const uint4& v) {
     const uint32_t a = max(v.x & 0x7fffu, (v.x >> 16) & 0x7fffu);
@@ -68,30 +78,33 @@ __global__ __launch_bounds__(256) void qz_amax(const uint4* __restrict__ w,
   for (; i < nvec; i += stride) fold(w[i]);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
-  __shared__ uint32_t red[4];
+  __shared__ uint32_t red[kAmaxThreads / 64];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   if (lane == 0) red[wid] = m;
   __syncthreads();
   if (threadIdx.x == 0) {
-    uint32_t r = max(max(red[0], red[1]), max(red[2], red[3]));
-    if (r) atomicMax(slot, r << 16);   // fp32 bits of the bf16 magnitude
+    uint32_t r = 0;
+#pragma unroll
+    for (int u = 0; u < kAmaxThreads / 64; ++u) r = max(r, red[u]);
+    if (r) atomicMax(slot, kAmaxMark | (r << 16));   // fp32 bits of the bf16 magnitude
   }
 }
 
-__global__ void qz_scale(uint32_t* slot, int32_t* flag) {
-  const uint32_t bits = *slot;
-  const bool nonfinite = bits >= 0x7f800000u;
-  if (flag) *flag = nonfinite ? 1 : 0;
-  float S;
-  if (nonfinite) {
-    S = __uint_as_float(0x7fc00000u);
-  } else {
-    // amax / 2688 in fp64, then to fp32: the exact quotient is amax/21
-    // times a power of two, never an fp32 midpoint nor within fp64
-    // rounding of one, so this is the correctly rounded fp32 quotient.
-    S = (float)((double)__uint_as_float(bits) / 2688.0);
+// S and the non-finite flag from the slot: the marked amax (S is formed
+// here), or S itself, stored by a workgroup that got there first.
+__device__ __forceinline__ float scale_from_slot(uint32_t bits, bool* nonfinite) {
+  if (!(bits & kAmaxMark)) {
+    const float S = __uint_as_float(bits);
+    *nonfinite = S != S;
+    return S;
   }
-  *reinterpret_cast<float*>(slot) = S;
+  bits &= ~kAmaxMark;
+  *nonfinite = bits >= 0x7f800000u;
+  if (*nonfinite) return __uint_as_float(0x7fc00000u);
+  // amax / 2688 in fp64, then to fp32: the exact quotient is amax/21 times a
+  // power of two, never an fp32 midpoint nor within fp64 rounding of one,
+  // so this is the correctly rounded fp32 quotient.
+  return (float)((double)__uint_as_float(bits) / 2688.0);
 }
 
 // Round q > 0 to OCP E4M3 (nearest, ties to even), saturating at 448.
@@ -132,50 +145,83 @@ __device__ __forceinline__ void build_keys(int16_t (*key_tab)[8], double S) {
   }
 }
 
-// Grid-stride over 16-element blocks; each thread encodes one block per
-// iteration (blocks are contiguous in memory because k % 16 == 0).
+typedef int16_t i16x2 __attribute__((ext_vector_type(2)));
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+
+// One 16-element block: E4M3 block-scale code and the 16 packed E2M1 codes.
+// The element codes are counted two at a time in 16-bit halves: a bf16 word
+// pair masked with 0x7fff7fff holds the two magnitudes, and key - |w| (both
+// in [-1, 0x7fff]) is negative exactly when |w| > key.
+__device__ __forceinline__ uint32_t encode_block(const uint4& lo, const uint4& hi, float S,
+                                                 const int16_t (*key_tab)[8], uint2* out) {
+  const uint32_t words[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  uint32_t amax_b = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    amax_b = max(amax_b, max(words[i] & 0x7fffu, (words[i] >> 16) & 0x7fffu));
+  uint32_t scode = 0;
+  if (S > 0.0f && amax_b != 0) {
+    const double q = (double)bf16_to_f32(amax_b) / (6.0 * (double)S);
+    scode = e4m3_rne_code(q);
+  }
+  i16x2 key[7];
+#pragma unroll
+  for (int t = 0; t < 7; ++t) {
+    const int16_t kt = scode ? key_tab[scode][t] : (int16_t)0x7fff;
+    key[t] = i16x2{kt, kt};
+  }
+  uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t mw = words[i] & 0x7fff7fffu;
+    const i16x2 a = __builtin_bit_cast(i16x2, mw);
+    u16x2 cnt = u16x2{0, 0};
+#pragma unroll
+    for (int t = 0; t < 7; ++t) cnt += __builtin_bit_cast(u16x2, key[t] - a) >> (uint16_t)15;
+    // the two codes (0..7) with their sign bits (bf16 bit 15 -> code bit 3)
+    const uint32_t c2 = __builtin_bit_cast(uint32_t, cnt) | ((words[i] >> 12) & 0x00080008u);
+    packed[i >> 2] |= ((c2 & 0xfu) | ((c2 >> 12) & 0xf0u)) << (8 * (i & 3));
+  }
+  *out = make_uint2(packed[0], packed[1]);
+  return scode;
+}
+
+// Grid-stride over 16-element blocks, two per thread per iteration (their
+// four loads issued together); blocks are contiguous in memory because
+// k % 16 == 0.
 __global__ __launch_bounds__(256) void qz_encode(const uint4* __restrict__ w,
                                                  int64_t nblocks,
-                                                 const float* __restrict__ gscale,
+                                                 uint32_t* __restrict__ slot,
+                                                 int32_t* __restrict__ flag,
                                                  uint2* __restrict__ codes,
                                                  uint8_t* __restrict__ scales) {
   __shared__ int16_t key_tab[kCodes][8];
-  const float S = *gscale;
+  bool nonfinite = false;
+  const float S = scale_from_slot(*slot, &nonfinite);
   build_keys(key_tab, (double)S);
   __syncthreads();
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    *reinterpret_cast<float*>(slot) = S;
+    if (flag) *flag = nonfinite ? 1 : 0;
+  }
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nblocks; b += stride) {
-    const uint4 lo = w[2 * b], hi = w[2 * b + 1];
-    const uint32_t words[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-    uint32_t mag[16];
-    uint32_t amax_b = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      mag[2 * i] = words[i] & 0x7fffu;
-      mag[2 * i + 1] = (words[i] >> 16) & 0x7fffu;
-      amax_b = max(amax_b, max(mag[2 * i], mag[2 * i + 1]));
-    }
-    uint32_t scode = 0;
-    if (S > 0.0f && amax_b != 0) {
-      const double q = (double)bf16_to_f32(amax_b) / (6.0 * (double)S);
-      scode = e4m3_rne_code(q);
-    }
-    int32_t key[7];
-#pragma unroll
-    for (int t = 0; t < 7; ++t) key[t] = scode ? (int32_t)key_tab[scode][t] : 0x7fff;
-    uint32_t packed[2] = {0u, 0u};
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int32_t a = (int32_t)mag[i];
-      uint32_t c = 0;
-#pragma unroll
-      for (int t = 0; t < 7; ++t) c += (a > key[t]) ? 1u : 0u;
-      const uint32_t sign = (words[i >> 1] >> ((i & 1) ? 31 : 15)) & 1u;
-      c |= sign << 3;
-      packed[i >> 3] |= c << (4 * (i & 7));
-    }
-    codes[b] = make_uint2(packed[0], packed[1]);
-    scales[b] = (uint8_t)scode;
+  int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; b + stride < nblocks; b += 2 * stride) {
+    const uint4 lo0 = w[2 * b], hi0 = w[2 * b + 1];
+    const uint4 lo1 = w[2 * (b + stride)], hi1 = w[2 * (b + stride) + 1];
+    uint2 c0, c1;
+    const uint32_t s0 = encode_block(lo0, hi0, S, key_tab, &c0);
+    const uint32_t s1 = encode_block(lo1, hi1, S, key_tab, &c1);
+    codes[b] = c0;
+    scales[b] = (uint8_t)s0;
+    codes[b + stride] = c1;
+    scales[b + stride] = (uint8_t)s1;
+  }
+  if (b < nblocks) {
+    uint2 c0;
+    const uint32_t s0 = encode_block(w[2 * b], w[2 * b + 1], S, key_tab, &c0);
+    codes[b] = c0;
+    scales[b] = (uint8_t)s0;
   }
 }
 
@@ -188,20 +234,17 @@ hipError_t launch_quantize(const uint16_t* w, int64_t n, int64_t k,
   const int64_t nvec = n * k / 8;
   const int64_t nblocks = n * k / 16;
   hipLaunchKernelGGL(qz_reset, dim3(1), dim3(1), 0, stream, slot);
-  int64_t grid = (nvec + 255) / 256;
-  const int64_t cap = (int64_t)device_cu_count() * 8;
-  if (grid > cap) grid = cap;
-  if (grid < 1) grid = 1;
-  hipLaunchKernelGGL(qz_amax, dim3((unsigned)grid), dim3(256), 0, stream,
+  const int64_t grid =
+      std::max<int64_t>(1, std::min<int64_t>((nvec + kAmaxThreads - 1) / kAmaxThreads,
+                                             (int64_t)device_cu_count()));
+  hipLaunchKernelGGL(qz_amax, dim3((unsigned)grid), dim3(kAmaxThreads), 0, stream,
                      reinterpret_cast<const uint4*>(w), nvec, slot);
-  hipLaunchKernelGGL(qz_scale, dim3(1), dim3(1), 0, stream, slot, flag);
   // Enough workgroups to fill the chip a few times over; each builds its
   // key table once and then loops over its blocks.
   const int64_t eg = std::min<int64_t>((nblocks + 255) / 256, (int64_t)device_cu_count() * 8);
   hipLaunchKernelGGL(qz_encode, dim3((unsigned)eg), dim3(256), 0, stream,
-                     reinterpret_cast<const uint4*>(w), nblocks,
-                     (const float*)gscale, reinterpret_cast<uint2*>(codes),
-                     scales);
+                     reinterpret_cast<const uint4*>(w), nblocks, slot, flag,
+                     reinterpret_cast<uint2*>(codes), scales);
   return hipGetLastError();
 }
 
