@@ -871,7 +871,7 @@ def run_rmsnorm(q, dev, stream, to_dev):
 
 
 # --------------------------------------------------------- oracle on the host
-def oracle_sweep_rate(sw, min_seconds=12.0, max_reps=30):
+def oracle_sweep_rate(sw, min_seconds=12.0, max_reps=100):
     """The oracle running a labelled slice of the headline step on the host:
     layer 0 of the 32B sweep, the first 512 output rows of each of its four
     projections, all 128 tokens and all K: per projection, draw the noise

@@ -22,7 +22,9 @@
  *   - The return value reports host-side validation and launch errors
  *     only (qerl_status).  On an error nothing has been enqueued.
  *   - Calls are reentrant and thread-safe; the library keeps no mutable
- *     global state besides a per-process cache of device properties.
+ *     global state besides a per-process cache of device properties (and
+ *     the per-device scratch array of qerl_linear_decode_noalloc, whose
+ *     calls must not overlap on one GPU).
  *
  * NVFP4 storage [QeRL summary, §3.4, Eq. 6: W_hat = S_FP32 * (S_E4M3 (.)
  * W_tilde), one E4M3 scale per block of 16 contiguous elements and one
