@@ -100,6 +100,30 @@ QERL_API qerl_status qerl_quantize_nvfp4(const void* w_bf16, int64_t n, int64_t 
                                 int32_t* nonfinite_flag, void* stream);
 
 /*
+ * qerl_quantize_nvfp4_batch -- qerl_quantize_nvfp4 of `count` tensors in
+ * one call, each with the same result (bit for bit) as its own call.  The
+ * pages quantize a model's weights once, when it is loaded, and keep them
+ * [QeRL summary, §3.2 and §3.3]; this is that bulk step.  count + 2 kernels
+ * are enqueued: one launch per tensor runs the encode pass of tensor i
+ * beside the amax pass of tensor i + 1, so tensor i's second read mostly
+ * hits the last-level cache and no launch is spent on a separate pass.
+ *   count              1 <= count <= 1 << 20
+ *   w_bf16, n, k,      host arrays of `count` entries; entry i is as the
+ *   codes, scales,     arguments of qerl_quantize_nvfp4 (device pointers,
+ *   gscale             same shapes and alignment).  No two tensors' outputs
+ *                      may overlap.
+ *   nonfinite_flag     host array of `count` device pointers (entries
+ *                      nullable), or NULL for no flags
+ * Every entry is checked before anything is enqueued; the first bad entry
+ * decides the status.  The host arrays are read during the call only.
+ */
+QERL_API qerl_status qerl_quantize_nvfp4_batch(int32_t count, const void* const* w_bf16,
+                                               const int64_t* n, const int64_t* k,
+                                               void* const* codes, void* const* scales,
+                                               float* const* gscale,
+                                               int32_t* const* nonfinite_flag, void* stream);
+
+/*
  * qerl_aqn_sigma -- host, pure.  The AQN exponential decay schedule
  * [QeRL summary, §3.4, Eq. 8]:
  *   sigma(k) = sigma_start * (sigma_end / sigma_start)^((k-1)/(K-1)),

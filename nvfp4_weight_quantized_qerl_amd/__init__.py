@@ -107,6 +107,54 @@ def qerl_quantize_nvfp4(w):
     return codes, scales, gscale, flag
 
 
+def _quantize_batch_args(ws, outs):
+    """Host pointer arrays of qerl_quantize_nvfp4_batch for the bf16 weights
+    `ws` and their outputs `outs` [(codes, scales, gscale, flag or None)]."""
+    if not ws or len(ws) != len(outs):
+        raise ValueError("qerl_quantize_nvfp4_batch: one output tuple per weight, at least one")
+    cnt = len(ws)
+    ws = [_bits16(w, "w") for w in ws]
+    dev = ws[0].device
+    for w, (codes, scales, gscale, flag) in zip(ws, outs):
+        n, k = w.shape
+        if w.device != dev:
+            raise ValueError("qerl_quantize_nvfp4_batch: every tensor on one device")
+        _need(codes, "codes", torch.uint8, (n, k // 2), dev)
+        _need(scales, "scales", torch.uint8, (n, k // 16), dev)
+        _need(gscale, "gscale", torch.float32, (1,), dev)
+        _need(flag, "flag", torch.int32, (1,), dev)
+    ptrs = lambda ts: (ctypes.c_void_p * cnt)(*[None if t is None else t.data_ptr() for t in ts])
+    arrays = (ptrs(ws), (ctypes.c_int64 * cnt)(*[w.shape[0] for w in ws]),
+              (ctypes.c_int64 * cnt)(*[w.shape[1] for w in ws]),
+              ptrs([o[0] for o in outs]), ptrs([o[1] for o in outs]), ptrs([o[2] for o in outs]),
+              ptrs([o[3] for o in outs]))
+    args = (cnt,) + tuple(ctypes.cast(a, ctypes.c_void_p) for a in arrays) + (_stream(dev),)
+    return args, (ws, outs, arrays)
+
+
+def qerl_quantize_nvfp4_batch(ws):
+    """qerl_quantize_nvfp4 of every bf16 weight in the list `ws` in one call
+    (count + 2 launches); returns [(codes, scales, gscale, nonfinite)]."""
+    outs = []
+    for w in ws:
+        n, k = w.shape
+        dev = w.device
+        outs.append((torch.empty((n, k // 2), dtype=torch.uint8, device=dev),
+                     torch.empty((n, k // 16), dtype=torch.uint8, device=dev),
+                     torch.empty(1, dtype=torch.float32, device=dev),
+                     torch.empty(1, dtype=torch.int32, device=dev)))
+    args, keep = _quantize_batch_args(ws, outs)
+    _check(lib.qerl_quantize_nvfp4_batch(*args), "qerl_quantize_nvfp4_batch")
+    return outs
+
+
+def bind_quantize_nvfp4_batch(ws, outs):
+    """A BoundCall of qerl_quantize_nvfp4_batch into preallocated outputs
+    [(codes, scales, gscale, flag or None)], one tuple per weight in `ws`."""
+    args, keep = _quantize_batch_args(ws, outs)
+    return BoundCall("qerl_quantize_nvfp4_batch", args, keep, outs)
+
+
 def bind_quantize_nvfp4(w, codes, scales, gscale, flag=None):
     """A BoundCall of qerl_quantize_nvfp4 into preallocated outputs (codes
     uint8 [n, k/2], scales uint8 [n, k/16], gscale float32 [1], flag int32 [1]

@@ -16,6 +16,8 @@ SIGNATURES = {
     "qerl_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "qerl_abi_version": (ctypes.c_int, []),
     "qerl_quantize_nvfp4": (ctypes.c_int, [c_vp, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp]),
+    "qerl_quantize_nvfp4_batch": (ctypes.c_int, [c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                                 c_vp]),
     "qerl_quantize_mxfp4": (ctypes.c_int, [c_vp, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp]),
     "qerl_mxfp4_to_nvfp4": (ctypes.c_int, [c_vp, c_vp, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp]),
     "qerl_aqn_sigma": (ctypes.c_int, [c_f64, c_f64, c_i32, c_i32, ctypes.POINTER(c_f64)]),

@@ -56,7 +56,7 @@ const char* qerl_status_string(int status) {
   }
 }
 
-int qerl_abi_version(void) { return 10; }
+int qerl_abi_version(void) { return 11; }
 
 qerl_status qerl_quantize_nvfp4(const void* w_bf16, int64_t n, int64_t k, void* codes,
                                 void* scales, float* gscale, int32_t* nonfinite_flag,
@@ -70,6 +70,25 @@ qerl_status qerl_quantize_nvfp4(const void* w_bf16, int64_t n, int64_t k, void* 
       static_cast<const uint16_t*>(w_bf16), n, k, static_cast<uint8_t*>(codes),
       static_cast<uint8_t*>(scales), gscale, nonfinite_flag,
       static_cast<hipStream_t>(stream)));
+}
+
+qerl_status qerl_quantize_nvfp4_batch(int32_t count, const void* const* w_bf16, const int64_t* n,
+                                      const int64_t* k, void* const* codes, void* const* scales,
+                                      float* const* gscale, int32_t* const* nonfinite_flag,
+                                      void* stream) {
+  if (count < 1 || count > (1 << 20)) return QERL_ERR_SHAPE;
+  if (!w_bf16 || !n || !k || !codes || !scales || !gscale) return QERL_ERR_NULL;
+  for (int32_t i = 0; i < count; ++i) {
+    if (!w_bf16[i] || !codes[i] || !scales[i] || !gscale[i]) return QERL_ERR_NULL;
+    if (n[i] < 1 || k[i] < 16 || k[i] % 16) return QERL_ERR_SHAPE;
+    if (!aligned(w_bf16[i], 16) || !aligned(codes[i], 16) || !aligned(gscale[i], 4) ||
+        (nonfinite_flag && nonfinite_flag[i] && !aligned(nonfinite_flag[i], 4)))
+      return QERL_ERR_ALIGN;
+  }
+  return from_hip(qerl::launch_quantize_batch(
+      count, reinterpret_cast<const uint16_t* const*>(w_bf16), n, k,
+      reinterpret_cast<uint8_t* const*>(codes), reinterpret_cast<uint8_t* const*>(scales), gscale,
+      nonfinite_flag, static_cast<hipStream_t>(stream)));
 }
 
 qerl_status qerl_aqn_sigma(double sigma_start, double sigma_end, int32_t num_stages,

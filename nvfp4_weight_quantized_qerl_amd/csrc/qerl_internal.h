@@ -16,6 +16,11 @@ int device_cu_count();
 hipError_t launch_quantize(const uint16_t* w, int64_t n, int64_t k,
                            uint8_t* codes, uint8_t* scales, float* gscale,
                            int32_t* flag, hipStream_t stream);
+// `count` tensors in count + 2 launches (the encode pass of one tensor runs
+// beside the amax pass of the next); flag may be null, as may its entries.
+hipError_t launch_quantize_batch(int count, const uint16_t* const* w, const int64_t* n,
+                                 const int64_t* k, uint8_t* const* codes, uint8_t* const* scales,
+                                 float* const* gscale, int32_t* const* flag, hipStream_t stream);
 
 // MXFP4 (E8M0 scale per 32): quantize, and re-express the scales in the
 // NVFP4 layout (E4M3 per 16 + FP32 S) so the NVFP4 kernels run it exactly.

@@ -9,7 +9,7 @@
 //   code = sign | RNE_E2M1(|w| / (s_b S)), saturating at 6, ties to even
 // with the quotients taken exactly, so the encoding is unique.
 //
-// Three stream-ordered kernels:
+// Three stream-ordered kernels per tensor:
 //   reset    gscale slot <- 0x80000000 (the slot doubles as the amax
 //            accumulator; the top bit marks "still an amax")
 //   amax     max over |w| as integers (bf16 bits & 0x7fff; for
@@ -23,6 +23,9 @@
 //            k % 16 == 0), two blocks per iteration, grid-stride; each
 //            workgroup first tabulates the element keys of all 126 nonzero
 //            block-scale codes (they depend only on the code and S)
+// A batch of tensors runs in count + 2 launches: the reset of the first two
+// slots, the amax pass of the first tensor, then per tensor one launch with
+// its encode pass beside the amax pass of the next (qz_pipe).
 //
 // Exactness of `encode` (no rounding can change a decision):
 //  * q = amax_b / (6 S) in fp64.  amax_b has 8 significant bits and 6 S at
@@ -48,15 +51,19 @@ namespace {
 
 constexpr uint32_t kAmaxMark = 0x80000000u;
 
-__global__ void qz_reset(uint32_t* slot) { *slot = kAmaxMark; }
+// Both passes run workgroups of kThreads; the amax pass uses at most one
+// workgroup per CU: its per-workgroup atomics on the one slot are
+// serialised where the slot lives, so there are few of them.
+constexpr int kThreads = 512;
 
-// At most one workgroup per CU: the per-workgroup atomics on the one slot
-// are serialised where the slot lives, so there are few of them.
-constexpr int kAmaxThreads = 512;
+__global__ void qz_reset(uint32_t* a, uint32_t* b) {
+  *a = kAmaxMark;
+  if (b) *b = kAmaxMark;
+}
 
-__global__ __launch_bounds__(kAmaxThreads) void qz_amax(const uint4* __restrict__ w,
-                                                        int64_t nvec,
-                                                        uint32_t* __restrict__ slot) {
+// The amax pass over nvec 16-byte vectors, as workgroup wg of nwg.
+__device__ __forceinline__ void amax_body(const uint4* __restrict__ w, int64_t nvec,
+                                          uint32_t* __restrict__ slot, int64_t wg, int64_t nwg) {
   uint32_t m = 0;
   auto fold = [&](const uint4& v) {
     const uint32_t a = max(v.x & 0x7fffu, (v.x >> 16) & 0x7fffu);
@@ -66,8 +73,8 @@ __global__ __launch_bounds__(kAmaxThreads) void qz_amax(const uint4* __restrict_
     m = max(m, max(max(a, b), max(c, d)));
   };
   // Eight independent 16-byte loads per thread in flight per iteration.
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t stride = nwg * kThreads;
+  int64_t i = wg * kThreads + threadIdx.x;
   for (; i + 7 * stride < nvec; i += 8 * stride) {
     uint4 v[8];
 #pragma unroll
@@ -78,16 +85,21 @@ __global__ __launch_bounds__(kAmaxThreads) void qz_amax(const uint4* __restrict_
   for (; i < nvec; i += stride) fold(w[i]);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
-  __shared__ uint32_t red[kAmaxThreads / 64];
+  __shared__ uint32_t red[kThreads / 64];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   if (lane == 0) red[wid] = m;
   __syncthreads();
   if (threadIdx.x == 0) {
     uint32_t r = 0;
 #pragma unroll
-    for (int u = 0; u < kAmaxThreads / 64; ++u) r = max(r, red[u]);
+    for (int u = 0; u < kThreads / 64; ++u) r = max(r, red[u]);
     if (r) atomicMax(slot, kAmaxMark | (r << 16));   // fp32 bits of the bf16 magnitude
   }
+}
+
+__global__ __launch_bounds__(kThreads) void qz_amax(const uint4* __restrict__ w, int64_t nvec,
+                                                    uint32_t* __restrict__ slot) {
+  amax_body(w, nvec, slot, blockIdx.x, gridDim.x);
 }
 
 // S and the non-finite flag from the slot: the marked amax (S is formed
@@ -186,43 +198,94 @@ __device__ __forceinline__ uint32_t encode_block(const uint4& lo, const uint4& h
   return scode;
 }
 
-// Grid-stride over 16-element blocks, two per thread per iteration (their
-// four loads issued together); blocks are contiguous in memory because
-// k % 16 == 0.
-__global__ __launch_bounds__(256) void qz_encode(const uint4* __restrict__ w,
-                                                 int64_t nblocks,
-                                                 uint32_t* __restrict__ slot,
-                                                 int32_t* __restrict__ flag,
-                                                 uint2* __restrict__ codes,
-                                                 uint8_t* __restrict__ scales) {
-  __shared__ int16_t key_tab[kCodes][8];
+struct EncodeJob {
+  const uint4* w;
+  int64_t nblocks;
+  uint32_t* slot;   // the amax slot, S on return
+  int32_t* flag;    // nullable
+  uint2* codes;
+  uint8_t* scales;
+};
+
+// The encode pass as workgroup wg of nwg: S and the flag from the slot
+// (workgroup 0 stores them), the key table, then a grid-stride over the
+// 16-element blocks, two per thread per iteration (their four loads issued
+// together); blocks are contiguous in memory because k % 16 == 0.
+__device__ __forceinline__ void encode_body(const EncodeJob& j, int64_t wg, int64_t nwg,
+                                            int16_t (*key_tab)[8]) {
   bool nonfinite = false;
-  const float S = scale_from_slot(*slot, &nonfinite);
+  const float S = scale_from_slot(*j.slot, &nonfinite);
   build_keys(key_tab, (double)S);
   __syncthreads();
-  if (blockIdx.x == 0 && threadIdx.x == 0) {
-    *reinterpret_cast<float*>(slot) = S;
-    if (flag) *flag = nonfinite ? 1 : 0;
+  if (wg == 0 && threadIdx.x == 0) {
+    *reinterpret_cast<float*>(j.slot) = S;
+    if (j.flag) *j.flag = nonfinite ? 1 : 0;
   }
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  for (; b + stride < nblocks; b += 2 * stride) {
-    const uint4 lo0 = w[2 * b], hi0 = w[2 * b + 1];
-    const uint4 lo1 = w[2 * (b + stride)], hi1 = w[2 * (b + stride) + 1];
+  const int64_t stride = nwg * kThreads;
+  int64_t b = wg * kThreads + threadIdx.x;
+  for (; b + stride < j.nblocks; b += 2 * stride) {
+    const uint4 lo0 = j.w[2 * b], hi0 = j.w[2 * b + 1];
+    const uint4 lo1 = j.w[2 * (b + stride)], hi1 = j.w[2 * (b + stride) + 1];
     uint2 c0, c1;
     const uint32_t s0 = encode_block(lo0, hi0, S, key_tab, &c0);
     const uint32_t s1 = encode_block(lo1, hi1, S, key_tab, &c1);
-    codes[b] = c0;
-    scales[b] = (uint8_t)s0;
-    codes[b + stride] = c1;
-    scales[b + stride] = (uint8_t)s1;
+    j.codes[b] = c0;
+    j.scales[b] = (uint8_t)s0;
+    j.codes[b + stride] = c1;
+    j.scales[b + stride] = (uint8_t)s1;
   }
-  if (b < nblocks) {
+  if (b < j.nblocks) {
     uint2 c0;
-    const uint32_t s0 = encode_block(w[2 * b], w[2 * b + 1], S, key_tab, &c0);
-    codes[b] = c0;
-    scales[b] = (uint8_t)s0;
+    const uint32_t s0 = encode_block(j.w[2 * b], j.w[2 * b + 1], S, key_tab, &c0);
+    j.codes[b] = c0;
+    j.scales[b] = (uint8_t)s0;
   }
+}
+
+__global__ __launch_bounds__(kThreads) void qz_encode(EncodeJob j) {
+  __shared__ int16_t key_tab[kCodes][8];
+  encode_body(j, blockIdx.x, gridDim.x, key_tab);
+}
+
+// One launch of the batched quantizer: the encode pass of tensor i on
+// ewgs workgroups, the amax pass of tensor i + 1 on awgs workgroups (0 for
+// the last tensor), spread evenly through the grid so that the two run side
+// by side, and the reset of the slot of tensor i + 2 (nullable).  Tensor i
+// was read by its amax pass in the launch before, so its second read
+// mostly hits the last-level cache.
+__global__ __launch_bounds__(kThreads) void qz_pipe(EncodeJob e, int64_t ewgs, const uint4* aw,
+                                                    int64_t anvec, uint32_t* aslot, int64_t awgs,
+                                                    uint32_t* reset) {
+  __shared__ int16_t key_tab[kCodes][8];
+  if (reset && blockIdx.x == 0 && threadIdx.x == 0) *reset = kAmaxMark;
+  const int64_t G = ewgs + awgs, b = blockIdx.x;
+  const int64_t na0 = b * awgs / G, na1 = (b + 1) * awgs / G;   // amax workgroups before b, b + 1
+  if (na1 > na0) amax_body(aw, anvec, aslot, na0, awgs);
+  else encode_body(e, b - na0, ewgs, key_tab);
+}
+
+int64_t amax_wgs(int64_t nvec) {
+  return std::max<int64_t>(1, std::min<int64_t>((nvec + kThreads - 1) / kThreads,
+                                                (int64_t)device_cu_count()));
+}
+
+// Enough encode workgroups to fill the chip a few times over; each builds
+// its key table once and then loops over its blocks.
+int64_t encode_wgs(int64_t nblocks) {
+  return std::max<int64_t>(1, std::min<int64_t>((nblocks + kThreads - 1) / kThreads,
+                                                (int64_t)device_cu_count() * 4));
+}
+
+EncodeJob encode_job(const uint16_t* w, int64_t n, int64_t k, uint8_t* codes, uint8_t* scales,
+                     float* gscale, int32_t* flag) {
+  EncodeJob j;
+  j.w = reinterpret_cast<const uint4*>(w);
+  j.nblocks = n * k / 16;
+  j.slot = reinterpret_cast<uint32_t*>(gscale);
+  j.flag = flag;
+  j.codes = reinterpret_cast<uint2*>(codes);
+  j.scales = scales;
+  return j;
 }
 
 }  // namespace
@@ -232,20 +295,38 @@ hipError_t launch_quantize(const uint16_t* w, int64_t n, int64_t k,
                            int32_t* flag, hipStream_t stream) {
   uint32_t* slot = reinterpret_cast<uint32_t*>(gscale);
   const int64_t nvec = n * k / 8;
-  const int64_t nblocks = n * k / 16;
-  hipLaunchKernelGGL(qz_reset, dim3(1), dim3(1), 0, stream, slot);
-  const int64_t grid =
-      std::max<int64_t>(1, std::min<int64_t>((nvec + kAmaxThreads - 1) / kAmaxThreads,
-                                             (int64_t)device_cu_count()));
-  hipLaunchKernelGGL(qz_amax, dim3((unsigned)grid), dim3(kAmaxThreads), 0, stream,
+  hipLaunchKernelGGL(qz_reset, dim3(1), dim3(1), 0, stream, slot, nullptr);
+  hipLaunchKernelGGL(qz_amax, dim3((unsigned)amax_wgs(nvec)), dim3(kThreads), 0, stream,
                      reinterpret_cast<const uint4*>(w), nvec, slot);
-  // Enough workgroups to fill the chip a few times over; each builds its
-  // key table once and then loops over its blocks.
-  const int64_t eg = std::min<int64_t>((nblocks + 255) / 256, (int64_t)device_cu_count() * 8);
-  hipLaunchKernelGGL(qz_encode, dim3((unsigned)eg), dim3(256), 0, stream,
-                     reinterpret_cast<const uint4*>(w), nblocks, slot, flag,
-                     reinterpret_cast<uint2*>(codes), scales);
+  const EncodeJob j = encode_job(w, n, k, codes, scales, gscale, flag);
+  hipLaunchKernelGGL(qz_encode, dim3((unsigned)encode_wgs(j.nblocks)), dim3(kThreads), 0, stream,
+                     j);
   return hipGetLastError();
+}
+
+hipError_t launch_quantize_batch(int count, const uint16_t* const* w, const int64_t* n,
+                                 const int64_t* k, uint8_t* const* codes, uint8_t* const* scales,
+                                 float* const* gscale, int32_t* const* flag, hipStream_t stream) {
+  auto slot = [&](int i) { return reinterpret_cast<uint32_t*>(gscale[i]); };
+  auto nvec = [&](int i) { return n[i] * k[i] / 8; };
+  hipLaunchKernelGGL(qz_reset, dim3(1), dim3(1), 0, stream, slot(0),
+                     count > 1 ? slot(1) : nullptr);
+  hipLaunchKernelGGL(qz_amax, dim3((unsigned)amax_wgs(nvec(0))), dim3(kThreads), 0, stream,
+                     reinterpret_cast<const uint4*>(w[0]), nvec(0), slot(0));
+  for (int i = 0; i < count; ++i) {
+    const EncodeJob e = encode_job(w[i], n[i], k[i], codes[i], scales[i], gscale[i],
+                                   flag ? flag[i] : nullptr);
+    const int64_t ewgs = encode_wgs(e.nblocks);
+    const bool next = i + 1 < count;
+    const int64_t awgs = next ? amax_wgs(nvec(i + 1)) : 0;
+    hipLaunchKernelGGL(qz_pipe, dim3((unsigned)(ewgs + awgs)), dim3(kThreads), 0, stream, e, ewgs,
+                       next ? reinterpret_cast<const uint4*>(w[i + 1]) : nullptr,
+                       next ? nvec(i + 1) : 0, next ? slot(i + 1) : nullptr, awgs,
+                       i + 2 < count ? slot(i + 2) : nullptr);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  return hipSuccess;
 }
 
 }  // namespace qerl

@@ -42,7 +42,7 @@ def test_status_strings():
     for s in range(7):
         assert lib.qerl_status_string(s).decode().startswith("QERL_")
     assert b"unknown" in lib.qerl_status_string(99)
-    assert lib.qerl_abi_version() == 10
+    assert lib.qerl_abi_version() == 11
 
 
 FAKE = ctypes.c_void_p(0x10000)        # aligned, never dereferenced on error
@@ -58,6 +58,25 @@ def test_quantize_validation():
     assert f(FAKE, 4, 0, FAKE, FAKE, FAKE, None, None) == 2
     assert f(MIS, 4, 32, FAKE, FAKE, FAKE, None, None) == 3
     assert f(FAKE, 4, 32, MIS, FAKE, FAKE, None, None) == 3
+
+
+def test_quantize_batch_validation():
+    f = lib.qerl_quantize_nvfp4_batch
+    P = lambda *xs: ctypes.cast((ctypes.c_void_p * len(xs))(*[x.value if x else None for x in xs]),
+                                ctypes.c_void_p)
+    I = lambda *xs: ctypes.cast((ctypes.c_int64 * len(xs))(*xs), ctypes.c_void_p)
+    ok = (P(FAKE, FAKE), I(4, 8), I(32, 64), P(FAKE, FAKE), P(FAKE, FAKE), P(FAKE, FAKE))
+    assert f(0, *ok, None, None) == 2
+    assert f(-1, *ok, None, None) == 2
+    assert f(2, None, *ok[1:], None, None) == 1
+    assert f(2, ok[0], ok[1], ok[2], ok[3], ok[4], None, None, None) == 1
+    # the second tensor is bad: nothing is launched, the status names it
+    assert f(2, P(FAKE, None), *ok[1:], None, None) == 1
+    assert f(2, ok[0], I(4, 0), *ok[2:], None, None) == 2
+    assert f(2, ok[0], ok[1], I(32, 40), *ok[3:], None, None) == 2
+    assert f(2, P(FAKE, MIS), *ok[1:], None, None) == 3
+    assert f(2, *ok[:3], P(FAKE, MIS), *ok[4:], None, None) == 3
+    assert f(2, *ok, P(None, ctypes.c_void_p(0x10002)), None) == 3   # flags need 4 bytes
 
 
 def test_sigma_matches_oracle_and_validates():

@@ -119,3 +119,47 @@ def test_full_size_sampled_rows(name, idx):
     rc, rs = nvfp4.encode_with_scale(wf[rows], rS)
     assert np.array_equal(s[rows], rs)
     assert np.array_equal(c[rows], rc)
+
+
+def test_batch_matches_single_calls():
+    """qerl_quantize_nvfp4_batch: every tensor bit-identical to its own call
+    (and to the oracle), across tensors of very different sizes, a zero
+    tensor, a subnormal-S tensor and a non-finite one (its flag alone set)."""
+    shapes = [(1, 16), (3, 48), (512, 256), (1024, 5120), (2, 32), (37, 80), (2, 32),
+              (4608, 3584), (8, 64)]
+    ws = [weight_bf16(n, k, 0.02, 200 + i, outlier_frac=1e-3) for i, (n, k) in enumerate(shapes)]
+    ws[4] = np.zeros((2, 32), dtype=np.uint16)
+    ws[6] = np.full((2, 32), 0x0080, dtype=np.uint16)
+    ws[8] = ws[8].copy()
+    ws[8][3, 9] = 0x7F80
+    outs = q.qerl_quantize_nvfp4_batch([dev16(w) for w in ws])
+    torch.cuda.synchronize()
+    for i, w in enumerate(ws):
+        c, s, S, flag = (host(t) for t in outs[i])
+        c1, s1, S1, flag1 = gpu_quantize(w)
+        assert int(flag[0]) == flag1 == (1 if i == 8 else 0), i
+        if i == 8:
+            continue
+        assert np.float32(S[0]).view(np.uint32) == np.float32(S1).view(np.uint32), i
+        assert np.array_equal(s, s1) and np.array_equal(c, c1), i
+        if w.size <= 512 * 256:
+            rc, rs, rS = nvfp4.quantize(w)
+            assert np.float32(S[0]).view(np.uint32) == np.float32(rS).view(np.uint32), i
+            assert np.array_equal(s, rs) and np.array_equal(c, rc), i
+
+
+def test_batch_single_tensor_and_reuse():
+    w = weight_bf16(256, 512, 0.02, 7)
+    (c, s, S, flag), = q.qerl_quantize_nvfp4_batch([dev16(w)])
+    rc, rs, rS = nvfp4.quantize(w)
+    assert int(host(flag)[0]) == 0
+    assert np.float32(host(S)[0]).view(np.uint32) == np.float32(rS).view(np.uint32)
+    assert np.array_equal(host(s), rs) and np.array_equal(host(c), rc)
+    # the same outputs again, through a bound call (slots hold S from before)
+    ws = [dev16(weight_bf16(64, 128, 0.02, 8)), dev16(w)]
+    outs = q.qerl_quantize_nvfp4_batch(ws)
+    call = q.bind_quantize_nvfp4_batch(ws, outs)
+    for _ in range(2):
+        call()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(outs[1][0]), rc) and np.array_equal(host(outs[1][1]), rs)
