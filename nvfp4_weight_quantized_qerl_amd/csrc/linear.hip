@@ -95,14 +95,30 @@ void plan_decode(LinearPlan* p, int mt) {
 }
 
 // Single-pass 128-token contraction: 256 weight rows per workgroup; K is
-// split across workgroups when the row groups alone leave CUs idle (at
-// least two 128-wide blocks per split).
+// split across workgroups when the row groups alone leave CUs idle (one
+// round of workgroups, at least two 128-wide blocks per split).  The split
+// count minimises a cost fitted to whole calls on the 32B shapes at 128
+// tokens (qkv 7168 x 5120, o 5120 x 5120, down 5120 x 27648; splits 2-12):
+// about 1.16 us per K block of the longest split, plus 0.215 us per split
+// and 1000 output columns for writing and summing the fp32 partials, plus
+// one more launch (the finish) when K is split.
 void plan_m128(LinearPlan* p) {
   const int cu = device_cu_count();
   const int64_t groups = cdiv(p->n, 256);
   const int64_t nblocks = p->k / 128;
   int64_t split = 1;
-  if (groups * 4 < cu * 3) split = std::max<int64_t>(1, std::min<int64_t>(cu / groups, nblocks / 2));
+  if (groups * 4 < cu * 3) {
+    const int64_t smax = std::max<int64_t>(1, std::min<int64_t>(cu / groups, nblocks / 2));
+    double best = 0.0;
+    for (int64_t s = 1; s <= smax; ++s) {
+      const double cost = 1.16 * (double)cdiv(nblocks, s) + 0.215e-3 * (double)(s * p->n) +
+                          (s > 1 ? 4.0 : 0.0);
+      if (s == 1 || cost < best) {
+        best = cost;
+        split = s;
+      }
+    }
+  }
   p->m128 = true;
   p->m128_groups = (int)groups;
   p->m128_split = (int)split;
