@@ -169,9 +169,11 @@ def gpu_clock():
     return None
 
 
-# Sources of the decode contraction kernels; a committed counter summary is
-# only used while their digest is unchanged.
-DECODE_SOURCES = ("decode_lds.h", "decode_m128.h", "qerl_device.h", "decode.hip")
+# Sources of each decode contraction kernel and its launch; a committed
+# counter summary is only used while their digest is unchanged.
+M128_SOURCES = ("decode_m128.h", "decode_m128.hip", "qerl_device.h", "decode.hip")
+LDS_SOURCES = ("decode_lds.h", "decode_lds_mt1.hip", "decode_lds_mt2.hip", "qerl_device.h",
+               "decode.hip")
 
 
 def source_digest(*names):
@@ -352,7 +354,7 @@ def run_sweep(q, args, dev, stream):
     kbytes = main_kernel_bytes(cfg.m, s.n, s.k, cfg.r)
     # the same contraction on the standard (row-major) layout of one layer
     std = stats_ms(batch_times(lambda i: sw.gate_up_std(), stream, batches=5, per_batch=10))
-    digest = source_digest(*DECODE_SOURCES)
+    digest = source_digest(*M128_SOURCES)
     roofline = {"bound": "mfma", "achieved": round(kflops / avg_s / 1e12, 1),
                 "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(kflops / avg_s / 1e12 / BF16_PEAK_TFLOPS, 4),
@@ -543,7 +545,7 @@ def run_decode7b(q, args, dev, stream, to_dev):
     out["gate_up_kernel"] = {
         "bound": "hbm", "achieved": round(kbytes / avg_s / 1e9, 1), "peak": HBM_PEAK_GBS,
         "unit": "GB/s", "frac": round(kbytes / avg_s / 1e9 / HBM_PEAK_GBS, 4),
-        "traffic": measured_traffic("decode_main_gate_up_7b", source_digest(*DECODE_SOURCES)),
+        "traffic": measured_traffic("decode_main_gate_up_7b", source_digest(*LDS_SOURCES)),
         "kernel": "decode_lds<2,5> (gate/up 37888x3584, M=64, r=32)",
         "avg_launch_us": round(avg_s * 1e6, 2),
         "median_launch_us": round(ks["median_ms"] * 1e3, 2),

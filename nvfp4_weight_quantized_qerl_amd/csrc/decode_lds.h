@@ -195,7 +195,12 @@ __global__ __launch_bounds__(512, 1) void decode_lds(Args a) {
   const uint32_t kbytes = (uint32_t)(a.k / 2), kscales = (uint32_t)(a.k / 16);
   const uint32_t xrow = (uint32_t)a.k * 2;
   const __amdgpu_buffer_rsrc_t rw = rsrc(a.codes + row0 * kbytes, (uint32_t)((a.n - row0) * kbytes));
-  const __amdgpu_buffer_rsrc_t rs = rsrc(a.scales + row0 * kscales, (uint32_t)((a.n - row0) * kscales));
+  // The scale copies cover 256 rows per block (64 per wave); only the
+  // WROWS rows of this workgroup are in range, so the others read zeros
+  // without fetching the next workgroups' scales.
+  const __amdgpu_buffer_rsrc_t rs =
+      rsrc(a.scales + row0 * kscales,
+           (uint32_t)(min(a.n - row0, (int64_t)WROWS) * kscales));
   const __amdgpu_buffer_rsrc_t rx = rsrc(a.xt, (uint32_t)XROWS * xrow);
 
   // Copies are issued by waves 0..3 (see the file comment for the layout).

@@ -127,16 +127,17 @@ def test_zero_weight_gives_lora_only():
 
 
 @pytest.mark.parametrize("m,n,k,r", [
-    (64, 96, 8192, 32),      # K split: the finishing kernel forms t from the partials
-    (32, 16384, 512, 8),     # unsplit: the contraction kernel forms t
+    (64, 96, 8192, 32),      # K split: the finishing kernel applies S and t B^T
+    (32, 16384, 512, 8),     # unsplit: the contraction kernel's own epilogue
     (50, 16384, 256, 16),    # ragged m, unsplit
-    (128, 96, 2048, 40),     # two 64-row chunks, r not a multiple of 16 or 32
+    (128, 96, 2048, 40),     # the 128-token kernel, r not a multiple of 16 or 32
     (3, 96, 768, 8),         # one 32-row tile
 ])
 def test_deterministic_and_prepared_halves(m, n, k, r):
-    # The whole call forms t inside the contraction (or the split-K finish)
-    # from the chunk partials; the prepared halves reduce it in a separate
-    # kernel first.  Both sum in the same order: the outputs are identical.
+    # The whole call and its two halves run the same kernels (prepare with
+    # its LoRA-down reduction, then the contraction and, when K is split,
+    # the finish): repeated calls, and repeated contractions from one
+    # prepared workspace, must give the same bits.
     L = make_layer(m, n, k, r, seed=23, stage=1)
     g = GpuLayer(L)
     y1, y2 = g.run(), g.run()
