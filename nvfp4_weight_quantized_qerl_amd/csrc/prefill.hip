@@ -20,8 +20,10 @@ struct TileConfig {
                     // Qwen2.5-7B qkv and down shapes
 };
 
-// Candidate tiles: (waves M x N, wave tile WM x WN, waves per SIMD).  Each
-// compiles without register spills in the main loop.
+// Candidate tiles: (waves M x N, wave tile WM x WN, waves per SIMD).  None
+// spills inside its main loop: the 256 x 256 tile keeps one 8-byte value in
+// scratch (12 bytes per lane), stored once before the K loop and reloaded
+// once after it; the other two use no scratch.
 const TileConfig kConfigs[] = {
     {256, 256, prefill::gemm<2, 4, 128, 64, 2>, 512, 1, 550},
     {256, 192, prefill::gemm<2, 2, 128, 96, 1>, 256, 1, 430},
