@@ -446,6 +446,18 @@ QERL_API qerl_status qerl_linear_prefill_prepared(
     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * qerl_nvfp4_check_pow2_scales -- *flag = 1 if any block scale of an NVFP4
+ * weight is neither zero nor a positive power of two (the condition of
+ * qerl_linear_decode_mxfp4 below), else 0.  A one-time check for a weight
+ * that is to run on that path; qerl_mxfp4_to_nvfp4 output always passes.
+ *   scales   device, [n, k/16] E4M3 bytes; n >= 1, k >= 16, k % 16 == 0
+ *   flag     device out, 4-byte aligned, written by the call
+ * Two kernels are enqueued (clear the flag, scan the scales).
+ */
+QERL_API qerl_status qerl_nvfp4_check_pow2_scales(const void* scales, int64_t n, int64_t k,
+                                                  int32_t* flag, void* stream);
+
+/*
  * qerl_linear_decode_mxfp4 / qerl_linear_decode_prepared_mxfp4 -- the
  * same operations and arguments as qerl_linear_decode /
  * qerl_linear_decode_prepared, for an MXFP4 weight in the NVFP4 layout
@@ -453,7 +465,8 @@ QERL_API qerl_status qerl_linear_prefill_prepared(
  * lets the decode kernel form each pair of bf16 weight values with one
  * scaled-conversion instruction.  The result is bit-identical to the
  * general call on the same arguments; block scales that are not powers of
- * two give wrong results.
+ * two give wrong results (qerl_nvfp4_check_pow2_scales tells which weights
+ * qualify).
  */
 QERL_API qerl_status qerl_linear_decode_mxfp4(const void* x, int64_t m, const void* codes,
                                               const void* scales, const float* gscale,

@@ -519,6 +519,18 @@ def qerl_mxfp4_to_nvfp4(codes, scales_e8m0):
     return s4, g, flag
 
 
+def qerl_nvfp4_check_pow2_scales(scales, k):
+    """int32 [1] flag on the device: 1 if any block scale of the NVFP4 weight
+    (E4M3 bytes [n, k/16]) is neither zero nor a power of two (the weight then
+    must not run through qerl_linear_decode_mxfp4), else 0."""
+    n = scales.shape[0]
+    _need(scales, "scales", torch.uint8, (n, k // 16), scales.device)
+    flag = torch.empty(1, dtype=torch.int32, device=scales.device)
+    _check(lib.qerl_nvfp4_check_pow2_scales(_ptr(scales), n, k, _ptr(flag), _stream(scales.device)),
+           "qerl_nvfp4_check_pow2_scales")
+    return flag
+
+
 def qerl_linear_decode_mxfp4(x, codes, scales, gscale, lora_a=None, lora_b=None, lora_scale=0.0,
                              z=None, workspace=None, y=None):
     """qerl_linear_decode for an MXFP4 weight in the NVFP4 layout (power-of-two

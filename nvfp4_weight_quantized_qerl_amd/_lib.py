@@ -20,6 +20,7 @@ SIGNATURES = {
                                                  c_vp]),
     "qerl_quantize_mxfp4": (ctypes.c_int, [c_vp, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp]),
     "qerl_mxfp4_to_nvfp4": (ctypes.c_int, [c_vp, c_vp, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp]),
+    "qerl_nvfp4_check_pow2_scales": (ctypes.c_int, [c_vp, c_i64, c_i64, c_vp, c_vp]),
     "qerl_aqn_sigma": (ctypes.c_int, [c_f64, c_f64, c_i32, c_i32, ctypes.POINTER(c_f64)]),
     "qerl_aqn_sigma_schedule": (ctypes.c_int, [c_i32, c_f64, c_f64, c_i32, c_i32,
                                                 ctypes.POINTER(c_f64)]),

@@ -56,7 +56,7 @@ const char* qerl_status_string(int status) {
   }
 }
 
-int qerl_abi_version(void) { return 11; }
+int qerl_abi_version(void) { return 12; }
 
 qerl_status qerl_quantize_nvfp4(const void* w_bf16, int64_t n, int64_t k, void* codes,
                                 void* scales, float* gscale, int32_t* nonfinite_flag,
@@ -363,6 +363,15 @@ qerl_status qerl_linear_prefill_prepared(int64_t m, const void* codes, const voi
                                          void* stream) {
   return linear_prepared(true, m, codes, scales, gscale, n, k, lora_b, r, y, workspace,
                          workspace_bytes, stream);
+}
+
+qerl_status qerl_nvfp4_check_pow2_scales(const void* scales, int64_t n, int64_t k,
+                                         int32_t* flag, void* stream) {
+  if (!scales || !flag) return QERL_ERR_NULL;
+  if (n < 1 || k < 16 || k % 16) return QERL_ERR_SHAPE;
+  if (!aligned(flag, 4)) return QERL_ERR_ALIGN;
+  return from_hip(qerl::launch_check_pow2_scales(static_cast<const uint8_t*>(scales), n, k, flag,
+                                                 static_cast<hipStream_t>(stream)));
 }
 
 qerl_status qerl_linear_decode_mxfp4(const void* x, int64_t m, const void* codes,

@@ -115,6 +115,27 @@ __global__ void mx_scale(uint32_t* slot) {
   *reinterpret_cast<float*>(slot) = ldexpf(1.0f, e);
 }
 
+// Non-power-of-two check of NVFP4 block scales (E4M3 bytes), 16 per thread:
+// a byte is zero or a power of two when its mantissa is 0 (normal) or a
+// single set bit with exponent field 0 (subnormal m 2^-9, m = 1, 2 or 4),
+// and its sign is clear; NaN (0x7f) is neither.
+__global__ __launch_bounds__(256) void pow2_check(const uint8_t* __restrict__ scales,
+                                                  int64_t nbytes, int32_t* __restrict__ flag) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  bool bad = false;
+  for (int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 16; i < nbytes;
+       i += 16 * stride) {
+    const int64_t cnt = min<int64_t>(16, nbytes - i);
+    for (int64_t j = 0; j < cnt; ++j) {
+      const uint32_t b = scales[i + j];
+      const uint32_t e = (b >> 3) & 0xfu, m = b & 7u;
+      const bool ok = !(b & 0x80u) && b != 0x7fu && (e ? m == 0u : (m & (m - 1u)) == 0u);
+      bad = bad || !ok;
+    }
+  }
+  if (bad) atomicOr(flag, 1);
+}
+
 }  // namespace
 
 hipError_t launch_quantize_mxfp4(const uint16_t* w, int64_t n, int64_t k, uint8_t* codes,
@@ -138,6 +159,17 @@ hipError_t launch_mxfp4_to_nvfp4(const uint8_t* codes, const uint8_t* s8, int64_
   hipLaunchKernelGGL(mx_to_nv, dim3((unsigned)((n16 + 255) / 256)), dim3(256), 0, stream, codes,
                      s8, n16, (const uint32_t*)slot, s4, flag);
   hipLaunchKernelGGL(mx_scale, dim3(1), dim3(1), 0, stream, slot);
+  return hipGetLastError();
+}
+
+hipError_t launch_check_pow2_scales(const uint8_t* scales, int64_t n, int64_t k, int32_t* flag,
+                                   hipStream_t stream) {
+  const int64_t nbytes = n * (k / 16);
+  hipLaunchKernelGGL(mx_flag_reset, dim3(1), dim3(1), 0, stream, flag);
+  const int64_t grid =
+      std::max<int64_t>(1, std::min<int64_t>((nbytes + 16 * 256 - 1) / (16 * 256),
+                                             (int64_t)device_cu_count() * 4));
+  hipLaunchKernelGGL(pow2_check, dim3((unsigned)grid), dim3(256), 0, stream, scales, nbytes, flag);
   return hipGetLastError();
 }
 

@@ -28,6 +28,10 @@ hipError_t launch_quantize_mxfp4(const uint16_t* w, int64_t n, int64_t k, uint8_
                                  uint8_t* scales, int32_t* flag, hipStream_t stream);
 hipError_t launch_mxfp4_to_nvfp4(const uint8_t* codes, const uint8_t* s8, int64_t n, int64_t k,
                                  uint8_t* s4, float* gscale, int32_t* flag, hipStream_t stream);
+// flag <- 1 if any NVFP4 block scale of [n, k/16] is not zero or a power of
+// two (the condition of the power-of-two decode path), else 0.
+hipError_t launch_check_pow2_scales(const uint8_t* scales, int64_t n, int64_t k, int32_t* flag,
+                                   hipStream_t stream);
 
 // -------------------------------------------------------------------- noise
 // `count` vectors of length d, vector v with call id call0 + v * call_step

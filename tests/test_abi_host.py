@@ -42,7 +42,7 @@ def test_status_strings():
     for s in range(7):
         assert lib.qerl_status_string(s).decode().startswith("QERL_")
     assert b"unknown" in lib.qerl_status_string(99)
-    assert lib.qerl_abi_version() == 11
+    assert lib.qerl_abi_version() == 12
 
 
 FAKE = ctypes.c_void_p(0x10000)        # aligned, never dereferenced on error
@@ -175,6 +175,15 @@ def test_backward_validation_and_workspace():
     assert call(a10=129) == 4 and call(a11=float("nan")) == 4
     assert call(a0=MIS) == 3 and call(a7=MIS) == 3 and call(a16=MIS) == 3
     assert call(a17=16) == 5
+
+
+def test_pow2_check_validation():
+    f = lib.qerl_nvfp4_check_pow2_scales
+    assert f(None, 4, 32, FAKE, None) == 1
+    assert f(FAKE, 4, 32, None, None) == 1
+    assert f(FAKE, 0, 32, FAKE, None) == 2
+    assert f(FAKE, 4, 24, FAKE, None) == 2
+    assert f(FAKE, 4, 32, ctypes.c_void_p(0x10002), None) == 3
 
 
 def test_mxfp4_validation():

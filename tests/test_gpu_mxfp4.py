@@ -99,3 +99,38 @@ def test_power_of_two_decode_is_bit_identical(m, n, k, r):
     y1 = q.qerl_linear_decode_mxfp4(*args)
     torch.cuda.synchronize()
     assert torch.equal(y0.view(torch.int16), y1.view(torch.int16))
+
+
+def _pow2_or_zero(b):
+    """From the E4M3 decode table: zero, or a positive power of two."""
+    if b & 0x80 or (b & 0x7F) == 0x7F:      # negative, or NaN
+        return False
+    v = formats.E4M3_VALUES[b & 0x7F]
+    return v == 0.0 or float(np.log2(v)).is_integer()
+
+
+def test_pow2_scale_check_every_byte():
+    bad_bytes = 0
+    for b in range(256):
+        scales = torch.full((1, 1), b, dtype=torch.uint8, device="cuda:0")
+        flag = q.qerl_nvfp4_check_pow2_scales(scales, 16)
+        want = 0 if _pow2_or_zero(b) else 1
+        bad_bytes += want
+        assert int(flag.item()) == want, b
+    assert 0 < bad_bytes < 256
+
+
+def test_pow2_scale_check_on_weights():
+    w = weight_bf16(96, 512, 0.02, seed=43, outlier_frac=0.01)
+    codes, scales, _ = q.qerl_quantize_mxfp4(dev16(w))
+    s4, _, rflag = q.qerl_mxfp4_to_nvfp4(codes, scales)
+    assert int(q.qerl_nvfp4_check_pow2_scales(s4, 512).item()) == 0
+    _, nv_scales, _, _ = q.qerl_quantize_nvfp4(dev16(w))
+    want = 0 if all(_pow2_or_zero(int(b)) for b in host(nv_scales).ravel()) else 1
+    assert want == 1
+    assert int(q.qerl_nvfp4_check_pow2_scales(nv_scales, 512).item()) == want
+    # one bad byte in a large tensor, at its very end
+    big = torch.zeros((3000, 4096 // 16), dtype=torch.uint8, device="cuda:0")
+    assert int(q.qerl_nvfp4_check_pow2_scales(big, 4096).item()) == 0
+    big[-1, -1] = 0x39          # 1.125 * 2^0
+    assert int(q.qerl_nvfp4_check_pow2_scales(big, 4096).item()) == 1
