@@ -352,11 +352,13 @@ __global__ __launch_bounds__(256, 1) void decode_main(DecodeArgs a) {
 
 typedef void (*DecodeKernel)(DecodeArgs);
 
-// decode_main<MT, NT> if its accumulators fit (NT * MT <= 12 tiles of
-// 32 x 32), else null.
+// decode_main<MT, NT> if it holds its accumulators and operands in
+// registers without spilling (NT <= 6, 5 and 2 for MT = 1, 2 and 4, the
+// limits the planner keeps to; the compiler's resource report shows scratch
+// at MT = 2, NT = 6 and MT = 4, NT = 3), else null.
 template <int MT, int NT>
 DecodeKernel kernel_or_null() {
-  if constexpr (NT * MT <= 12 && NT >= 1) {
+  if constexpr (NT >= 1 && NT <= (MT == 1 ? 6 : (MT == 2 ? 5 : 2))) {
     return decode_main<MT, NT>;
   } else {
     return nullptr;
