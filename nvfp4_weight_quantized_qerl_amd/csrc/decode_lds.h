@@ -24,7 +24,9 @@
 // finished block i-1), the copying waves issue the copies of x_t(i+1) and
 // weights(i+2) into the stages block i-1 used, then block i is computed.
 // The raw s_barrier is used instead of __syncthreads, whose memory fence
-// would wait for every copy in flight.
+// would wait for every copy in flight.  The wait's count (the W_PER_WAVE
+// weight copies of block i+1 may be outstanding) needs the x_t copies of a
+// block issued before its weight copies; scheduling barriers keep them so.
 //
 // Waves.  Eight waves, two per SIMD so that one wave's LDS and VALU
 // latencies are covered by the other's MFMAs: wave w takes K quarter w % 4
@@ -283,8 +285,11 @@ __global__ __launch_bounds__(512, 1) void decode_lds(Args a) {
     const int64_t last = be - 1;
     if (hf == 0) {
       copy_w(bb, wc0, sc0);
+      __builtin_amdgcn_sched_barrier(0);
       copy_x(bb, xs0);
+      __builtin_amdgcn_sched_barrier(0);
       copy_w(min(bb + 1, last), wc1, sc1);
+      __builtin_amdgcn_sched_barrier(0);
     }
     // Block bb + i uses weight stage i % 3 and x_t stage i % 2; period 6.
 #define QERL_LDS_STEP(OFF, WC, SC, XS, XN, WN, SN)                         \
@@ -292,7 +297,9 @@ __global__ __launch_bounds__(512, 1) void decode_lds(Args a) {
   barrier_nofence();                                                        \
   if (hf == 0) {                                                            \
     copy_x(min(blk + (OFF) + 1, last), XN);                                 \
+    __builtin_amdgcn_sched_barrier(0);                                      \
     copy_w(min(blk + (OFF) + 2, last), WN, SN);                             \
+    __builtin_amdgcn_sched_barrier(0);                                      \
   }                                                                         \
   compute_half(WC, SC, XS);                                                 \
   if (blk + (OFF) + 1 >= be) break;

@@ -32,13 +32,14 @@
 // carries which channel, only that A and B agree), which makes the codes
 // of a lane contiguous.
 //
-// Pipeline.  x_t is double-buffered in LDS, the weights held in four
-// register sets (two blocks in flight, one in use).  Iteration i: wait for x_t(i) and W(i) (s_waitcnt with W(i+1)
-// still in flight), s_barrier (every wave's copies of x_t(i) have landed
-// and every wave is done with block i-1), issue the copies of x_t(i+1) and
-// the loads of W(i+2), compute block i.  A scheduling barrier after each
-// 16-deep step keeps the compiler from hoisting the operand reads of later
-// steps, which would run out of registers.
+// Pipeline.  x_t has four LDS stages and the weights four register sets;
+// both run two blocks ahead.  Block i: issue the copies of x_t(i+2) and
+// the loads of W(i+2); steps 0-1; wait for this wave's copies of x_t(i+1)
+// (s_waitcnt with the 12 later operations still in flight) and s_barrier
+// (every wave's copies of x_t(i+1) have landed and every wave is past
+// block i-1, whose stage the next block's copies overwrite); steps 2-3.
+// The operand reads and dequantization of each 16-deep step are
+// interleaved with the MFMAs of the previous one.
 //
 // When the weight rows are too few to fill the GPU, K is also split
 // across workgroups: each writes its fp32 partial tiles and a separate
@@ -273,7 +274,13 @@ __global__ __launch_bounds__(512, 1) void decode_m128(Args a) {
     // Block at offset OFF of a group of four: W = its weights, XS its stage,
     // XN the next block's stage and WN its weights, X2 / W2 / S2 the stage
     // and registers that receive the block two ahead.
-    //   top:        copies of x_t(i+2), loads of W(i+2)
+    //   top:        copies of x_t(i+2), then loads of W(i+2); the scheduling
+    //               barriers keep every copy ahead of every load, which the
+    //               count of the mid-block wait (12 = the 4 + 4 + 4 operations
+    //               issued after x_t(i+1)) relies on: with a load of W(i+1)
+    //               moved before a copy of x_t(i+1), fewer than 12 would
+    //               follow it and a wave could pass the barrier while its
+    //               copy is still in flight
     //   steps 0-1:  MFMAs of steps 0, 1 (reads and dequantization of 1, 2)
     //   mid-block:  wait for this wave's copies of x_t(i+1), s_barrier: every
     //               copy of x_t(i+1) has landed, and every wave is past block
@@ -282,7 +289,9 @@ __global__ __launch_bounds__(512, 1) void decode_m128(Args a) {
     //               and of the next block's step 0)
 #define QERL_M128_BLOCK(OFF, W, S, XS, XN, WN, SN, X2, W2, S2)            \
   copy_x(min(blk + (OFF) + 2, last), X2);                                 \
+  __builtin_amdgcn_sched_barrier(0);                                      \
   load_w(min(blk + (OFF) + 2, last), W2, S2);                             \
+  __builtin_amdgcn_sched_barrier(0);                                      \
   read_a(XS, 1, xa1);                                                     \
   dequant_b(W, S, 1, b1);                                                 \
   mfmas(xa0, b0);                                                         \
@@ -325,6 +334,19 @@ __global__ __launch_bounds__(512, 1) void decode_m128(Args a) {
       QERL_M128_BLOCK(2, w2, s2, xs2, xs3, w3, s3, xs0, w0, s0)
     }
 #undef QERL_M128_BLOCK
+    // An empty use of every weight register set: without it the compiler
+    // deletes the loads of the last blocks whose values are never used,
+    // and the mid-block waits, which count them, would then let the x_t
+    // copies they are meant to wait for still be in flight.
+    auto keep = [](const uint4 (&wv)[NTW], const uint32_t (&sv)[NTW])
+        __attribute__((always_inline)) {
+#pragma unroll
+      for (int t = 0; t < NTW; ++t) asm volatile("" ::"v"(wv[t].x), "v"(sv[t]));
+    };
+    keep(w0, s0);
+    keep(w1, s1);
+    keep(w2, s2);
+    keep(w3, s3);
   }
   wait_vmcnt<0>();
   __syncthreads();
