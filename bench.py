@@ -218,6 +218,22 @@ def dev_normal(shape, std, gen, dev):
             * std).to(torch.bfloat16)
 
 
+def library_bf16_gemm_ms(m, n, k, dev, stream, gen, iters=10):
+    """Median time (ms) of the vendor library's dense bf16 GEMM (torch.matmul,
+    hipBLASLt on this image) at the same shape: x [m, k] N(0, 1) times a
+    dense bf16 weight [k, n] N(0, 0.02^2), fp32 accumulation, no
+    dequantization, no LoRA and four times the weight bytes.  A reference
+    point for what a GEMM reaches on this machine with random data, not part of
+    the path."""
+    import torch
+    x = dev_normal((m, k), 1.0, gen, dev)
+    wt = dev_normal((k, n), 0.02, gen, dev)       # contiguous [k, n] right operand
+    y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+    st = stats_ms(event_times(lambda i: torch.matmul(x, wt, out=y), iters, stream))
+    del x, wt, y
+    return st["median_ms"]
+
+
 # ------------------------------------------------- headline: the 32B sweep
 class Sweep32:
     """The Qwen2.5-32B decode sweep (64 layers x 4 projections, M=128, r=64),
@@ -355,6 +371,9 @@ def run_sweep(q, args, dev, stream):
     # the same contraction on the standard (row-major) layout of one layer
     std = stats_ms(batch_times(lambda i: sw.gate_up_std(), stream, batches=5, per_batch=10))
     digest = source_digest(*M128_SOURCES)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(4900)
+    lib_ms = library_bf16_gemm_ms(cfg.m, s.n, s.k, dev, stream, gen, iters=50)
     roofline = {"bound": "mfma", "achieved": round(kflops / avg_s / 1e12, 1),
                 "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(kflops / avg_s / 1e12 / BF16_PEAK_TFLOPS, 4),
@@ -376,7 +395,11 @@ def run_sweep(q, args, dev, stream):
                 "GB_per_s": round(kbytes / avg_s / 1e9, 1),
                 "hbm_frac": round(kbytes / avg_s / 1e9 / HBM_PEAK_GBS, 4),
                 "roofline_us": round(max(kflops / BF16_PEAK_TFLOPS / 1e6,
-                                         kbytes / HBM_PEAK_GBS / 1e3), 2)}
+                                         kbytes / HBM_PEAK_GBS / 1e3), 2),
+                "library_bf16_gemm_us": round(lib_ms * 1e3, 2),
+                "library_bf16_gemm_note": "reference: torch.matmul (hipBLASLt) of the same "
+                                          "128 x 55296 x 5120 product with a dense bf16 weight "
+                                          "(4x the weight bytes, no LoRA), random data, same box"}
     roof_step_ms = max(sw.step_flops / BF16_PEAK_TFLOPS / 1e9, sw.step_bytes / HBM_PEAK_GBS / 1e6)
     head = {
         "value": round(sw.step_bytes / med_s / 1e9, 1),
@@ -824,7 +847,9 @@ def run_14b(q, args, dev, stream):
     gen = torch.Generator(device=dev)
     gen.manual_seed(5100)
     xs = {}
-    per_layer, t_tot, f_tot = [], 0.0, 0.0
+    lib_gen = torch.Generator(device=dev)
+    lib_gen.manual_seed(5200)
+    per_layer, t_tot, f_tot, lib_tot, lib_fl = [], 0.0, 0.0, 0.0, 0.0
     layer0 = {t["name"]: t for t in mdl.tensors if t["layer"] == 0}
     mdl.calls = None
     mdl.tensors = None
@@ -845,15 +870,24 @@ def run_14b(q, args, dev, stream):
                              y, entry="prefill")
         tt = stats_ms(event_times(lambda i: call(), 20, stream))
         fl = linear_flops(M, n, k, R)
+        del a, b, z, ws, y, call
+        lib_ms = library_bf16_gemm_ms(M, n, k, dev, stream, lib_gen)
         per_layer.append({"layer": f"{name} {n}x{k}", "ms": tt["median_ms"],
                           "p10_ms": tt["p10_ms"], "p90_ms": tt["p90_ms"],
-                          "tflops": round(fl / tt["median_ms"] / 1e9, 1)})
+                          "tflops": round(fl / tt["median_ms"] / 1e9, 1),
+                          "library_bf16_gemm_ms": lib_ms,
+                          "library_bf16_gemm_tflops": round(2.0 * M * n * k / lib_ms / 1e9, 1)})
         t_tot += tt["median_ms"]
         f_tot += fl
-        del a, b, z, ws, y, call
+        lib_tot += lib_ms
+        lib_fl += 2.0 * M * n * k
     out["prefill"] = {"tokens": M, "ms": round(t_tot, 4), "tflops": round(f_tot / t_tot / 1e9, 1),
                       "frac_bf16_peak": round(f_tot / t_tot / 1e9 / BF16_PEAK_TFLOPS, 4),
                       "roofline_ms": round(f_tot / BF16_PEAK_TFLOPS / 1e9, 4),
+                      "library_bf16_gemm_tflops": round(lib_fl / lib_tot / 1e9, 1),
+                      "library_bf16_gemm_note": "reference: torch.matmul (hipBLASLt) of the same "
+                                                "four products with dense bf16 weights (no "
+                                                "dequantization, no LoRA), random data, same box",
                       "layers": per_layer}
     del mdl, xs, layer0
     torch.cuda.synchronize()
