@@ -263,11 +263,16 @@ static qerl_status linear_full(bool prefill, const void* x, int64_t m, const voi
   s = check_prepare(x, r_eff ? lora_a : nullptr, r_eff);
   if (s != QERL_OK) return s;
   plan.pow2_scales = pow2;
+  // When the first contraction launch splits K, its extra workgroups sum the
+  // LoRA-down partials into t, which saves the reduction its own launch.
+  plan.t_in_contraction =
+      r_eff > 0 && (!prefill || plan.m <= 64) && qerl::t_reduce_can_merge(plan);
   hipStream_t st = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   hipError_t e = qerl::launch_linear_prepare(plan, static_cast<const uint16_t*>(x), z,
                                              static_cast<const uint16_t*>(lora_a),
-                                             lora_scale, ws, st, swiglu, true, z_rows);
+                                             lora_scale, ws, st, swiglu, true, z_rows,
+                                             !plan.t_in_contraction);
   if (e != hipSuccess) return QERL_ERR_HIP;
   const uint8_t* c = static_cast<const uint8_t*>(codes);
   const uint8_t* sc = static_cast<const uint8_t*>(scales);

@@ -168,13 +168,38 @@ hipError_t launch_finish(const LinearPlan& p, int split, int rows, int m_valid,
   return hipGetLastError();
 }
 
+// Workgroups appended to a split contraction launch of `wgs` workgroups to
+// sum the LoRA-down partials: up to 8, on CU slots the contraction leaves
+// free (one workgroup per CU: both kernels hold most of the LDS).
+int reduce_wgs(int wgs) {
+  return (int)std::max<int64_t>(0, std::min<int64_t>(8, (int64_t)device_cu_count() - wgs));
+}
+
+// Kernel of the chunk of a decode call that starts at token row m0: the
+// 128-token kernel, the LDS-staged one or the general one, with its K
+// split and token tiles.
+enum class ChunkKernel { kM128, kLds, kMain };
+struct ChunkChoice {
+  ChunkKernel kind;
+  int mt, split;
+};
+
+ChunkChoice choose_chunk(const LinearPlan& p, int64_t m0) {
+  const int64_t tiles_left = (p.mpad - m0) / 32;
+  if (p.m128 && (tiles_left >= 3 || p.tiled)) return {ChunkKernel::kM128, 4, p.m128_split};
+  int mt = p.dec_mt;
+  if (tiles_left < mt) mt = tiles_left >= 2 ? 2 : 1;
+  if (mt <= 2 && p.k % 256 == 0 && p.dec_nt <= 5) return {ChunkKernel::kLds, mt, lds_split(p)};
+  return {ChunkKernel::kMain, mt, p.dec_split};
+}
+
 // LDS-staged contraction (decode_lds.h) for one chunk of <= 64 rows, when
 // k is a multiple of 256.
 hipError_t run_decode_lds(const LinearPlan& p, int mt, const uint8_t* codes,
                           const uint8_t* scales, const float* gscale, const uint16_t* t,
                           const uint16_t* lora_b, int r, int lora_vec, const uint16_t* xt,
                           uint16_t* y, int m_valid, int64_t m0_chunk, char* ws,
-                          hipStream_t stream) {
+                          hipStream_t stream, const TReduceArgs* tr) {
   dlds::Kernel kern = mt == 1 ? dlds::pick_mt1(p.dec_nt, p.pow2_scales)
                               : dlds::pick_mt2(p.dec_nt, p.pow2_scales);
   if (!kern) return hipErrorInvalidConfiguration;
@@ -197,7 +222,11 @@ hipError_t run_decode_lds(const LinearPlan& p, int mt, const uint8_t* codes,
   a.r = r;
   a.rpad16 = p.rpad16;
   a.lora_vec = lora_vec;
-  hipLaunchKernelGGL(kern, dim3((unsigned)p.dec_groups, (unsigned)split), dim3(512), 0, stream, a);
+  a.groups = p.dec_groups;
+  a.tr_wgs = tr ? reduce_wgs(p.dec_groups * split) : 0;
+  a.tr = tr ? *tr : TReduceArgs{};
+  hipLaunchKernelGGL(kern, dim3((unsigned)(p.dec_groups * split + a.tr_wgs)), dim3(512), 0,
+                     stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || split == 1) return e;
   return launch_finish(p, split, 32 * mt, m_valid, a.ypart, gscale, t, lora_b, r, lora_vec, y,
@@ -209,7 +238,7 @@ hipError_t run_decode_lds(const LinearPlan& p, int mt, const uint8_t* codes,
 hipError_t run_decode_m128(const LinearPlan& p, const uint8_t* codes, const uint8_t* scales,
                            const float* gscale, const uint16_t* t, const uint16_t* lora_b, int r,
                            int lora_vec, const uint16_t* xt, uint16_t* y, int xrows, int m_valid,
-                           char* ws, hipStream_t stream) {
+                           char* ws, hipStream_t stream, const TReduceArgs* tr) {
   d128::Args a;
   a.xt = xt;
   a.codes = codes;
@@ -228,9 +257,12 @@ hipError_t run_decode_m128(const LinearPlan& p, const uint8_t* codes, const uint
   a.r = r;
   a.rpad16 = p.rpad16;
   a.lora_vec = lora_vec;
+  a.groups = p.m128_groups;
+  a.tr_wgs = tr ? reduce_wgs(p.m128_groups * a.split) : 0;
+  a.tr = tr ? *tr : TReduceArgs{};
   hipLaunchKernelGGL(d128::pick(p.pow2_scales, p.tiled),
-                     dim3((unsigned)p.m128_groups, (unsigned)a.split),
-                     dim3(512), 0, stream, a);
+                     dim3((unsigned)(p.m128_groups * a.split + a.tr_wgs)), dim3(512), 0, stream,
+                     a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.split == 1) return e;
   return launch_finish(p, a.split, (int)((xrows + 31) / 32 * 32), m_valid, a.ypart, gscale, t,
@@ -261,29 +293,39 @@ hipError_t run_decode_chunks(const LinearPlan& p, const uint8_t* codes,
   a.lora_vec = (a.r % 8 == 0) && ((reinterpret_cast<uintptr_t>(lora_b) & 15) == 0);
   const uint16_t* xt = reinterpret_cast<const uint16_t*>(ws + p.off_xt);
   const uint16_t* t = reinterpret_cast<const uint16_t*>(ws + p.off_t);
+  // The LoRA-down partials are summed into t by the first launch's extra
+  // workgroups when the prepare left that to it, else t is already there.
+  const TReduceArgs trs = treduce_args(p, ws);
+  const TReduceArgs* tr = (a.r > 0 && p.t_in_contraction) ? &trs : nullptr;
+  if (tr && !t_reduce_can_merge(p)) {
+    hipError_t e = launch_treduce(p, ws, stream);
+    if (e != hipSuccess) return e;
+    tr = nullptr;
+  }
   int64_t m0 = 0;
   while (m0 < p.m) {
-    const int64_t tiles_left = (p.mpad - m0) / 32;
-    if (p.m128 && (tiles_left >= 3 || p.tiled)) {
+    const ChunkChoice ch = choose_chunk(p, m0);
+    if (ch.kind == ChunkKernel::kM128) {
       const int xrows = (int)std::min<int64_t>(d128::kTokens, p.mpad - m0);
       const int m_valid = (int)std::min<int64_t>(d128::kTokens, p.m - m0);
       hipError_t e = run_decode_m128(p, codes, scales, gscale, t + m0 * p.rpad16, lora_b, a.r,
                                      a.lora_vec, xt + m0 * p.k, y + m0 * p.n, xrows, m_valid, ws,
-                                     stream);
+                                     stream, tr);
       if (e != hipSuccess) return e;
+      tr = nullptr;
       m0 += d128::kTokens;
       continue;
     }
-    int mt = p.dec_mt;
-    if (tiles_left < mt) mt = tiles_left >= 2 ? 2 : 1;
+    const int mt = ch.mt;
     a.xt = xt + m0 * p.k;
     a.t = t + m0 * p.rpad16;
     a.y = y + m0 * p.n;
     a.m_valid = (int)std::min<int64_t>(32 * mt, p.m - m0);
     hipError_t e;
-    if (mt <= 2 && p.k % 256 == 0 && p.dec_nt <= 5) {
+    if (ch.kind == ChunkKernel::kLds) {
       e = run_decode_lds(p, mt, codes, scales, gscale, a.t, lora_b, a.r, a.lora_vec, a.xt,
-                         a.y, a.m_valid, m0, ws, stream);
+                         a.y, a.m_valid, m0, ws, stream, tr);
+      tr = nullptr;
     } else {
       decode::DecodeKernel kern = pick_decode(mt, p.dec_nt);
       if (!kern) return hipErrorInvalidConfiguration;
@@ -298,6 +340,13 @@ hipError_t run_decode_chunks(const LinearPlan& p, const uint8_t* codes,
     m0 += 32 * mt;
   }
   return hipSuccess;
+}
+
+bool t_reduce_can_merge(const LinearPlan& p) {
+  const ChunkChoice ch = choose_chunk(p, 0);
+  if (ch.split < 2) return false;
+  const int groups = ch.kind == ChunkKernel::kM128 ? p.m128_groups : p.dec_groups;
+  return ch.kind != ChunkKernel::kMain && reduce_wgs(groups * ch.split) > 0;
 }
 
 hipError_t tile128(const uint8_t* codes, const uint8_t* scales, int64_t n, int64_t k,

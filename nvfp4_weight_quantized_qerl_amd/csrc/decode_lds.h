@@ -36,6 +36,7 @@
 #include <type_traits>
 
 #include "qerl_device.h"
+#include "treduce.h"
 
 namespace qerl {
 namespace dlds {
@@ -52,6 +53,11 @@ struct Args {
   int64_t n, k;
   int64_t nblocks;           // 256-wide K blocks (k / 256), spread evenly over the splits
   int m_valid, rows, split, r, rpad16, lora_vec;
+  // Grid: groups * split contraction workgroups (workgroup g + groups * s
+  // owns row group g and K split s), then tr_wgs workgroups that sum the
+  // LoRA-down partials into t (split > 1 only: the finish reads t).
+  int groups, tr_wgs;
+  TReduceArgs tr;
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
@@ -173,6 +179,12 @@ __global__ __launch_bounds__(512, 1) void decode_lds(Args a) {
   __shared__ __attribute__((aligned(16))) uint4 xs0[XROWS * 32], xs1[XROWS * 32];
   __shared__ __attribute__((aligned(16))) uint16_t t_lds[XROWS * 128];
 
+  const int bid = __builtin_amdgcn_readfirstlane((int)blockIdx.x);
+  if (bid >= a.groups * a.split) {
+    treduce_strided(a.tr, (int64_t)(bid - a.groups * a.split) * 512 + threadIdx.x,
+                    (int64_t)a.tr_wgs * 512);
+    return;
+  }
   const int lane = threadIdx.x & 63;
   // Wave-uniform values the compiler cannot prove uniform by itself.
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -180,15 +192,18 @@ __global__ __launch_bounds__(512, 1) void decode_lds(Args a) {
   const int hf = wave >> 2;                   // row half: subtiles [0, NT0) or [NT0, NT)
   const int tbase = hf ? NT0 : 0;
   const int h = lane >> 5, c = lane & 31;
-  const int64_t row0 = (int64_t)blockIdx.x * a.rows;
+  const int split_id = bid / a.groups;
+  const int64_t row0 = (int64_t)(bid - split_id * a.groups) * a.rows;
   const int64_t row_end = min(a.n, row0 + (int64_t)a.rows);
-  const int split_id = blockIdx.y;
   // Blocks [bb, be) of this split: the splits differ by at most one block.
   const int64_t bb = (int64_t)split_id * a.nblocks / a.split;
   const int64_t be = (int64_t)(split_id + 1) * a.nblocks / a.split;
 
   const float S = *a.gscale;     // first needed in the epilogue
-  if (a.r > 0) {
+  // t is read only by the unsplit epilogue (with K split the finishing
+  // kernel adds t B^T, and t may still be being summed by this launch's
+  // reduction workgroups).
+  if (a.r > 0 && a.split == 1) {
     const int words = XROWS * a.rpad16 / 8;
     for (int i = threadIdx.x; i < words; i += 512)
       reinterpret_cast<uint4*>(t_lds)[i] = reinterpret_cast<const uint4*>(a.t)[i];

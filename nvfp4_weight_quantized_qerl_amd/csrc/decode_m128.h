@@ -47,6 +47,7 @@
 #pragma once
 
 #include "qerl_device.h"
+#include "treduce.h"
 
 namespace qerl {
 namespace d128 {
@@ -79,6 +80,11 @@ struct Args {
   int64_t n, k;
   int64_t nblocks;         // k / 128, spread evenly over the splits
   int xrows, m_valid, split, r, rpad16, lora_vec;
+  // Grid: groups * split contraction workgroups (workgroup g + groups * s
+  // owns row group g and K split s), then tr_wgs workgroups that sum the
+  // LoRA-down partials into t (split > 1 only: the finish reads t).
+  int groups, tr_wgs;
+  TReduceArgs tr;
 };
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -146,12 +152,18 @@ __global__ __launch_bounds__(512, 1) void decode_m128(Args a) {
   __shared__ __attribute__((aligned(16))) uint4 xs0[kTokens * 16], xs1[kTokens * 16],
       xs2[kTokens * 16], xs3[kTokens * 16];
 
+  const int bid = __builtin_amdgcn_readfirstlane((int)blockIdx.x);
+  if (bid >= a.groups * a.split) {
+    treduce_strided(a.tr, (int64_t)(bid - a.groups * a.split) * 512 + threadIdx.x,
+                    (int64_t)a.tr_wgs * 512);
+    return;
+  }
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int kh = wave >> 2, rg = wave & 3;
   const int h = lane >> 5, c = lane & 31;
-  const int64_t row0 = (int64_t)blockIdx.x * kRows;
-  const int split_id = blockIdx.y;
+  const int split_id = bid / a.groups;
+  const int64_t row0 = (int64_t)(bid - split_id * a.groups) * kRows;
   const int64_t bb = (int64_t)split_id * a.nblocks / a.split;
   const int64_t be = (int64_t)(split_id + 1) * a.nblocks / a.split;
 

@@ -23,6 +23,7 @@
 #include "qerl_act.h"
 #include "qerl_device.h"
 #include "qerl_internal.h"
+#include "treduce.h"
 
 namespace qerl {
 
@@ -323,30 +324,10 @@ __global__ __launch_bounds__(256) void xt_kernel(PrepArgs p) {
 }
 
 // t = bf16(sum over chunks of tpart) (the partials carry s already): one
-// thread per (row, j); the chunks are summed in a fixed order (four
-// interleaved partial sums, then combined), so the result is deterministic.
-__global__ __launch_bounds__(256) void treduce_kernel(const float* __restrict__ tpart,
-                                                      uint16_t* __restrict__ t,
-                                                      int64_t mpad, int rpad32,
-                                                      int rpad16, int kchunks) {
+// thread per (row, j), the chunks summed in the fixed order of treduce_one.
+__global__ __launch_bounds__(256) void treduce_kernel(TReduceArgs a) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= mpad * rpad16) return;
-  const int64_t mrow = i / rpad16;
-  const int j = (int)(i % rpad16);
-  const float* src = tpart + mrow * rpad32 + j;
-  const int64_t stride = mpad * rpad32;
-  // Chunk c goes to partial sum c % 4; the loads of a batch of 16 chunks
-  // are all issued before the first add.
-  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int c0 = 0; c0 < kchunks; c0 += 16) {
-    float v[16];
-#pragma unroll
-    for (int u = 0; u < 16; ++u) v[u] = c0 + u < kchunks ? src[(int64_t)(c0 + u) * stride] : 0.0f;
-#pragma unroll
-    for (int u = 0; u < 16; ++u)
-      if (c0 + u < kchunks) acc[u & 3] += v[u];
-  }
-  t[i] = f32_to_bf16_bits((acc[0] + acc[1]) + (acc[2] + acc[3]));
+  if (i < a.mpad * a.rpad16) treduce_one(a, i);
 }
 
 }  // namespace
@@ -381,19 +362,33 @@ hipError_t launch_lora_down(const uint16_t* x, int64_t m, int64_t mpad, int64_t 
   hipLaunchKernelGGL(prep_kernel<1>, grid, dim3(256), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int rpad16 = (int)rup(r, 16);
-  const int64_t total = mpad * rpad16;
-  hipLaunchKernelGGL(treduce_kernel, dim3((unsigned)cdiv(total, 256)), dim3(256), 0, stream,
-                     tpart, t, mpad, a.rpad32, rpad16, kchunks);
+  TReduceArgs tr;
+  tr.tpart = tpart;
+  tr.t = t;
+  tr.mpad = mpad;
+  tr.rpad32 = a.rpad32;
+  tr.rpad16 = (int)rup(r, 16);
+  tr.kchunks = kchunks;
+  hipLaunchKernelGGL(treduce_kernel, dim3((unsigned)cdiv(mpad * tr.rpad16, 256)), dim3(256), 0,
+                     stream, tr);
   return hipGetLastError();
 }
 
+TReduceArgs treduce_args(const LinearPlan& p, char* ws) {
+  TReduceArgs tr;
+  tr.tpart = reinterpret_cast<const float*>(ws + p.off_tpart);
+  tr.t = reinterpret_cast<uint16_t*>(ws + p.off_t);
+  tr.mpad = p.mpad;
+  tr.rpad32 = p.rpad32;
+  tr.rpad16 = p.rpad16;
+  tr.kchunks = p.kchunks;
+  return tr;
+}
+
 hipError_t launch_treduce(const LinearPlan& p, char* ws, hipStream_t stream) {
-  const int64_t total = p.mpad * p.rpad16;
-  hipLaunchKernelGGL(treduce_kernel, dim3((unsigned)cdiv(total, 256)), dim3(256), 0, stream,
-                     reinterpret_cast<const float*>(ws + p.off_tpart),
-                     reinterpret_cast<uint16_t*>(ws + p.off_t), p.mpad, p.rpad32, p.rpad16,
-                     p.kchunks);
+  const TReduceArgs tr = treduce_args(p, ws);
+  hipLaunchKernelGGL(treduce_kernel, dim3((unsigned)cdiv(p.mpad * p.rpad16, 256)), dim3(256), 0,
+                     stream, tr);
   return hipGetLastError();
 }
 
@@ -401,7 +396,7 @@ hipError_t launch_linear_prepare(const LinearPlan& p, const uint16_t* x,
                                  const float* z, const uint16_t* lora_a,
                                  float lora_scale, char* ws,
                                  hipStream_t stream, bool swiglu_input, bool write_xt,
-                                 bool z_rows) {
+                                 bool z_rows, bool reduce_t) {
   PrepArgs a;
   a.x = x;
   a.ldx = swiglu_input ? 2 * p.k : p.k;
@@ -429,7 +424,7 @@ hipError_t launch_linear_prepare(const LinearPlan& p, const uint16_t* x,
   if (p.rpad32 < 32 || p.rpad32 > 128) return hipErrorInvalidValue;
   hipLaunchKernelGGL(prep_kernel<1>, grid, dim3(256), 0, stream, a);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || !reduce_t) return e;
   return launch_treduce(p, ws, stream);
 }
 

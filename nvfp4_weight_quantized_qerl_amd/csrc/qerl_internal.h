@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "treduce.h"
+
 namespace qerl {
 
 // Number of compute units of the current device (cached; 256 on MI355X,
@@ -76,6 +78,10 @@ struct LinearPlan {
   // every block scale is a power of two (MXFP4 in the NVFP4 layout): the
   // LDS-staged decode kernel may use its single-instruction dequantization
   bool pow2_scales;
+  // a whole decode call whose first contraction launch splits K: the prepare
+  // leaves the LoRA-down partials and that launch's extra workgroups sum
+  // them into t (set by the caller after t_reduce_can_merge)
+  bool t_in_contraction;
   // prefill main kernel
   int pf_tile_m, pf_tile_n;
   // workspace byte offsets
@@ -90,11 +96,14 @@ bool make_linear_plan(int64_t m, int64_t n, int64_t k, int r, LinearPlan* p, boo
 // write_xt only t is produced (x_t is not stored; nothing is launched
 // without a LoRA branch).
 // z_rows: z is [m, k], one noise row per token (else [k], shared).
+// Without reduce_t only the LoRA-down partials are written; the contraction
+// launch then sums them into t (LinearPlan::t_in_contraction).
 hipError_t launch_linear_prepare(const LinearPlan& p, const uint16_t* x,
                                  const float* z, const uint16_t* lora_a,
                                  float lora_scale, char* ws,
                                  hipStream_t stream, bool swiglu_input = false,
-                                 bool write_xt = true, bool z_rows = false);
+                                 bool write_xt = true, bool z_rows = false,
+                                 bool reduce_t = true);
 
 // Single-position attention stub: out[i, h dh + e] = v[i, (h / (hq / hkv)) dh + e]
 // of qkv [m, (hq + 2 hkv) dh] (q, then k, then v heads).
@@ -111,6 +120,12 @@ hipError_t launch_lora_down(const uint16_t* x, int64_t m, int64_t mpad, int64_t 
 // LoRA-down reduction: launch_linear_prepare writes the chunk partials
 // s x_t A^T (tpart) and then t = bf16(sum of the partials) (launch_treduce).
 hipError_t launch_treduce(const LinearPlan& p, char* ws, hipStream_t stream);
+TReduceArgs treduce_args(const LinearPlan& p, char* ws);
+
+// Whether the first contraction launch of a decode call splits K with CU
+// slots to spare, so that it can also sum the LoRA-down partials into t
+// (the contraction does not read t when K is split; the finish does).
+bool t_reduce_can_merge(const LinearPlan& p);
 
 // K splits of the LDS-staged decode kernel: the planned split, capped at
 // the number of 256-wide K blocks.

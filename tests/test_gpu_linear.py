@@ -94,7 +94,7 @@ def test_tiny_layer_full():
     (150, 200, 272, 12, 2),   # prefill GEMM: partial last K step, r % 8 != 0
     (257, 130, 1040, 40, 3),  # prefill GEMM: ragged M tile, ragged N tile
     (96, 384, 2048, 0, 1),    # prefill GEMM without LoRA
-    (40, 200, 4096, 12, 2),   # split-K finish: LoRA-down partials reduced there, r % 8 != 0
+    (40, 200, 4096, 12, 2),   # split-K finish, r % 8 != 0; t summed by the split launch
     (64, 130, 6144, 72, 1),   # split-K finish, r > 64 (B row read in the loop)
     (17, 64, 1040, 24, 3),    # split-K in the general kernel (k % 256 != 0)
 ])
@@ -131,13 +131,16 @@ def test_zero_weight_gives_lora_only():
     (32, 16384, 512, 8),     # unsplit: the contraction kernel's own epilogue
     (50, 16384, 256, 16),    # ragged m, unsplit
     (128, 96, 2048, 40),     # the 128-token kernel, r not a multiple of 16 or 32
+    (200, 96, 2048, 40),     # two 128-token chunks, K split in both
     (3, 96, 768, 8),         # one 32-row tile
 ])
 def test_deterministic_and_prepared_halves(m, n, k, r):
-    # The whole call and its two halves run the same kernels (prepare with
-    # its LoRA-down reduction, then the contraction and, when K is split,
-    # the finish): repeated calls, and repeated contractions from one
-    # prepared workspace, must give the same bits.
+    # The whole call and its two halves give the same bits.  The halves run
+    # the prepare with its own LoRA-down reduction launch, then the
+    # contraction and, when K is split, the finish.  A whole call whose first
+    # contraction splits K leaves the reduction to workgroups appended to
+    # that launch.  Both use one reduction routine.  Repeated calls, and
+    # repeated contractions from one prepared workspace, must agree.
     L = make_layer(m, n, k, r, seed=23, stage=1)
     g = GpuLayer(L)
     y1, y2 = g.run(), g.run()
