@@ -34,10 +34,11 @@
 //
 // Pipeline.  x_t has four LDS stages and the weights four register sets;
 // both run two blocks ahead.  Block i: issue the copies of x_t(i+2) and
-// the loads of W(i+2); steps 0-1; wait for this wave's copies of x_t(i+1)
+// the loads of W(i+2); steps 0-2; wait for this wave's copies of x_t(i+1)
 // (s_waitcnt with the 12 later operations still in flight) and s_barrier
 // (every wave's copies of x_t(i+1) have landed and every wave is past
-// block i-1, whose stage the next block's copies overwrite); steps 2-3.
+// block i-1, whose stage the next block's copies overwrite); step 3, whose
+// shadow holds the first read of x_t(i+1).
 // The operand reads and dequantization of each 16-deep step are
 // interleaved with the MFMAs of the previous one.
 //
@@ -288,17 +289,20 @@ __global__ __launch_bounds__(512, 1) void decode_m128(Args a) {
     // and registers that receive the block two ahead.
     //   top:        copies of x_t(i+2), then loads of W(i+2); the scheduling
     //               barriers keep every copy ahead of every load, which the
-    //               count of the mid-block wait (12 = the 4 + 4 + 4 operations
+    //               count of the wait below (12 = the 4 + 4 + 4 operations
     //               issued after x_t(i+1)) relies on: with a load of W(i+1)
     //               moved before a copy of x_t(i+1), fewer than 12 would
     //               follow it and a wave could pass the barrier while its
     //               copy is still in flight
-    //   steps 0-1:  MFMAs of steps 0, 1 (reads and dequantization of 1, 2)
-    //   mid-block:  wait for this wave's copies of x_t(i+1), s_barrier: every
+    //   steps 0-2:  MFMAs of steps 0, 1, 2 (reads and dequantization of
+    //               steps 1, 2, 3)
+    //   late:       wait for this wave's copies of x_t(i+1), s_barrier: every
     //               copy of x_t(i+1) has landed, and every wave is past block
-    //               i-1, so the stage written at the next block's top is free
-    //   steps 2-3:  MFMAs of steps 2, 3 (reads and dequantization of step 3
-    //               and of the next block's step 0)
+    //               i-1, so the stage written at the next block's top is free;
+    //               placed as late as it can be, just before the first read
+    //               of x_t(i+1), to give the copies the most time
+    //   step 3:     MFMAs of step 3 (reads and dequantization of the next
+    //               block's step 0)
 #define QERL_M128_BLOCK(OFF, W, S, XS, XN, WN, SN, X2, W2, S2)            \
   copy_x(min(blk + (OFF) + 2, last), X2);                                 \
   __builtin_amdgcn_sched_barrier(0);                                      \
@@ -312,12 +316,12 @@ __global__ __launch_bounds__(512, 1) void decode_m128(Args a) {
   dequant_b(W, S, 2, b0);                                                 \
   mfmas(xa1, b1);                                                         \
   interleave();                                                           \
-  wait_vmcnt<12>();                                                       \
-  barrier_nofence();                                                      \
   read_a(XS, 3, xa1);                                                     \
   dequant_b(W, S, 3, b1);                                                 \
   mfmas(xa0, b0);                                                         \
   interleave();                                                           \
+  wait_vmcnt<12>();                                                       \
+  barrier_nofence();                                                      \
   read_a(XN, 0, xa0);                                                     \
   dequant_b(WN, SN, 0, b0);                                               \
   mfmas(xa1, b1);                                                         \
