@@ -149,7 +149,8 @@ __global__ __launch_bounds__(512, 1) void decode_m128(Args a) {
   constexpr int XCOPIES = kTokens / 4 / 8;    // x_t copies per wave and block (4 rows each)
   // x_t stages: 128 rows x 16 chunks of 16 B (32 KB each).  After the main
   // loop the first two hold the reduction slots: 8 waves x two tiles x 1024
-  // floats, tile t of every wave in stage t.
+  // floats, tile t of every wave in stage t; the last two hold the bf16
+  // output tiles of the unsplit epilogue, 8 KB per wave.
   __shared__ __attribute__((aligned(16))) uint4 xs0[kTokens * 16], xs1[kTokens * 16],
       xs2[kTokens * 16], xs3[kTokens * 16];
 
@@ -416,6 +417,13 @@ __global__ __launch_bounds__(512, 1) void decode_m128(Args a) {
     return;
   }
   const float S = *a.gscale;
+  // With n a multiple of 8 and y 16-byte aligned, the wave's 64 token rows x
+  // 64 columns of y pass through an 8 KB LDS tile of its own (stages 2 and 3
+  // are idle after the K-half exchange) and leave as 16-byte stores that
+  // cover whole 128-byte rows, instead of 2-byte stores that fill each line
+  // in two halves from different instructions.
+  const bool vec = a.n % 8 == 0 && (reinterpret_cast<uintptr_t>(a.y) & 15) == 0;
+  uint16_t* ytile = reinterpret_cast<uint16_t*>(wave < 4 ? xs2 : xs3) + (wave & 3) * 4096;
 #pragma unroll
   for (int t = 0; t < NTW; ++t) {
     const int64_t row = row0 + 64 * rg + 32 * t + c;
@@ -436,6 +444,12 @@ __global__ __launch_bounds__(512, 1) void decode_m128(Args a) {
           v = mfma_bf16(tv, lora_b8(a, row, live, j0 + 8 * h), v);
         }
       }
+      if (vec) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          ytile[(32 * uu + acc_row(e, lane)) * 64 + 32 * t + c] = f32_to_bf16_bits(v[e]);
+        continue;
+      }
       if (!live) continue;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
@@ -443,6 +457,22 @@ __global__ __launch_bounds__(512, 1) void decode_m128(Args a) {
         if (mrow < a.m_valid) a.y[(int64_t)mrow * a.n + row] = f32_to_bf16_bits(v[e]);
       }
     }
+  }
+  if (!vec) return;
+  // 16-byte chunk q = lane + 64 j of the tile holds token row 64 kh + q / 8,
+  // columns 8 (q % 8) .. 8 (q % 8) + 7 of the wave's block.  The wave reads
+  // back only its own writes, and one wave's LDS operations complete in
+  // order.  row_end and the columns are multiples of 8, so a chunk is either
+  // wholly inside y or wholly past its end.
+  const int64_t col0 = row0 + 64 * rg;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int q = lane + 64 * j;
+    const int rr = q >> 3, cc = 8 * (q & 7);
+    const uint4 val = *reinterpret_cast<const uint4*>(ytile + rr * 64 + cc);
+    const int mrow = 64 * kh + rr;
+    if (mrow < a.m_valid && col0 + cc < row_end)
+      *reinterpret_cast<uint4*>(a.y + (int64_t)mrow * a.n + col0 + cc) = val;
   }
 }
 

@@ -238,6 +238,8 @@ def test_prefill_14b_m16384_sampled(idx):
     (70, 777, 1024, 8, 1),       # 70 tokens: three tiles, ragged output rows
     (96, 64, 384, 72, 4),        # one subtile of rows, 3 blocks, rank 72 (B read in the loop)
     (128, 20000, 256, 0, 1),     # no LoRA, unsplit (79 row groups), 2 blocks
+    (100, 2056, 256, 24, 2),     # unsplit, 16-byte y stores: 100 tokens, last group 8 rows wide
+    (128, 1001, 256, 16, 1),     # unsplit, n % 8 != 0: 2-byte y stores
     (128, 7168, 5120, 64, 0),    # the 32B qkv shape, no noise
     (160, 640, 1280, 32, 2),     # a 128-token chunk and a 32-token remainder
     (224, 384, 768, 16, 1),      # a 128-token chunk and a 96-token chunk
