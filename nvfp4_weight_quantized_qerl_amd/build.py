@@ -28,21 +28,49 @@ COMMON = [
     "-ffp-contract=off", "-fno-gpu-flush-denormals-to-zero",
     "-fvisibility=hidden",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+    # Per-kernel resource report, checked below for scratch use.
+    "-Rpass-analysis=kernel-resource-usage",
 ]
+
+# Kernels allowed to use scratch memory, with the bytes per lane they may
+# use: the 256 x 256 prefill tile keeps one 8-byte value there across its K
+# loop.  Any other kernel with scratch fails the build (a spill inside a hot
+# loop costs far more than any change that causes it could gain).
+SCRATCH_ALLOWED = {"_ZN4qerl7prefill4gemmILi2ELi4ELi128ELi64ELi2EEEvNS0_4ArgsE": 12}
 
 
 def sources():
     return sorted(f for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
+def _scratch_users(text):
+    """(kernel, bytes per lane) of every kernel whose resource report shows
+    scratch, from hipcc's kernel-resource-usage remarks."""
+    out, name = [], None
+    for line in text.splitlines():
+        if "remark:" not in line:
+            continue
+        if "Function Name:" in line:
+            name = line.split("Function Name:")[1].split()[0]
+        elif "ScratchSize [bytes/lane]:" in line and name:
+            size = int(line.split("ScratchSize [bytes/lane]:")[1].split()[0])
+            if size > 0:
+                out.append((name, size))
+    return out
+
+
 def _compile(src, verbose):
     obj = os.path.join(BUILD, src.replace(".hip", ".o"))
     cmd = [HIPCC] + COMMON + ["-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
-    msgs = "\n".join(l for l in (res.stdout + res.stderr).splitlines()
-                     if "packed-fp32-ops" not in l)
+    text = res.stdout + res.stderr
+    msgs = "\n".join(l for l in text.splitlines()
+                     if "packed-fp32-ops" not in l and "kernel-resource-usage" not in l)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{msgs}")
+    bad = [(k, b) for k, b in _scratch_users(text) if b > SCRATCH_ALLOWED.get(k, 0)]
+    if bad:
+        raise RuntimeError(f"{src}: kernels using scratch memory: {bad}")
     if verbose and msgs.strip():
         print(msgs)
     return obj

@@ -410,8 +410,13 @@ __global__ __launch_bounds__(512, 1) void decode_m128(Args a) {
         const int u = 2 * kh + uu;
         const f32x16_t v = kh ? acc[t][2 + uu] : acc[t][uu];
         float* dst = a.ypart + ((int64_t)split_id * kTokens + 32 * u) * a.n + row;
+        // Written through to memory (device-scope stores): the finishing
+        // launch reads them from there anyway, and the kernel's end then
+        // has no dirty L2 lines of partials to write back.
 #pragma unroll
-        for (int e = 0; e < 16; ++e) dst[(int64_t)acc_row(e, lane) * a.n] = v[e];
+        for (int e = 0; e < 16; ++e)
+          __hip_atomic_store(dst + (int64_t)acc_row(e, lane) * a.n, v[e], __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
       }
     }
     return;

@@ -133,6 +133,7 @@ def test_zero_weight_gives_lora_only():
     (128, 96, 2048, 40),     # the 128-token kernel, r not a multiple of 16 or 32
     (200, 96, 2048, 40),     # two 128-token chunks, K split in both
     (3, 96, 768, 8),         # one 32-row tile
+    (100, 300, 2048, 24),    # 128-token kernel, 100 tokens, ragged last row group, K split
 ])
 def test_deterministic_and_prepared_halves(m, n, k, r):
     # The whole call and its two halves give the same bits.  The halves run
