@@ -269,10 +269,10 @@ static qerl_status linear_full(bool prefill, const void* x, int64_t m, const voi
       r_eff > 0 && (!prefill || plan.m <= 64) && qerl::t_reduce_can_merge(plan);
   hipStream_t st = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
-  hipError_t e = qerl::launch_linear_prepare(plan, static_cast<const uint16_t*>(x), z,
-                                             static_cast<const uint16_t*>(lora_a),
-                                             lora_scale, ws, st, swiglu, true, z_rows,
-                                             !plan.t_in_contraction);
+  hipError_t e = qerl::launch_linear_prepare(
+      plan, static_cast<const uint16_t*>(x), z, static_cast<const uint16_t*>(lora_a), lora_scale,
+      ws, st, swiglu, true, z_rows, !plan.t_in_contraction,
+      plan.t_in_contraction ? reinterpret_cast<unsigned*>(ws + plan.off_sync) : nullptr);
   if (e != hipSuccess) return QERL_ERR_HIP;
   const uint8_t* c = static_cast<const uint8_t*>(codes);
   const uint8_t* sc = static_cast<const uint8_t*>(scales);

@@ -352,6 +352,7 @@ BackwardPlan make_backward_plan(int64_t m, int64_t n, int64_t k, int r) {
   // Of the forward's workspace the backward uses only the LoRA-down partials
   // and t (x_t is formed from x and z where it is needed, and not stored).
   b.fwd.off_xt = 0;
+  b.fwd.off_sync = 0;
   b.fwd.off_ypart = 0;
   b.fwd.off_tpart = take(r ? (size_t)b.fwd.kchunks * mpad * b.fwd.rpad32 * 4 : 0);
   b.fwd.off_t = take(r ? (size_t)mpad * b.fwd.rpad16 * 2 : 0);

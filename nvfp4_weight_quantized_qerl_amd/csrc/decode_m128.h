@@ -86,7 +86,17 @@ struct Args {
   // LoRA-down partials into t (split > 1 only: the finish reads t).
   int groups, tr_wgs;
   TReduceArgs tr;
+  // Unsplit with tr_wgs > 0: the reduction workgroups come first in the
+  // grid instead (workgroup tr_wgs + g owns row group g), store t at device
+  // scope and count themselves in tsync[0] (zero at launch); the epilogue
+  // waits for the count before it reads t.  tsync[1] is set if that wait
+  // gave up.  Null otherwise.
+  unsigned* tsync;
 };
+
+// A wait for t gives up after this many polls (about a second); the output
+// is then undefined and tsync[1] is set.
+constexpr uint32_t kTWaitLimit = 1u << 20;
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -154,8 +164,19 @@ __global__ __launch_bounds__(512, 1) void decode_m128(Args a) {
   __shared__ __attribute__((aligned(16))) uint4 xs0[kTokens * 16], xs1[kTokens * 16],
       xs2[kTokens * 16], xs3[kTokens * 16];
 
-  const int bid = __builtin_amdgcn_readfirstlane((int)blockIdx.x);
-  if (bid >= a.groups * a.split) {
+  int bid = __builtin_amdgcn_readfirstlane((int)blockIdx.x);
+  if (a.tsync) {
+    if (bid < a.tr_wgs) {
+      treduce_strided(a.tr, (int64_t)bid * 512 + threadIdx.x, (int64_t)a.tr_wgs * 512);
+      // every wave's t stores have completed before the count goes up
+      wait_vmcnt<0>();
+      __syncthreads();
+      if (threadIdx.x == 0)
+        __hip_atomic_fetch_add(a.tsync, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return;
+    }
+    bid -= a.tr_wgs;
+  } else if (bid >= a.groups * a.split) {
     treduce_strided(a.tr, (int64_t)(bid - a.groups * a.split) * 512 + threadIdx.x,
                     (int64_t)a.tr_wgs * 512);
     return;
@@ -429,6 +450,36 @@ __global__ __launch_bounds__(512, 1) void decode_m128(Args a) {
   // in two halves from different instructions.
   const bool vec = a.n % 8 == 0 && (reinterpret_cast<uintptr_t>(a.y) & 15) == 0;
   uint16_t* ytile = reinterpret_cast<uint16_t*>(wave < 4 ? xs2 : xs3) + (wave & 3) * 4096;
+  if (a.tsync) {
+    // t comes from this launch's first workgroups (dispatched before this
+    // one, so the wait ends); its rows are read at device scope below
+    if (threadIdx.x == 0) {
+      for (uint32_t it = 0;
+           __hip_atomic_load(a.tsync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
+           (unsigned)a.tr_wgs;
+           ++it) {
+        if (it >= kTWaitLimit) {
+          __hip_atomic_store(a.tsync + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+    }
+    // t (rows past xrows as zeros) into LDS once per workgroup, loaded at
+    // device scope (aux 16: sc1): token rows 0-63 in stage 0, 64-127 in
+    // stage 1, nch + 1 16-byte chunks per row (an odd stride: the MFMA-layout
+    // reads of 16 consecutive rows hit 16 different bank groups)
+    if (a.r > 0) {
+      const int nch = a.rpad16 / 8;
+      const __amdgpu_buffer_rsrc_t rt = rsrc(a.t, (uint32_t)(a.xrows * a.rpad16 * 2));
+      for (int ch = threadIdx.x; ch < kTokens * nch; ch += 512) {
+        const int tr = ch / nch, q = ch - tr * nch;
+        (tr < 64 ? xs0 : xs1)[(tr & 63) * (nch + 1) + q] = __builtin_bit_cast(
+            uint4, __builtin_amdgcn_raw_buffer_load_b128(rt, (tr * a.rpad16 + 8 * q) * 2, 0, 16));
+      }
+    }
+    __syncthreads();
+  }
 #pragma unroll
   for (int t = 0; t < NTW; ++t) {
     const int64_t row = row0 + 64 * rg + 32 * t + c;
@@ -443,9 +494,11 @@ __global__ __launch_bounds__(512, 1) void decode_m128(Args a) {
         // t has xrows rows (rows past it are zero tokens)
         const bool trow_in = 32 * u + c < a.xrows;
         const uint16_t* trow = a.t + (int64_t)(32 * u + c) * a.rpad16 + 8 * h;
+        const uint4* tl = (u < 2 ? xs0 : xs1) + ((32 * u + c) & 63) * (a.rpad16 / 8 + 1) + h;
         for (int j0 = 0; j0 < a.rpad16; j0 += 16) {
-          const uint4 tv = trow_in ? *reinterpret_cast<const uint4*>(trow + j0)
-                                   : make_uint4(0u, 0u, 0u, 0u);
+          const uint4 tv = a.tsync ? tl[j0 / 8]
+                                   : (trow_in ? *reinterpret_cast<const uint4*>(trow + j0)
+                                              : make_uint4(0u, 0u, 0u, 0u));
           v = mfma_bf16(tv, lora_b8(a, row, live, j0 + 8 * h), v);
         }
       }

@@ -167,6 +167,7 @@ bool make_linear_plan(int64_t m, int64_t n, int64_t k, int r, LinearPlan* p, boo
   p->off_xt = take((size_t)p->mpad * k * 2);
   p->off_tpart = take(r ? (size_t)p->kchunks * p->mpad * p->rpad32 * 4 : 0);
   p->off_t = take(r ? (size_t)p->mpad * p->rpad16 * 2 : 0);
+  p->off_sync = take(8);
   size_t ypart = p->dec_split > 1 ? (size_t)p->dec_split * 32 * p->dec_mt * n * 4 : 0;
   if (p->m128 && p->m128_split > 1)
     ypart = std::max(ypart, (size_t)p->m128_split * 128 * n * 4);
@@ -186,6 +187,7 @@ struct PrepArgs {
   const uint16_t* __restrict__ a;
   uint16_t* __restrict__ xt;     // null: x_t is not written (only the LoRA-down partials)
   float* __restrict__ tpart;
+  unsigned* sync;                  // two words cleared by the first workgroup, or null
   int64_t m, mpad, k;
   int r, rpad32;
   float lora_scale;
@@ -212,6 +214,8 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs p) {
   const int h = lane >> 5, c = lane & 31;
   const int64_t kc = (int64_t)blockIdx.y * kPrepChunk;
   const int64_t row0 = (int64_t)blockIdx.x * 32;
+  if (p.sync && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x < 2)
+    p.sync[threadIdx.x] = 0u;
 
   // A operands of this wave's 128 channels (lane: row j = 32 t + c of A,
   // from the rank tiles of this workgroup: blockIdx.z picks RT tiles of 32).
@@ -307,6 +311,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs p) {
 // m..mpad-1 are written as zeros.
 __global__ __launch_bounds__(256) void xt_kernel(PrepArgs p) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (p.sync && i < 2) p.sync[i] = 0u;
   const int64_t per_row = p.k / 8;
   if (i >= p.mpad * per_row) return;
   const int64_t mrow = i / per_row, k0 = (i % per_row) * 8;
@@ -348,6 +353,7 @@ hipError_t launch_lora_down(const uint16_t* x, int64_t m, int64_t mpad, int64_t 
   a.a = a_rk;
   a.xt = nullptr;
   a.tpart = tpart;
+  a.sync = nullptr;
   a.m = m;
   a.mpad = mpad;
   a.k = k;
@@ -369,6 +375,7 @@ hipError_t launch_lora_down(const uint16_t* x, int64_t m, int64_t mpad, int64_t 
   tr.rpad32 = a.rpad32;
   tr.rpad16 = (int)rup(r, 16);
   tr.kchunks = kchunks;
+  tr.coherent = 0;
   hipLaunchKernelGGL(treduce_kernel, dim3((unsigned)cdiv(mpad * tr.rpad16, 256)), dim3(256), 0,
                      stream, tr);
   return hipGetLastError();
@@ -382,6 +389,7 @@ TReduceArgs treduce_args(const LinearPlan& p, char* ws) {
   tr.rpad32 = p.rpad32;
   tr.rpad16 = p.rpad16;
   tr.kchunks = p.kchunks;
+  tr.coherent = 0;
   return tr;
 }
 
@@ -396,7 +404,7 @@ hipError_t launch_linear_prepare(const LinearPlan& p, const uint16_t* x,
                                  const float* z, const uint16_t* lora_a,
                                  float lora_scale, char* ws,
                                  hipStream_t stream, bool swiglu_input, bool write_xt,
-                                 bool z_rows, bool reduce_t) {
+                                 bool z_rows, bool reduce_t, unsigned* clear_sync) {
   PrepArgs a;
   a.x = x;
   a.ldx = swiglu_input ? 2 * p.k : p.k;
@@ -406,6 +414,7 @@ hipError_t launch_linear_prepare(const LinearPlan& p, const uint16_t* x,
   a.a = lora_a;
   a.xt = write_xt ? reinterpret_cast<uint16_t*>(ws + p.off_xt) : nullptr;
   a.tpart = reinterpret_cast<float*>(ws + p.off_tpart);
+  a.sync = clear_sync;
   a.m = p.m;
   a.mpad = p.mpad;
   a.k = p.k;

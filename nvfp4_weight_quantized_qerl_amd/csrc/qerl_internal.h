@@ -85,7 +85,10 @@ struct LinearPlan {
   // prefill main kernel
   int pf_tile_m, pf_tile_n;
   // workspace byte offsets
-  size_t off_xt, off_tpart, off_t, off_ypart, total;
+  size_t off_xt, off_tpart, off_t, off_sync, off_ypart, total;
+  // off_sync: two words that the prepare of a whole call clears: the count
+  // of reduction workgroups done and the wait-timeout flag of an unsplit
+  // 128-token launch that also sums t (decode_m128.h, Args::tsync)
 };
 
 // tiled: the plan of the tiled-layout entry points (k % 128 == 0).
@@ -98,12 +101,14 @@ bool make_linear_plan(int64_t m, int64_t n, int64_t k, int r, LinearPlan* p, boo
 // z_rows: z is [m, k], one noise row per token (else [k], shared).
 // Without reduce_t only the LoRA-down partials are written; the contraction
 // launch then sums them into t (LinearPlan::t_in_contraction).
+// clear_sync: two words set to zero by the launch (needs a LoRA branch or
+// write_xt, so that a kernel is launched).
 hipError_t launch_linear_prepare(const LinearPlan& p, const uint16_t* x,
                                  const float* z, const uint16_t* lora_a,
                                  float lora_scale, char* ws,
                                  hipStream_t stream, bool swiglu_input = false,
                                  bool write_xt = true, bool z_rows = false,
-                                 bool reduce_t = true);
+                                 bool reduce_t = true, unsigned* clear_sync = nullptr);
 
 // Single-position attention stub: out[i, h dh + e] = v[i, (h / (hq / hkv)) dh + e]
 // of qkv [m, (hq + 2 hkv) dh] (q, then k, then v heads).
@@ -122,9 +127,11 @@ hipError_t launch_lora_down(const uint16_t* x, int64_t m, int64_t mpad, int64_t 
 hipError_t launch_treduce(const LinearPlan& p, char* ws, hipStream_t stream);
 TReduceArgs treduce_args(const LinearPlan& p, char* ws);
 
-// Whether the first contraction launch of a decode call splits K with CU
-// slots to spare, so that it can also sum the LoRA-down partials into t
-// (the contraction does not read t when K is split; the finish does).
+// Whether the first contraction launch of a decode call has CU slots to
+// spare, so that it can also sum the LoRA-down partials into t: when it
+// splits K (the contraction does not read t then; the finish does), or
+// when it is an unsplit 128-token launch (its epilogue waits for t on the
+// sync words, which the prepare clears: launch_linear_prepare clear_sync).
 bool t_reduce_can_merge(const LinearPlan& p);
 
 // K splits of the LDS-staged decode kernel: the planned split, capped at

@@ -14,6 +14,9 @@ struct TReduceArgs {
   uint16_t* t;          // [mpad, rpad16] bf16
   int64_t mpad;
   int rpad32, rpad16, kchunks;
+  // t is read by other workgroups of the same launch: stored at device
+  // scope (past the per-XCD L2s)
+  int coherent;
 };
 
 // Output i = row * rpad16 + j.  Chunk c goes to partial sum c % 4 (the
@@ -34,7 +37,11 @@ __device__ __forceinline__ void treduce_one(const TReduceArgs& a, int64_t i) {
     for (int u = 0; u < 16; ++u)
       if (c0 + u < a.kchunks) acc[u & 3] += v[u];
   }
-  a.t[i] = f32_to_bf16_bits((acc[0] + acc[1]) + (acc[2] + acc[3]));
+  const uint16_t tb = f32_to_bf16_bits((acc[0] + acc[1]) + (acc[2] + acc[3]));
+  if (a.coherent)
+    __hip_atomic_store(a.t + i, tb, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else
+    a.t[i] = tb;
 }
 
 // Outputs first, first + stride, ... of the mpad x rpad16.

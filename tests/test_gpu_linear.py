@@ -134,19 +134,23 @@ def test_zero_weight_gives_lora_only():
     (200, 96, 2048, 40),     # two 128-token chunks, K split in both
     (3, 96, 768, 8),         # one 32-row tile
     (100, 300, 2048, 24),    # 128-token kernel, 100 tokens, ragged last row group, K split
+    (128, 2056, 256, 24),    # 128-token kernel unsplit: its epilogue waits for t from the launch
+    (100, 4104, 384, 16),    # the same with 100 tokens and a ragged last row group
 ])
 def test_deterministic_and_prepared_halves(m, n, k, r):
     # The whole call and its two halves give the same bits.  The halves run
     # the prepare with its own LoRA-down reduction launch, then the
     # contraction and, when K is split, the finish.  A whole call whose first
-    # contraction splits K leaves the reduction to workgroups appended to
-    # that launch.  Both use one reduction routine.  Repeated calls, and
+    # contraction splits K (or is an unsplit 128-token launch) leaves the
+    # reduction to workgroups of that launch.  Both use one reduction routine.  Repeated calls, and
     # repeated contractions from one prepared workspace, must agree.
     L = make_layer(m, n, k, r, seed=23, stage=1)
     g = GpuLayer(L)
     y1, y2 = g.run(), g.run()
     assert np.array_equal(y1, y2)
     ws = q.workspace(m, n, k, r, "cuda:0")
+    for _ in range(2):       # whole calls on one workspace (its sync words are reused)
+        assert np.array_equal(g.run(workspace=ws), y1)
     q.qerl_linear_prepare(g.x, n, g.a, L.lora_scale, g.z, ws)
     y = torch.empty((m, n), dtype=torch.bfloat16, device="cuda:0")
     for _ in range(3):       # repeated contractions from one prepared workspace
