@@ -225,6 +225,11 @@ hipError_t run_decode_lds(const LinearPlan& p, int mt, const uint8_t* codes,
   a.groups = p.dec_groups;
   a.tr_wgs = tr ? reduce_wgs(p.dec_groups * split) : 0;
   a.tr = tr ? *tr : TReduceArgs{};
+  // Unsplit, the epilogue reads t: the reduction workgroups go first and
+  // the contraction workgroups wait for them (sync words cleared by the
+  // call's prepare).
+  a.tsync = (a.tr_wgs > 0 && split == 1) ? reinterpret_cast<unsigned*>(ws + p.off_sync) : nullptr;
+  a.tr.coherent = a.tsync ? 1 : 0;
   hipLaunchKernelGGL(kern, dim3((unsigned)(p.dec_groups * split + a.tr_wgs)), dim3(512), 0,
                      stream, a);
   hipError_t e = hipGetLastError();
@@ -351,7 +356,6 @@ hipError_t run_decode_chunks(const LinearPlan& p, const uint8_t* codes,
 bool t_reduce_can_merge(const LinearPlan& p) {
   const ChunkChoice ch = choose_chunk(p, 0);
   const int groups = ch.kind == ChunkKernel::kM128 ? p.m128_groups : p.dec_groups;
-  if (ch.split < 2 && ch.kind != ChunkKernel::kM128) return false;
   return ch.kind != ChunkKernel::kMain && reduce_wgs(groups * ch.split) > 0;
 }
 

@@ -58,7 +58,17 @@ struct Args {
   // LoRA-down partials into t (split > 1 only: the finish reads t).
   int groups, tr_wgs;
   TReduceArgs tr;
+  // Unsplit with tr_wgs > 0: the reduction workgroups come first in the
+  // grid instead (workgroup tr_wgs + g owns row group g), store t at device
+  // scope and count themselves in tsync[0] (zero at launch); after the main
+  // loop the contraction workgroups wait for the count and load t.  tsync[1]
+  // is set if that wait gave up.  Null otherwise.
+  unsigned* tsync;
 };
+
+// A wait for t gives up after this many polls (about a second); the output
+// is then undefined and tsync[1] is set.
+constexpr uint32_t kTWaitLimit = 1u << 20;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
@@ -179,8 +189,19 @@ __global__ __launch_bounds__(512, 1) void decode_lds(Args a) {
   __shared__ __attribute__((aligned(16))) uint4 xs0[XROWS * 32], xs1[XROWS * 32];
   __shared__ __attribute__((aligned(16))) uint16_t t_lds[XROWS * 128];
 
-  const int bid = __builtin_amdgcn_readfirstlane((int)blockIdx.x);
-  if (bid >= a.groups * a.split) {
+  int bid = __builtin_amdgcn_readfirstlane((int)blockIdx.x);
+  if (a.tsync) {
+    if (bid < a.tr_wgs) {
+      treduce_strided(a.tr, (int64_t)bid * 512 + threadIdx.x, (int64_t)a.tr_wgs * 512);
+      // every wave's t stores have completed before the count goes up
+      wait_vmcnt<0>();
+      __syncthreads();
+      if (threadIdx.x == 0)
+        __hip_atomic_fetch_add(a.tsync, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return;
+    }
+    bid -= a.tr_wgs;
+  } else if (bid >= a.groups * a.split) {
     treduce_strided(a.tr, (int64_t)(bid - a.groups * a.split) * 512 + threadIdx.x,
                     (int64_t)a.tr_wgs * 512);
     return;
@@ -202,8 +223,8 @@ __global__ __launch_bounds__(512, 1) void decode_lds(Args a) {
   const float S = *a.gscale;     // first needed in the epilogue
   // t is read only by the unsplit epilogue (with K split the finishing
   // kernel adds t B^T, and t may still be being summed by this launch's
-  // reduction workgroups).
-  if (a.r > 0 && a.split == 1) {
+  // reduction workgroups; with tsync it is loaded after the main loop).
+  if (a.r > 0 && a.split == 1 && !a.tsync) {
     const int words = XROWS * a.rpad16 / 8;
     for (int i = threadIdx.x; i < words; i += 512)
       reinterpret_cast<uint4*>(t_lds)[i] = reinterpret_cast<const uint4*>(a.t)[i];
@@ -331,6 +352,32 @@ __global__ __launch_bounds__(512, 1) void decode_lds(Args a) {
   // Every copy has landed and every wave is done with the stages.
   wait_vmcnt<0>();
   barrier_nofence();
+  if (a.tsync) {
+    // t comes from this launch's first workgroups (dispatched before this
+    // one, so the wait ends); loaded at device scope (aux 16: sc1).  The
+    // reduction rounds below end with barriers, so t_lds is complete before
+    // the epilogue reads it.
+    if (threadIdx.x == 0) {
+      for (uint32_t it = 0;
+           __hip_atomic_load(a.tsync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
+           (unsigned)a.tr_wgs;
+           ++it) {
+        if (it >= kTWaitLimit) {
+          __hip_atomic_store(a.tsync + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+    }
+    __syncthreads();
+    if (a.r > 0) {
+      const int words = XROWS * a.rpad16 / 8;
+      const __amdgpu_buffer_rsrc_t rt = rsrc(a.t, (uint32_t)(words * 16));
+      for (int i = threadIdx.x; i < words; i += 512)
+        reinterpret_cast<uint4*>(t_lds)[i] =
+            __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rt, 16 * i, 0, 16));
+    }
+  }
 
   // Sum the four K quarters of each row half through the (now free) x_t
   // stages.  Half hf uses slices [hf * SPH, (hf + 1) * SPH); per round TPR

@@ -130,8 +130,9 @@ TReduceArgs treduce_args(const LinearPlan& p, char* ws);
 // Whether the first contraction launch of a decode call has CU slots to
 // spare, so that it can also sum the LoRA-down partials into t: when it
 // splits K (the contraction does not read t then; the finish does), or
-// when it is an unsplit 128-token launch (its epilogue waits for t on the
-// sync words, which the prepare clears: launch_linear_prepare clear_sync).
+// when it is unsplit (its workgroups wait for t after their main loop, on
+// the sync words, which the prepare clears: launch_linear_prepare
+// clear_sync).
 bool t_reduce_can_merge(const LinearPlan& p);
 
 // K splits of the LDS-staged decode kernel: the planned split, capped at
