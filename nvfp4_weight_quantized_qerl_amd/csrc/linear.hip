@@ -16,7 +16,9 @@
 //           and written one row per instruction, and tpart = x_t A^T over
 //           the chunk (bf16 MFMA, fp32, operands through LDS);
 //   treduce: t = bf16(sum over chunks of tpart), summed in a fixed order
-//           so the result is deterministic.
+//           so the result is deterministic; a launch of its own, or (whole
+//           decode calls whose first contraction launch has CU slots to
+//           spare) workgroups of that launch running the same routine.
 // Without a LoRA branch a single elementwise kernel (xt_kernel) writes x_t.
 #include <algorithm>
 
