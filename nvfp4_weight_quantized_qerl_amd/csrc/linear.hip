@@ -46,8 +46,25 @@ namespace {
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int64_t rup(int64_t a, int64_t b) { return cdiv(a, b) * b; }
 
-// K range of one prepare workgroup: four waves of 128.
+// K range of one prepare workgroup (four waves of a quarter each) for the
+// LoRA-down of other operands (launch_lora_down).
 constexpr int64_t kPrepChunk = 512;
+
+// K range of one prepare workgroup of a linear call (mtiles 32-row tiles,
+// rtiles 32-wide rank tiles): 512 channels, halved (down to 128) while the
+// launch has fewer than 256 workgroups and the K chunks -- the partial sums
+// the LoRA-down reduction adds per output -- stay at most kMaxPrepChunks.
+// Narrow chunks give the latency-bound prepare of a decode call more
+// workgroups; the reduction's loads grow with the chunk count.  (Measured on
+// whole decode steps: 128 for K = 5120 and 3584, 256 for K = 18944, 512 for
+// K = 27648 and for prefill-sized m.)
+constexpr int64_t kMaxPrepChunks = 80;
+int64_t prep_chunk(int64_t k, int64_t mtiles, int64_t rtiles) {
+  int64_t ch = 512;
+  while (ch > 128 && mtiles * cdiv(k, ch) * rtiles < 256 && cdiv(k, ch / 2) <= kMaxPrepChunks)
+    ch /= 2;
+  return ch;
+}
 
 // Largest weight subtile count NT per wave that the decode kernels hold in
 // registers without spilling, for MT token tiles (from the compiler's
@@ -141,8 +158,8 @@ bool make_linear_plan(int64_t m, int64_t n, int64_t k, int r, LinearPlan* p, boo
   p->rpad32 = r ? (int)rup(r, 32) : 0;
   p->rpad16 = r ? (int)rup(r, 16) : 0;
   const int64_t mtiles = p->mpad / 32;
-  p->kchunk = kPrepChunk;
-  p->kchunks = (int)cdiv(k, kPrepChunk);
+  p->kchunk = prep_chunk(k, mtiles, std::max(1, p->rpad32 / 32));
+  p->kchunks = (int)cdiv(k, p->kchunk);
   // Token tiles per decode launch: 1, 2 or 4 (the instantiated kernels);
   // run_decode_chunks takes smaller chunks for the remainder.
   // With k % 256 == 0 the LDS-staged kernel (up to two tiles) is used even
@@ -195,33 +212,37 @@ struct PrepArgs {
   float lora_scale;
 };
 
-// One workgroup: 32 rows x one 512-wide K chunk x RT 32-wide rank tiles
+// One workgroup: 32 rows x one CH-wide K chunk x RT 32-wide rank tiles
 // (the launches use RT = 1 and one rank tile per grid z).
-//   x_t: wave w reads and writes rows 8 w .. 8 w + 7, one row of the chunk
-//        (1 KB) per instruction, lane l holding channels 8 l .. 8 l + 7; the
-//        rows also go to an LDS tile, 16-byte chunk q of row rr stored at
-//        q ^ (rr mod 16) so that the MFMA reads below (lane = row) hit 16
-//        different bank groups per 16 lanes.
-//   LoRA-down: wave w takes the 128 channels at 128 w: eight 32x32x16 MFMAs
-//        per 32 rows of A, operands x_t from the LDS tile and A from global
-//        memory (issued first, so their latency passes under the x_t work).
+//   x_t: wave w reads and writes rows 8 w .. 8 w + 7, RPI rows of the chunk
+//        per instruction (CH / 8 lanes per row, each holding eight
+//        channels); the rows also go to an LDS tile, 16-byte chunk q of row
+//        rr stored at q ^ (rr mod 16) so that the MFMA reads below (lane =
+//        row) hit 16 different bank groups per 16 lanes.
+//   LoRA-down: wave w takes the CH / 4 channels at w CH / 4:
+//        STEPS 32x32x16 MFMAs per 32 rows of A, operands x_t from the LDS tile
+//        and A from global memory (issued first, so their latency passes
+//        under the x_t work).
 // The four waves' LoRA-down tiles are summed through LDS and wave 0 writes
 // the chunk's partial tpart[chunk, rows, rpad32].
-template <int RT>
+template <int RT, int CH>
 __global__ __launch_bounds__(256) void prep_kernel(PrepArgs p) {
-  constexpr int STEPS = 8;
-  __shared__ __attribute__((aligned(16))) uint4 xs[32 * 64];
+  constexpr int STEPS = CH / 64;     // 16-deep steps per wave
+  constexpr int QPR = CH / 8;        // 16-byte chunks per row
+  constexpr int RPI = 64 / QPR;                   // rows per load instruction
+  static_assert(QPR >= 16 && QPR <= 64 && 64 % QPR == 0, "chunk of 128 to 512 channels");
+  __shared__ __attribute__((aligned(16))) uint4 xs[32 * QPR];
   __shared__ float red[3 * (RT > 0 ? RT : 1) * 16 * 64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int h = lane >> 5, c = lane & 31;
-  const int64_t kc = (int64_t)blockIdx.y * kPrepChunk;
+  const int64_t kc = (int64_t)blockIdx.y * CH;
   const int64_t row0 = (int64_t)blockIdx.x * 32;
   if (p.sync && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x < 2)
     p.sync[threadIdx.x] = 0u;
 
-  // A operands of this wave's 128 channels (lane: row j = 32 t + c of A,
-  // from the rank tiles of this workgroup: blockIdx.z picks RT tiles of 32).
-  const int64_t kb = kc + 128 * wave;
+  // A operands of this wave's channels (lane: row j = 32 t + c of A, from
+  // the rank tiles of this workgroup: blockIdx.z picks RT tiles of 32).
+  const int64_t kb = kc + (CH / 4) * wave;
   const int rank0 = 32 * RT * (int)blockIdx.z;
   uint4 av[RT > 0 ? RT : 1][STEPS];
 #pragma unroll
@@ -236,25 +257,28 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs p) {
     }
   }
 
-  // x_t rows, coalesced.
-  const int64_t kl = kc + 8 * lane;       // this lane's channels
+  // x_t rows, coalesced: lane l holds channels 8 (l mod QPR) .. + 7 of row
+  // 8 wave + RPI i + l / QPR.
+  const int q = lane % QPR, sub = lane / QPR;
+  const int64_t kl = kc + 8 * q;          // this lane's channels
   const bool kin = kl < p.k;              // k % 8 == 0: all eight in range or none
   float4 z0 = make_float4(0.0f, 0.0f, 0.0f, 0.0f), z1 = z0;
   if (kin && p.z && p.z_ld == 0) {
     z0 = *reinterpret_cast<const float4*>(p.z + kl);
     z1 = *reinterpret_cast<const float4*>(p.z + kl + 4);
   }
-  uint4 xv[8];
+  constexpr int NX = 8 / RPI;             // load instructions per wave
+  uint4 xv[NX];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int64_t mrow = row0 + 8 * wave + i;
+  for (int i = 0; i < NX; ++i) {
+    const int64_t mrow = row0 + 8 * wave + RPI * i + sub;
     xv[i] = (kin && mrow < p.m) ? *reinterpret_cast<const uint4*>(p.x + mrow * p.ldx + kl)
                                 : make_uint4(0u, 0u, 0u, 0u);
   }
   if (p.swiglu) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int64_t mrow = row0 + 8 * wave + i;
+    for (int i = 0; i < NX; ++i) {
+      const int64_t mrow = row0 + 8 * wave + RPI * i + sub;
       const uint4 up = (kin && mrow < p.m)
                            ? *reinterpret_cast<const uint4*>(p.x + mrow * p.ldx + p.k + kl)
                            : make_uint4(0u, 0u, 0u, 0u);
@@ -262,8 +286,8 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs p) {
     }
   }
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int rr = 8 * wave + i;
+  for (int i = 0; i < NX; ++i) {
+    const int rr = 8 * wave + RPI * i + sub;
     const int64_t mrow = row0 + rr;
     if (mrow < p.m && p.z) {
       if (p.z_ld && kin) {
@@ -275,7 +299,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs p) {
       }
     }
     if (kin && p.xt && blockIdx.z == 0) *reinterpret_cast<uint4*>(p.xt + mrow * p.k + kl) = xv[i];
-    xs[rr * 64 + (lane ^ (rr & 15))] = xv[i];
+    xs[rr * QPR + (q ^ (rr & 15))] = xv[i];
   }
   if (RT == 0) return;
   __syncthreads();
@@ -285,7 +309,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs p) {
   for (int t = 0; t < (RT > 0 ? RT : 1); ++t) acc[t] = zero16();
 #pragma unroll
   for (int s = 0; s < STEPS; ++s) {
-    const uint4 xa = xs[c * 64 + ((16 * wave + 2 * s + h) ^ (c & 15))];
+    const uint4 xa = xs[c * QPR + (((QPR / 4) * wave + 2 * s + h) ^ (c & 15))];
 #pragma unroll
     for (int t = 0; t < RT; ++t) acc[t] = mfma_bf16(xa, av[t][s], acc[t]);
   }
@@ -367,7 +391,7 @@ hipError_t launch_lora_down(const uint16_t* x, int64_t m, int64_t mpad, int64_t 
   // quarter of A at rank 128 and finishes sooner; x is read once per tile.
   const dim3 grid((unsigned)(mpad / 32), (unsigned)kchunks, (unsigned)(a.rpad32 / 32));
   if (a.rpad32 < 32 || a.rpad32 > 128) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(prep_kernel<1>, grid, dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((prep_kernel<1, (int)kPrepChunk>), grid, dim3(256), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   TReduceArgs tr;
@@ -433,7 +457,12 @@ hipError_t launch_linear_prepare(const LinearPlan& p, const uint16_t* x,
   // also write x_t.
   const dim3 grid((unsigned)(p.mpad / 32), (unsigned)p.kchunks, (unsigned)(p.rpad32 / 32));
   if (p.rpad32 < 32 || p.rpad32 > 128) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(prep_kernel<1>, grid, dim3(256), 0, stream, a);
+  switch (p.kchunk) {
+    case 128: hipLaunchKernelGGL((prep_kernel<1, 128>), grid, dim3(256), 0, stream, a); break;
+    case 256: hipLaunchKernelGGL((prep_kernel<1, 256>), grid, dim3(256), 0, stream, a); break;
+    case 512: hipLaunchKernelGGL((prep_kernel<1, 512>), grid, dim3(256), 0, stream, a); break;
+    default: return hipErrorInvalidValue;
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !reduce_t) return e;
   return launch_treduce(p, ws, stream);
