@@ -322,7 +322,12 @@ QERL_API size_t qerl_linear_workspace_bytes(int64_t m, int64_t n, int64_t k,
  *   workspace    device scratch of at least
  *                qerl_linear_workspace_bytes(m, n, k, r) bytes,
  *                256-byte aligned; its contents on entry do not matter
- * Concurrent calls must not share a workspace.
+ * Concurrent calls must not share a workspace.  Within one call, the
+ * workgroups of a contraction launch may wait (a bounded poll on words of
+ * the workspace that the call's own prepare launch clears) for workgroups
+ * of the same launch that are dispatched ahead of them; should a wait ever
+ * give up (after about a second: only if those workgroups could not run),
+ * y is undefined.
  */
 QERL_API qerl_status qerl_linear_decode(const void* x, int64_t m, const void* codes,
                                const void* scales, const float* gscale,
