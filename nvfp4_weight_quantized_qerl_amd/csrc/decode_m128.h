@@ -43,8 +43,12 @@
 // interleaved with the MFMAs of the previous one.
 //
 // When the weight rows are too few to fill the GPU, K is also split
-// across workgroups: each writes its fp32 partial tiles and a separate
-// finishing kernel sums them in split order and applies the epilogue.
+// across workgroups: each writes its fp32 partial tiles (written through
+// to memory) and a separate finishing kernel sums them in split order and
+// applies the epilogue.  A whole call's launch also runs the LoRA-down
+// reduction (t) in a few extra workgroups: appended when K is split (the
+// finish reads t), first in the grid when it is not (the epilogue waits
+// for them).
 #pragma once
 
 #include "qerl_device.h"
