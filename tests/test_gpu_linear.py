@@ -97,6 +97,8 @@ def test_tiny_layer_full():
     (40, 200, 4096, 12, 2),   # split-K finish, r % 8 != 0; t summed by the split launch
     (64, 130, 6144, 72, 1),   # split-K finish, r > 64 (B row read in the loop)
     (17, 64, 1040, 24, 3),    # split-K in the general kernel (k % 256 != 0)
+    (40, 2048, 256, 8, 1),    # LDS-staged, unsplit with t summed inside the launch (2 token tiles)
+    (20, 2048, 256, 8, 2),    # the same with one token tile
 ])
 def test_shapes(m, n, k, r, stage):
     L = make_layer(m, n, k, r, seed=m * 7 + n, stage=stage, outlier_frac=1e-3)
@@ -136,6 +138,9 @@ def test_zero_weight_gives_lora_only():
     (100, 300, 2048, 24),    # 128-token kernel, 100 tokens, ragged last row group, K split
     (128, 2056, 256, 24),    # 128-token kernel unsplit: its epilogue waits for t from the launch
     (100, 4104, 384, 16),    # the same with 100 tokens and a ragged last row group
+    (96, 2056, 256, 24),     # the same with three token tiles (t rows past 96 read as zeros)
+    (40, 2048, 256, 8),      # LDS-staged, unsplit, t summed inside the launch
+    (20, 2048, 256, 8),      # the same with one token tile
 ])
 def test_deterministic_and_prepared_halves(m, n, k, r):
     # The whole call and its two halves give the same bits.  The halves run
@@ -248,6 +253,7 @@ def test_prefill_14b_m16384_sampled(idx):
     (128, 7168, 5120, 64, 0),    # the 32B qkv shape, no noise
     (160, 640, 1280, 32, 2),     # a 128-token chunk and a 32-token remainder
     (224, 384, 768, 16, 1),      # a 128-token chunk and a 96-token chunk
+    (96, 2056, 256, 24, 3),      # unsplit, three token tiles, t summed inside the launch
 ])
 def test_decode_128_tokens(m, n, k, r, stage):
     L = make_layer(m, n, k, r, seed=3 * m + n + k, stage=stage, outlier_frac=1e-3, call_id=2)
